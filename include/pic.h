@@ -1,0 +1,195 @@
+/*
+ * pic.h -- C ABI of the position-free paged attention library (libpic.so).
+ *
+ * The operation is the one of "MiniPIC: Flexible Position-Independent Caching
+ * in <100LOC", §2.1 (Position-free KV implementation): keys are cached
+ * UNROTATED in fixed-size physical blocks that several requests may share at
+ * different logical offsets, and the attention kernel applies the rotary
+ * rotation on the fly from a cosine/sine table indexed by each request's own
+ * logical positions:
+ *
+ *     score(t, j) = (R_t q_t)^T (R_pi(j) k~_j) / sqrt(d)
+ *
+ * with pi(j) the logical position of stored key j in the current request.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers: every array argument is DEVICE memory owned by the caller,
+ *   unless the argument is documented as host memory.  The library never
+ *   allocates or frees memory and keeps no state between calls.
+ * - stream: a hipStream_t (NULL = the legacy default stream).  Every call
+ *   only enqueues work on that stream and returns without synchronising the
+ *   host.
+ * - Return value: PIC_OK (0) or a negative pic_status.  Problems that can be
+ *   seen on the host (null pointers, unsupported shapes or dtypes, a
+ *   workspace that is too small) are reported before anything is launched.
+ *   PIC_EHIP means a HIP launch reported an error.
+ * - Device-resident values are PRECONDITIONS (checked by
+ *   pic_validate_metadata on host copies, not by the kernels): block ids in
+ *   [0, num_blocks), positions in [0, max_pos), 1 <= q_len <= seq_len,
+ *   seq_len <= max_seq_len, cu_seqlens consistent.  The kernels clamp block
+ *   ids and positions into range so that a violated precondition yields wrong
+ *   numbers, never an out-of-bounds access.
+ * - Supported shapes: head_dim in {64, 128}; block_size == 16;
+ *   num_q_heads % num_kv_heads == 0 with group size Hq/Hkv in {1,2,4,8,16}.
+ *
+ * Memory layouts (row-major, element type = dtype)
+ * ------------------------------------------------
+ *   k_pool  [num_blocks][Hkv][block_size][head_dim]   unrotated keys
+ *   v_pool  [num_blocks][Hkv][head_dim][block_size]   values, transposed per block
+ *   cache slot s = block * block_size + offset.
+ *   q, out  [rows][Hq][head_dim]  (one row per query token)
+ *   cos_tab, sin_tab  float32 [max_pos][head_dim/2]
+ *
+ * Readings of the page that the ABI fixes (the page is silent on them):
+ *   rotate-half pairing (element i with i + d/2); theta_i = base^(-2i/d);
+ *   q head h reads kv head h / (Hq/Hkv); V is not rotated; query row i of a
+ *   request with q_len rows and seq_len slots sees slots j <= seq_len - q_len
+ *   + i (causal, bottom-right aligned, over slot index -- positions never
+ *   affect the mask); softmax with the natural exponential.
+ */
+#ifndef PIC_H_
+#define PIC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PIC_OK = 0,
+    PIC_EINVAL = -1,        /* bad argument (null pointer, negative size, ...) */
+    PIC_EUNSUPPORTED = -2,  /* shape or dtype outside the supported set */
+    PIC_EWORKSPACE = -3,    /* workspace missing or smaller than required */
+    PIC_EHIP = -4           /* a HIP call or kernel launch failed */
+} pic_status;
+
+typedef enum {
+    PIC_F32 = 0,            /* float32 q, K, V, out */
+    PIC_BF16 = 1            /* bfloat16 q, K, V, out (fp32 accumulation) */
+} pic_dtype;
+
+/* Human-readable name of a pic_status value.  Never returns NULL. */
+const char* pic_status_string(int status);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int pic_version(void);
+
+/*
+ * pic_rope_table -- fill the cosine/sine lookup table (MiniPIC §2.1,
+ * Implementation bullet: the kernel looks up a cosine/sine table for every
+ * key element).
+ *   cos_tab[p][i] = cos(p * theta_i), sin_tab[p][i] = sin(p * theta_i),
+ *   theta_i = base^(-2i/head_dim), p in [0, max_pos), i in [0, head_dim/2).
+ * Angles and trig are evaluated in float64 and stored as float32 (round to
+ * nearest even).  Both outputs are float32 [max_pos][head_dim/2], device.
+ * Errors: PIC_EINVAL for null outputs, max_pos <= 0, base <= 0;
+ * PIC_EUNSUPPORTED for odd or non-positive head_dim.
+ */
+int pic_rope_table(float* cos_tab, float* sin_tab, int max_pos, int head_dim, double base,
+                   void* stream);
+
+/*
+ * pic_cache_write -- store the step's new keys and values, UNROTATED, into
+ * the paged pools (MiniPIC §2.1: the cache holds non-rotated key vectors, so
+ * a block never has to be rewritten when it is reused at another offset).
+ *   k, v          [num_tokens][Hkv][head_dim] (dtype), device, read only
+ *   slot_mapping  int32 [num_tokens], device: cache slot of each token;
+ *                 slots < 0 or >= num_blocks * block_size are skipped
+ *   k_pool/v_pool the pools in the layouts above (written in place)
+ * Bytes are copied unchanged (no arithmetic).  Two tokens mapped to the same
+ * slot in one call race.  num_tokens == 0 is a no-op.
+ * Errors: PIC_EINVAL (null pointers with num_tokens > 0, negative sizes),
+ * PIC_EUNSUPPORTED (dtype, head_dim, block_size).
+ */
+int pic_cache_write(const void* k, const void* v, const int32_t* slot_mapping, int num_tokens,
+                    int num_kv_heads, int head_dim, int dtype, void* k_pool, void* v_pool,
+                    int num_blocks, int block_size, void* stream);
+
+/*
+ * pic_attn_workspace_size -- bytes of device workspace that pic_attn_decode /
+ * pic_attn_prefill need for these bounds (total_q = number of query rows,
+ * max_seq_len >= every seq_len).  The workspace must be zero-filled once
+ * after allocation; every call leaves its split-combine counters at zero
+ * again, so the same workspace can be reused by later calls on the same
+ * stream.  Calls that overlap in time must use different workspaces.
+ * Returns 0 for unsupported arguments.
+ */
+size_t pic_attn_workspace_size(int num_reqs, int total_q, int max_seq_len, int num_q_heads,
+                               int num_kv_heads, int head_dim, int dtype);
+
+/*
+ * pic_attn_decode -- one query row per request (q_len == 1), the
+ * memory-bound path.  Request r's query is row r of q; it sits at logical
+ * position q_pos[r] and attends to key slots 0..seq_lens[r]-1, whose logical
+ * positions are k_pos[cu_seqlens_k[r] + j] (= pi(j), MiniPIC §2.1 score
+ * equation).  Slot j of request r lives in physical block
+ * block_table[r * block_table_stride + j / block_size] at offset
+ * j % block_size.  Long contexts are split into chunks whose count depends
+ * only on seq_len (so a request's result does not depend on the rest of the
+ * batch); the last chunk of a request to finish merges the partial results
+ * inside the same kernel.
+ *   q        [num_reqs][Hq][head_dim] unrotated, dtype
+ *   q_pos    int32 [num_reqs]
+ *   out      [num_reqs][Hq][head_dim], dtype (written)
+ *   workspace  >= pic_attn_workspace_size(num_reqs, num_reqs, max_seq_len, ...)
+ * A request with seq_len == 0 gets a zero output row.  The pools, tables and
+ * metadata are only read.
+ */
+int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, int block_table_stride, const int32_t* seq_lens,
+                    const int32_t* cu_seqlens_k, const int32_t* k_pos, const float* cos_tab,
+                    const float* sin_tab, int max_pos, int num_reqs, int num_q_heads,
+                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                    int max_seq_len, int dtype, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * pic_attn_prefill -- any mix of requests in ONE launch (chunked prefill,
+ * span prefill, and q_len == 1 decodes side by side: the interleaved
+ * span-prefill schedule of MiniPIC §2.2 "Scheduling" puts span prefills and
+ * ongoing decodes in the same batch).  Request r owns query rows
+ * cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1 of q; query row i of the request
+ * (0-based) sits at position q_pos[cu_seqlens_q[r] + i] and sees key slots
+ * j <= seq_lens[r] - q_len + i.  Other arguments as in pic_attn_decode.
+ * A small planner kernel builds the work list in the workspace first.
+ *   q, out   [total_q][Hq][head_dim]
+ *   workspace >= pic_attn_workspace_size(num_reqs, total_q, max_seq_len, ...)
+ */
+int pic_attn_prefill(const void* q, const int32_t* cu_seqlens_q, const int32_t* q_pos,
+                     const void* k_pool, const void* v_pool, const int32_t* block_table,
+                     int block_table_stride, const int32_t* seq_lens,
+                     const int32_t* cu_seqlens_k, const int32_t* k_pos, const float* cos_tab,
+                     const float* sin_tab, int max_pos, int num_reqs, int total_q,
+                     int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     int block_size, int num_blocks, int max_seq_len, int dtype, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pic_validate_metadata -- check the device-value preconditions above on
+ * HOST copies of the metadata (test and debug helper; no device work).
+ * cu_seqlens_q may be NULL for a decode batch (one query per request).
+ * Returns PIC_OK or PIC_EINVAL; when msg is not NULL a description of the
+ * first violation is written into msg[0..msg_len-1] (NUL terminated).
+ */
+int pic_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* q_pos,
+                          const int32_t* block_table, int block_table_stride,
+                          const int32_t* seq_lens, const int32_t* cu_seqlens_k,
+                          const int32_t* k_pos, int num_reqs, int total_q, int max_seq_len,
+                          int max_pos, int num_blocks, int block_size, char* msg, int msg_len);
+
+/*
+ * pic_decode_num_splits -- number of key chunks a request with seq_len keys
+ * is split into by the attention kernels (a pure function of seq_len and
+ * dtype), and pic_decode_split_len the keys per chunk (all but the last).
+ */
+int pic_decode_num_splits(int seq_len, int dtype);
+int pic_decode_split_len(int seq_len, int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PIC_H_ */

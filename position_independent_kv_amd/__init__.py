@@ -1,0 +1,272 @@
+"""Position-free paged attention for MI355X (gfx950): Python binding.
+
+Thin ctypes marshalling over ``libpic.so`` (declared in ``include/pic.h``):
+each function takes torch tensors, checks dtypes / shapes / devices, derives
+the integer sizes from the shapes, and passes raw pointers plus the current
+HIP stream.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback path.  If the library is not built, importing
+works but every call raises ``PicLibraryMissing``.
+
+The operation is the one of "MiniPIC: Flexible Position-Independent Caching
+in <100LOC", §2.1: keys cached unrotated, rotary rotation applied inside the
+attention kernel from each request's logical positions.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpic.so")
+
+PIC_OK, PIC_EINVAL, PIC_EUNSUPPORTED, PIC_EWORKSPACE, PIC_EHIP = 0, -1, -2, -3, -4
+PIC_F32, PIC_BF16 = 0, 1
+BLOCK_SIZE = 16
+
+EXPORTS = [
+    "pic_status_string", "pic_version", "pic_rope_table", "pic_cache_write",
+    "pic_attn_workspace_size", "pic_attn_decode", "pic_attn_prefill", "pic_validate_metadata",
+    "pic_decode_num_splits", "pic_decode_split_len",
+]
+
+
+class PicError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_status_string(status)} ({status})")
+
+
+class PicLibraryMissing(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise PicLibraryMissing(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_void, c_size, c_double = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_double
+    c_char_p = ctypes.c_char_p
+    lib.pic_status_string.restype = c_char_p
+    lib.pic_status_string.argtypes = [c_int]
+    lib.pic_version.restype = c_int
+    lib.pic_rope_table.argtypes = [c_void, c_void, c_int, c_int, c_double, c_void]
+    lib.pic_cache_write.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_void,
+                                    c_void, c_int, c_int, c_void]
+    lib.pic_attn_workspace_size.restype = c_size
+    lib.pic_attn_workspace_size.argtypes = [c_int] * 7
+    lib.pic_attn_decode.argtypes = ([c_void] * 5 + [c_int] + [c_void] * 5 + [c_int] * 9
+                                    + [c_void, c_void, c_size, c_void])
+    lib.pic_attn_prefill.argtypes = ([c_void] * 6 + [c_int] + [c_void] * 5 + [c_int] * 11
+                                     + [c_void, c_void, c_size, c_void])
+    lib.pic_validate_metadata.argtypes = ([c_void] * 3 + [c_int] + [c_void] * 3 + [c_int] * 6
+                                          + [ctypes.c_char_p, c_int])
+    lib.pic_decode_num_splits.argtypes = [c_int, c_int]
+    lib.pic_decode_split_len.argtypes = [c_int, c_int]
+    for name in EXPORTS:
+        getattr(lib, name)  # every declared symbol must resolve
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises PicLibraryMissing if not built)."""
+    return _load()
+
+
+def _status_string(status: int) -> str:
+    try:
+        return _load().pic_status_string(status).decode()
+    except PicLibraryMissing:
+        return "status"
+
+
+def _check(status: int, where: str):
+    if status != PIC_OK:
+        raise PicError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return PIC_BF16
+    if t.dtype == torch.float32:
+        return PIC_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def pic_version() -> int:
+    return _load().pic_version()
+
+
+def pic_status_string(status: int) -> str:
+    return _load().pic_status_string(status).decode()
+
+
+def pic_rope_table(cos_tab, sin_tab, base: float, stream=None):
+    """Fill float32 [max_pos][head_dim/2] cos/sin tables for rotary base ``base``."""
+    torch = _torch()
+    if cos_tab.shape != sin_tab.shape or cos_tab.dim() != 2:
+        raise ValueError("cos_tab and sin_tab must both be [max_pos][head_dim/2]")
+    max_pos, half = cos_tab.shape
+    _check(_load().pic_rope_table(_ptr(cos_tab, "cos_tab", torch.float32),
+                                  _ptr(sin_tab, "sin_tab", torch.float32), max_pos, 2 * half,
+                                  float(base), _stream(stream)), "pic_rope_table")
+
+
+def pic_cache_write(k, v, slot_mapping, k_pool, v_pool, stream=None):
+    """Scatter unrotated k, v [T][Hkv][d] into the pools at slot_mapping[T] (int32)."""
+    torch = _torch()
+    if k.shape != v.shape or k.dim() != 3:
+        raise ValueError("k and v must both be [num_tokens][Hkv][head_dim]")
+    T, hkv, d = k.shape
+    nb, phkv, bs, pd = k_pool.shape
+    if (phkv, pd) != (hkv, d) or tuple(v_pool.shape) != (nb, hkv, d, bs):
+        raise ValueError("pool shapes must be k [nb][Hkv][B][d] and v [nb][Hkv][d][B]")
+    if k.dtype != k_pool.dtype or v.dtype != k.dtype or v_pool.dtype != k.dtype:
+        raise TypeError("k, v and the pools must share one dtype")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    _check(_load().pic_cache_write(_ptr(k, "k"), _ptr(v, "v"),
+                                   _ptr(slot_mapping, "slot_mapping", torch.int32), T, hkv, d,
+                                   _dtype_code(k), _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
+                                   nb, bs, _stream(stream)), "pic_cache_write")
+
+
+def pic_attn_workspace_size(num_reqs, total_q, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                            dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
+    return int(_load().pic_attn_workspace_size(num_reqs, total_q, max_seq_len, num_q_heads,
+                                               num_kv_heads, head_dim, code))
+
+
+def _pool_dims(k_pool, v_pool):
+    nb, hkv, bs, d = k_pool.shape
+    if tuple(v_pool.shape) != (nb, hkv, d, bs):
+        raise ValueError("v_pool must be [num_blocks][Hkv][head_dim][block_size]")
+    return nb, hkv, bs, d
+
+
+def pic_attn_decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens_k, k_pos,
+                    cos_tab, sin_tab, max_seq_len, out, workspace, stream=None):
+    """One query row per request: q, out [R][Hq][d]; metadata int32 device tensors."""
+    torch = _torch()
+    i32 = torch.int32
+    R, hq, d = q.shape
+    nb, hkv, bs, pd = _pool_dims(k_pool, v_pool)
+    if pd != d or tuple(out.shape) != (R, hq, d) or out.dtype != q.dtype:
+        raise ValueError("q / out / pool head sizes disagree")
+    if block_table.dim() != 2 or block_table.shape[0] < R:
+        raise ValueError("block_table must be [R][stride]")
+    _check(_load().pic_attn_decode(
+        _ptr(q, "q"), _ptr(q_pos, "q_pos", i32), _ptr(k_pool, "k_pool", q.dtype),
+        _ptr(v_pool, "v_pool", q.dtype), _ptr(block_table, "block_table", i32),
+        block_table.shape[1], _ptr(seq_lens, "seq_lens", i32),
+        _ptr(cu_seqlens_k, "cu_seqlens_k", i32), _ptr(k_pos, "k_pos", i32),
+        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
+        cos_tab.shape[0], R, hq, hkv, d, bs, nb, int(max_seq_len), _dtype_code(q),
+        _ptr(out, "out"), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "pic_attn_decode")
+
+
+def pic_attn_prefill(q, cu_seqlens_q, q_pos, k_pool, v_pool, block_table, seq_lens,
+                     cu_seqlens_k, k_pos, cos_tab, sin_tab, max_q_len, max_seq_len, out,
+                     workspace, stream=None):
+    """Mixed batch in one launch: q, out [total_q][Hq][d]; cu_seqlens_q [R+1]."""
+    torch = _torch()
+    i32 = torch.int32
+    total_q, hq, d = q.shape
+    R = seq_lens.shape[0]
+    nb, hkv, bs, pd = _pool_dims(k_pool, v_pool)
+    if pd != d or tuple(out.shape) != (total_q, hq, d) or out.dtype != q.dtype:
+        raise ValueError("q / out / pool head sizes disagree")
+    if cu_seqlens_q.shape != (R + 1,) or block_table.dim() != 2:
+        raise ValueError("cu_seqlens_q must be [R+1] and block_table [R][stride]")
+    _check(_load().pic_attn_prefill(
+        _ptr(q, "q"), _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(q_pos, "q_pos", i32),
+        _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype),
+        _ptr(block_table, "block_table", i32), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", i32), _ptr(cu_seqlens_k, "cu_seqlens_k", i32),
+        _ptr(k_pos, "k_pos", i32), _ptr(cos_tab, "cos_tab", torch.float32),
+        _ptr(sin_tab, "sin_tab", torch.float32), cos_tab.shape[0], R, total_q, int(max_q_len),
+        hq, hkv, d, bs, nb, int(max_seq_len), _dtype_code(q), _ptr(out, "out"),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "pic_attn_prefill")
+
+
+def pic_validate_metadata(cu_seqlens_q, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos,
+                          max_seq_len, max_pos, num_blocks, block_size=BLOCK_SIZE):
+    """Check the device-value preconditions on host (numpy int32) copies.
+
+    Returns (status, message).  cu_seqlens_q may be None for a decode batch.
+    """
+    arrs = {}
+    for name, a in [("cu_seqlens_q", cu_seqlens_q), ("q_pos", q_pos), ("block_table", block_table),
+                    ("seq_lens", seq_lens), ("cu_seqlens_k", cu_seqlens_k), ("k_pos", k_pos)]:
+        arrs[name] = None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+    R = arrs["seq_lens"].shape[0]
+    bt = arrs["block_table"]
+    stride = bt.shape[1] if bt.ndim == 2 else 0
+    total_q = R if arrs["cu_seqlens_q"] is None else int(arrs["q_pos"].shape[0])
+
+    def p(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    buf = ctypes.create_string_buffer(256)
+    st = _load().pic_validate_metadata(p(arrs["cu_seqlens_q"]), p(arrs["q_pos"]), p(bt), stride,
+                                       p(arrs["seq_lens"]), p(arrs["cu_seqlens_k"]),
+                                       p(arrs["k_pos"]), R, total_q, int(max_seq_len),
+                                       int(max_pos), int(num_blocks), int(block_size), buf, 256)
+    return st, buf.value.decode()
+
+
+def pic_decode_num_splits(seq_len: int, dtype: int = PIC_BF16) -> int:
+    return int(_load().pic_decode_num_splits(seq_len, dtype))
+
+
+def pic_decode_split_len(seq_len: int, dtype: int = PIC_BF16) -> int:
+    return int(_load().pic_decode_split_len(seq_len, dtype))

@@ -1,0 +1,832 @@
+// Position-free paged attention for gfx950: pic_attn_decode, pic_attn_prefill.
+//
+// What is computed (MiniPIC §2.1, score equation): for query row t of a
+// request and each of its key slots j,
+//     score(t, j) = (R_t q_t)^T (R_pi(j) k~_j) / sqrt(d)
+// where k~_j is the UNROTATED key stored in a shared physical block, pi(j) is
+// the key's logical position in this request, and R_p is the rotary rotation
+// (rotate-half pairing, theta_i = base^(-2i/d), read from the cos/sin table).
+// Softmax over the visible slots, then the weighted sum of the (unrotated)
+// values.  Doing the rotation here instead of in the cache is algebraically
+// the same as re-rotating the cache hit, without writing the shared block
+// (MiniPIC §2.1, Implementation bullet).
+//
+// Formulation on the matrix cores (per kv head g and group of q heads):
+//     S^T = K_rot * Q_rot^T      A = rotated keys (16 keys x d), B = queries
+//     O^T += V^T * P^T           A = values transposed (d x keys), B = probs
+// Keys are the M dimension of the score tile, so the score accumulator lands
+// in exactly the register layout the PV product wants for its B operand (no
+// shuffles), and V^T is read straight from the pool because the pool stores
+// V transposed inside each block.  The rotation pairs element i with i + d/2;
+// in this operand layout both halves of a pair sit in the same lane, so the
+// rotation is a handful of FMAs on registers right after the load.
+//
+// Decode (one query row per request, memory bound): one wave per
+// (request, kv head, key chunk), the G query heads of the kv head are the
+// columns of the tile; K, V and the table row are read from global memory.
+// Chunks of one request are merged in the same kernel: each chunk writes its
+// normalised partial output and (max, sum) to the workspace, and the last
+// workgroup of a (request, head group) to arrive merges them.
+//
+// Prefill (q_len > 1, MFMA bound): one workgroup per (request, kv head,
+// 128 query rows); the rows are (token, q head of the group) pairs, 32 per
+// wave.  Each 32-key step is gathered from the paged pool once per
+// workgroup, rotated while it is written to LDS as the MFMA operand, and
+// shared by the four waves; V^T is staged in LDS next to it.  Online softmax
+// keeps one running max/sum per row.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "../../include/pic.h"
+#include "pic_common.hpp"
+#include "pic_device.hpp"
+#include "pic_host.hpp"
+
+namespace pic {
+
+struct AttnArgs {
+  const void* q;
+  const int32_t* cu_q;  // null for the decode-only kernel: row r is request r
+  const int32_t* q_pos;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  long long bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* cu_k;
+  const int32_t* k_pos;
+  const float* cos_tab;
+  const float* sin_tab;
+  int max_pos;
+  int num_reqs;
+  int hq;
+  int hkv;
+  int group;
+  int num_blocks;
+  int max_seq_len;
+  int s_max;
+  int nhg;
+  float scale_log2;  // log2(e) / sqrt(d): scores are kept in base-2 units
+  void* out;
+  float2* ws_ml;
+  float* ws_o;
+  int* ws_cnt;
+  const int4* items;
+  const int* nitems;
+};
+
+// seq_len of request r, clamped to what the grid, the workspace and the block
+// table were sized for (a violated precondition gives wrong numbers, never an
+// out-of-bounds access).
+__device__ __forceinline__ int seq_len_of(const AttnArgs& a, int r) {
+  const long long cap = min((long long)a.max_seq_len, a.bt_stride * kBlockSize);
+  return (int)min((long long)a.seq_lens[r], cap);
+}
+
+// ---------------------------------------------------------------------------
+// rotation helpers
+// ---------------------------------------------------------------------------
+
+// cos/sin of the pairs a lane owns: pair index c*KCH + grp*KPL + e for the
+// first-half chunks c < NH, at table row `pos`.
+template <typename T, int D>
+__device__ __forceinline__ void load_trig(const AttnArgs& a, int pos, int grp, float* cs,
+                                          float* sn) {
+  using C = Cfg<T, D>;
+  const float* crow = a.cos_tab + (size_t)pos * (D / 2) + grp * C::KPL;
+  const float* srow = a.sin_tab + (size_t)pos * (D / 2) + grp * C::KPL;
+#pragma unroll
+  for (int c = 0; c < C::NH; ++c) {
+    const typename Run<float, C::KPL>::V cv = Run<float, C::KPL>::load(crow + c * C::KCH);
+    const typename Run<float, C::KPL>::V sv = Run<float, C::KPL>::load(srow + c * C::KCH);
+#pragma unroll
+    for (int e = 0; e < C::KPL; ++e) {
+      cs[c * C::KPL + e] = elem<float, C::KPL>(cv, e);
+      sn[c * C::KPL + e] = elem<float, C::KPL>(sv, e);
+    }
+  }
+}
+
+// x[c] and x[c + NH] hold the two halves of the same pairs: rotate in place.
+template <typename T, int D>
+__device__ __forceinline__ void rotate_ops(OpT<T>* x, const float* cs, const float* sn) {
+  using C = Cfg<T, D>;
+  using M = Mma<T>;
+#pragma unroll
+  for (int c = 0; c < C::NH; ++c) {
+#pragma unroll
+    for (int e = 0; e < C::KPL; ++e) {
+      const float lo = M::get(x[c], e);
+      const float hi = M::get(x[c + C::NH], e);
+      const float co = cs[c * C::KPL + e], si = sn[c * C::KPL + e];
+      M::set(x[c], e, lo * co - hi * si);
+      M::set(x[c + C::NH], e, hi * co + lo * si);
+    }
+  }
+}
+
+// Rotated query operand for one column: q row `qrow`, q head `head`.
+template <typename T, int D>
+__device__ __forceinline__ void load_query(const AttnArgs& a, long long qrow, int head, int pos,
+                                           bool valid, int grp, OpT<T>* qop) {
+  using C = Cfg<T, D>;
+  using M = Mma<T>;
+  const T* qp = (const T*)a.q + ((size_t)qrow * a.hq + head) * D + grp * C::KPL;
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) qop[c] = M::load(qp + c * C::KCH);
+  float cs[C::NH * C::KPL], sn[C::NH * C::KPL];
+  load_trig<T, D>(a, clampi(pos, 0, a.max_pos - 1), grp, cs, sn);
+  rotate_ops<T, D>(qop, cs, sn);
+  if (!valid) {
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) qop[c] = M::zero();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// online softmax on one 16-column score tile set
+// ---------------------------------------------------------------------------
+
+// s[t][i]: masked scores (base-2 units, -inf where masked) of keys
+// key_of(t, grp*4+i) for this lane's column.  Updates the running max m
+// (identical in the four lanes of a column) and the lane-partial sum l,
+// rescales acc, and overwrites s with the probabilities.
+template <int NT, int ND>
+__device__ __forceinline__ void softmax_step(f32x4 (&s)[NT], f32x4 (&acc)[ND], float& m,
+                                             float& l) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m, mx);
+  const float base = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = fast_exp2(m - base);
+  float psum = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = fast_exp2(s[t][i] - base);
+      s[t][i] = p;
+      psum += p;
+    }
+  l = l * alpha + psum;
+  m = m_new;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) acc[dt] *= alpha;
+}
+
+// B operand of PV MFMA number mi: probabilities of keys grp*4*NT + mi*KPL + e.
+template <typename T, int D>
+__device__ __forceinline__ typename Mma<T>::Op pack_probs(const f32x4 (&s)[Cfg<T, D>::NT],
+                                                          int mi) {
+  using C = Cfg<T, D>;
+  typename Mma<T>::Op p;
+#pragma unroll
+  for (int e = 0; e < C::KPL; ++e) {
+    const int idx = mi * C::KPL + e;
+    Mma<T>::set(p, e, s[idx / 4][idx % 4]);
+  }
+  return p;
+}
+
+__device__ __forceinline__ float col_sum(float l) {
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  return l;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, f32x4 v, float scale) {
+  if constexpr (sizeof(T) == 2) {
+    vec<bf16, 4> o;
+    o[0] = (bf16)(v[0] * scale);
+    o[1] = (bf16)(v[1] * scale);
+    o[2] = (bf16)(v[2] * scale);
+    o[3] = (bf16)(v[3] * scale);
+    *reinterpret_cast<vec<bf16, 4>*>(p) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v * scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode: one wave = (request r, kv head g, keys [k0, k1)), q row qrow
+// ---------------------------------------------------------------------------
+
+template <typename T, int D>
+__device__ void decode_wave(const AttnArgs& a, int r, int g, long long qrow, int k0, int k1,
+                            int L, f32x4 (&acc)[Cfg<T, D>::ND], float& m_run, float& l_run) {
+  using C = Cfg<T, D>;
+  using M = Mma<T>;
+  typedef typename M::Op Op;
+  const int lane = threadIdx.x & 63;
+  const int row16 = lane & 15;
+  const int grp = lane >> 4;
+  const int G = a.group;
+
+  Op qop[C::NC];
+  const bool qvalid = row16 < G;
+  load_query<T, D>(a, qrow, g * G + (qvalid ? row16 : 0), a.q_pos[qrow], qvalid, grp, qop);
+
+  const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
+  const int32_t* kp = a.k_pos + a.cu_k[r];
+  const T* kpool = (const T*)a.k_pool;
+  const T* vpool = (const T*)a.v_pool;
+  const int nb_max = a.num_blocks - 1;
+  const int pmax = a.max_pos - 1;
+
+#pragma unroll
+  for (int dt = 0; dt < C::ND; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  m_run = -INFINITY;
+  l_run = 0.0f;
+
+  for (int kb = k0; kb < k1; kb += C::KSTEP) {
+    f32x4 s[C::NT];
+    // scores: lane loads and rotates the key of its A row in each tile
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+      const int kc = min(kb + key_of<C::NT>(t, row16), L - 1);
+      const int blk = clampi(bt[kc >> 4], 0, nb_max);
+      const int pos = clampi(kp[kc], 0, pmax);
+      const T* krow = kpool + (((size_t)blk * a.hkv + g) * kBlockSize + (kc & 15)) * D +
+                      grp * C::KPL;
+      Op kop[C::NC];
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) kop[c] = M::load(krow + c * C::KCH);
+      float cs[C::NH * C::KPL], sn[C::NH * C::KPL];
+      load_trig<T, D>(a, pos, grp, cs, sn);
+      rotate_ops<T, D>(kop, cs, sn);
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) s[t] = M::run(kop[c], qop[c], s[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb + key_of<C::NT>(t, grp * 4 + i);
+        s[t][i] = key < k1 ? s[t][i] * a.scale_log2 : -INFINITY;
+      }
+    softmax_step<C::NT, C::ND>(s, acc, m_run, l_run);
+    // O^T += V^T P^T
+#pragma unroll
+    for (int mi = 0; mi < C::NPV; ++mi) {
+      const Op p = pack_probs<T, D>(s, mi);
+      const int vkey = kb + grp * 4 * C::NT + mi * C::KPL;  // first of KPL keys
+      const int vkc = min(vkey, L - 1);
+      const int vblk = clampi(bt[vkc >> 4], 0, nb_max);
+      const T* vrow = vpool + (((size_t)vblk * a.hkv + g) * D + row16) * kBlockSize + (vkey & 15);
+      const bool tail = vkey + C::KPL > L;
+#pragma unroll
+      for (int dt = 0; dt < C::ND; ++dt) {
+        Op v = M::load(vrow + (size_t)dt * 16 * kBlockSize);
+        if (tail) {
+#pragma unroll
+          for (int e = 0; e < C::KPL; ++e)
+            if (vkey + e >= L) M::set(v, e, 0.0f);
+        }
+        acc[dt] = M::run(v, p, acc[dt]);
+      }
+    }
+  }
+}
+
+// Merge the S chunk partials of (request r, kv head g) into the output row.
+template <typename T, int D>
+__device__ void combine_wave(const AttnArgs& a, int r, int g, long long qrow, int S) {
+  const int lane = threadIdx.x & 63;
+  const int G = a.group;
+  constexpr int PER = D / 64;  // output elements per lane
+  for (int col = 0; col < G; ++col) {
+    const size_t pbase = (((size_t)r * a.hkv + g) * a.s_max) * G + col;  // + s * G
+    float mstar = -INFINITY;
+    for (int s = 0; s < S; ++s) mstar = fmaxf(mstar, a.ws_ml[pbase + (size_t)s * G].x);
+    float o[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = 0.0f;
+    float wsum = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      const float2 ml = a.ws_ml[pbase + (size_t)s * G];
+      const float w = ml.y * fast_exp2(ml.x - mstar);
+      wsum += w;
+      const float* op = a.ws_o + (pbase + (size_t)s * G) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] += w * op[e];
+    }
+    const float inv = 1.0f / wsum;
+    T* out = (T*)a.out + ((size_t)qrow * a.hq + g * G + col) * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) out[e] = (T)(o[e] * inv);
+  }
+}
+
+// One decode work item: request r, kv heads hg*4 .. hg*4+3 (one per wave),
+// key chunk s.  Uniform across the workgroup.
+template <typename T, int D>
+__device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long qrow,
+                            int* s_flag) {
+  using C = Cfg<T, D>;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int row16 = lane & 15;
+  const int grp = lane >> 4;
+  const int g = hg * kWaves + wave;
+  const bool active = g < a.hkv;
+  const int G = a.group;
+  const int L = seq_len_of(a, r);
+  const int S = num_splits(L, C::KSTEP);
+  if (s >= S) return;
+  if (L <= 0) {  // empty context: zero output
+    if (active) {
+      T* out = (T*)a.out + ((size_t)qrow * a.hq + g * G) * D;
+      for (int e = lane; e < G * D; e += 64) out[e] = (T)0.0f;
+    }
+    return;
+  }
+  const int chunk = split_len(L, C::KSTEP);
+  const int k0 = s * chunk;
+  const int k1 = min(L, k0 + chunk);
+  f32x4 acc[C::ND];
+  float m_run = -INFINITY, l_run = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < C::ND; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (active) decode_wave<T, D>(a, r, g, qrow, k0, k1, L, acc, m_run, l_run);
+  const float l_tot = col_sum(l_run);
+  if (S == 1) {
+    if (active && row16 < G) {
+      T* out = (T*)a.out + ((size_t)qrow * a.hq + g * G + row16) * D + grp * 4;
+      const float inv = 1.0f / l_tot;
+#pragma unroll
+      for (int dt = 0; dt < C::ND; ++dt) store4<T>(out + dt * 16, acc[dt], inv);
+    }
+    return;
+  }
+  if (active && row16 < G) {
+    const size_t pidx = (((size_t)r * a.hkv + g) * a.s_max + s) * G + row16;
+    const float inv = 1.0f / l_tot;
+    float* op = a.ws_o + pidx * D + grp * 4;
+#pragma unroll
+    for (int dt = 0; dt < C::ND; ++dt) *reinterpret_cast<f32x4*>(op + dt * 16) = acc[dt] * inv;
+    if (grp == 0) a.ws_ml[pidx] = make_float2(m_run, l_tot);
+  }
+  // Publish the partials, then count this chunk in.  The workgroup that
+  // brings the count to S merges all chunks and re-arms the counter.
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = atomicAdd(&a.ws_cnt[r * a.nhg + hg], 1);
+    *s_flag = (old == S - 1);
+  }
+  __syncthreads();
+  if (*s_flag) {
+    __threadfence();
+    if (active) combine_wave<T, D>(a, r, g, qrow, S);
+    if (threadIdx.x == 0) a.ws_cnt[r * a.nhg + hg] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prefill tile: request r, kv head g, query rows [tile*128, tile*128+128)
+// ---------------------------------------------------------------------------
+
+template <typename T, int D>
+struct PrefillSmem {
+  using C = Cfg<T, D>;
+  static constexpr int KLD = D + C::PAD;            // K row stride (elements)
+  static constexpr int VLD = C::KSTEP + C::PAD;     // V^T row stride (elements)
+  static constexpr int BYTES = (C::KSTEP * KLD + D * VLD) * (int)sizeof(T);
+};
+
+template <typename T, int D>
+__device__ void prefill_tile(const AttnArgs& a, int r, int g, int tile, unsigned char* smem) {
+  using C = Cfg<T, D>;
+  using M = Mma<T>;
+  using SM = PrefillSmem<T, D>;
+  typedef typename M::Op Op;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int row16 = lane & 15;
+  const int grp = lane >> 4;
+  const int G = a.group;
+  const int q0 = a.cu_q[r];
+  const int ql = a.cu_q[r + 1] - q0;
+  const int L = seq_len_of(a, r);
+  const int nrows = ql * G;
+  const int trow0 = tile * kPrefillRows;
+  const int last_tok = min((trow0 + kPrefillRows - 1) / G, ql - 1);
+  const int kend = min(L, L - ql + last_tok + 1);  // slots any row of the tile sees
+
+  Op qop[2][C::NC];
+  int lim[2];      // last visible slot of the column, -1 for padding columns
+  int tok_of[2], head_of[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = trow0 + wave * 32 + j * 16 + row16;
+    const bool valid = n < nrows;
+    const int nn = valid ? n : 0;
+    tok_of[j] = nn / G;
+    head_of[j] = nn % G;
+    lim[j] = valid ? L - ql + tok_of[j] : -1;
+    load_query<T, D>(a, (long long)q0 + tok_of[j], g * G + head_of[j], a.q_pos[q0 + tok_of[j]],
+                     valid, grp, qop[j]);
+  }
+
+  T* Ks = reinterpret_cast<T*>(smem);
+  T* Vs = Ks + C::KSTEP * SM::KLD;
+  const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
+  const int32_t* kp = a.k_pos + a.cu_k[r];
+  const T* kpool = (const T*)a.k_pool;
+  const T* vpool = (const T*)a.v_pool;
+  const int nb_max = a.num_blocks - 1;
+  const int pmax = a.max_pos - 1;
+
+  f32x4 acc[2][C::ND];
+  float m_run[2], l_run[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int dt = 0; dt < C::ND; ++dt) acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.0f;
+  }
+
+  // cooperative staging shapes
+  constexpr int PPT = C::KSTEP * (D / 2) / kThreads;  // rotation pairs per thread
+  constexpr int TPK = (D / 2) / PPT;                  // threads per key
+  constexpr int EPT = C::KSTEP * D / kThreads;        // V elements per thread
+  constexpr int TPR = C::KSTEP / EPT;                 // threads per V^T row
+  static_assert(PPT >= 1 && EPT >= 1 && EPT <= kBlockSize, "staging shape");
+
+  for (int kb = 0; kb < kend; kb += C::KSTEP) {
+    {  // rotated K rows -> LDS
+      const int key = threadIdx.x / TPK;
+      const int i0 = (threadIdx.x % TPK) * PPT;
+      const int kc = min(kb + key, L - 1);
+      const int blk = clampi(bt[kc >> 4], 0, nb_max);
+      const int pos = clampi(kp[kc], 0, pmax);
+      const T* src = kpool + (((size_t)blk * a.hkv + g) * kBlockSize + (kc & 15)) * D + i0;
+      typedef Run<T, PPT> RT;
+      typedef Run<float, PPT> RF;
+      typename RT::V lo = RT::load(src), hi = RT::load(src + D / 2);
+      const typename RF::V cv = RF::load(a.cos_tab + (size_t)pos * (D / 2) + i0);
+      const typename RF::V sv = RF::load(a.sin_tab + (size_t)pos * (D / 2) + i0);
+#pragma unroll
+      for (int e = 0; e < PPT; ++e) {
+        const float x = elem<T, PPT>(lo, e), y = elem<T, PPT>(hi, e);
+        const float c = elem<float, PPT>(cv, e), sn = elem<float, PPT>(sv, e);
+        set_elem<T, PPT>(lo, e, x * c - y * sn);
+        set_elem<T, PPT>(hi, e, y * c + x * sn);
+      }
+      RT::store(Ks + key * SM::KLD + i0, lo);
+      RT::store(Ks + key * SM::KLD + D / 2 + i0, hi);
+    }
+    {  // V^T rows -> LDS (keys at or beyond L are zeroed)
+      const int d = threadIdx.x / TPR;
+      const int kr0 = (threadIdx.x % TPR) * EPT;
+      const int vk = kb + kr0;
+      const int vkc = min(vk, L - 1);
+      const int blk = clampi(bt[vkc >> 4], 0, nb_max);
+      const T* src = vpool + (((size_t)blk * a.hkv + g) * D + d) * kBlockSize + (vk & 15);
+      T* dst = Vs + d * SM::VLD + kr0;
+      constexpr int VEC = 16 / (int)sizeof(T);
+      constexpr int NV = EPT >= VEC ? EPT / VEC : 1;
+      constexpr int W = EPT >= VEC ? VEC : EPT;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        typename Run<T, W>::V x = Run<T, W>::load(src + u * W);
+        if (vk + (u + 1) * W > L) {
+#pragma unroll
+          for (int e = 0; e < W; ++e)
+            if (vk + u * W + e >= L) set_elem<T, W>(x, e, 0.0f);
+        }
+        Run<T, W>::store(dst + u * W, x);
+      }
+    }
+    __syncthreads();
+
+    f32x4 s[2][C::NT];
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+      const T* kr = Ks + key_of<C::NT>(t, row16) * SM::KLD + grp * C::KPL;
+      Op kop[C::NC];
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) kop[c] = M::load(kr + c * C::KCH);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        s[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) s[j][t] = M::run(kop[c], qop[j][c], s[j][t]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb + key_of<C::NT>(t, grp * 4 + i);
+          s[j][t][i] = key <= lim[j] ? s[j][t][i] * a.scale_log2 : -INFINITY;
+        }
+      softmax_step<C::NT, C::ND>(s[j], acc[j], m_run[j], l_run[j]);
+    }
+#pragma unroll
+    for (int mi = 0; mi < C::NPV; ++mi) {
+      Op p[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) p[j] = pack_probs<T, D>(s[j], mi);
+      const T* vr = Vs + row16 * SM::VLD + grp * 4 * C::NT + mi * C::KPL;
+#pragma unroll
+      for (int dt = 0; dt < C::ND; ++dt) {
+        const Op v = M::load(vr + dt * 16 * SM::VLD);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[j][dt] = M::run(v, p[j], acc[j][dt]);
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float l_tot = col_sum(l_run[j]);
+    if (lim[j] >= 0) {
+      T* out = (T*)a.out + (((size_t)q0 + tok_of[j]) * a.hq + g * G + head_of[j]) * D + grp * 4;
+      const float inv = 1.0f / l_tot;
+#pragma unroll
+      for (int dt = 0; dt < C::ND; ++dt) store4<T>(out + dt * 16, acc[j][dt], inv);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kernels
+// ---------------------------------------------------------------------------
+
+// Workgroup b runs on XCD b % 8 (round-robin dispatch).  Give each XCD a
+// contiguous range of logical items so items that share data (the same
+// table rows, the same request's blocks) share that XCD's L2.
+__device__ __forceinline__ long long xcd_logical(long long b, long long n) {
+  const long long q = n / 8, rem = n % 8;
+  const long long x = b % 8, k = b / 8;
+  return x * q + min(x, rem) + k;
+}
+// Inverse of xcd_logical: dispatch position of logical item l.
+__device__ __forceinline__ long long xcd_position(long long l, long long n) {
+  const long long q = n / 8, rem = n % 8;
+  long long x, k;
+  if (l < rem * (q + 1)) {
+    x = l / (q + 1);
+    k = l % (q + 1);
+  } else {
+    x = rem + (l - rem * (q + 1)) / q;
+    k = (l - rem * (q + 1)) % q;
+  }
+  return k * 8 + x;
+}
+
+// Decode-only launch: logical item = (chunk s, request r, head group hg),
+// chunk-major so all requests' chunk s (same key positions in a batch of
+// equal-shaped contexts) run on one XCD.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
+  __shared__ int s_flag;
+  const long long n = (long long)gridDim.x;
+  const long long l = xcd_logical(blockIdx.x, n);
+  const int hg = (int)(l % a.nhg);
+  const long long rs = l / a.nhg;
+  const int r = (int)(rs % a.num_reqs);
+  const int s = (int)(rs / a.num_reqs);
+  decode_item<T, D>(a, r, hg, s, r, &s_flag);
+}
+
+// Mixed launch over the planner's work list.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads, 2) mixed_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[PrefillSmem<T, D>::BYTES];
+  __shared__ int s_flag;
+  if ((int)blockIdx.x >= *a.nitems) return;
+  const int4 it = a.items[blockIdx.x];
+  if (it.x == kItemPrefill) {
+    prefill_tile<T, D>(a, it.y, it.z, it.w, smem);
+  } else {
+    decode_item<T, D>(a, it.y, it.z, it.w, (long long)a.cu_q[it.y], &s_flag);
+  }
+}
+
+// Planner: one workgroup of 1024 threads turns (cu_seqlens_q, seq_lens) into
+// the work list.  Prefill tiles first (per request and kv head, last tile
+// first: the later query rows see more keys), then the chunks of q_len == 1
+// requests; each item is written at its XCD dispatch position.  Also zeroes
+// the split-combine counters of the decode requests.
+__global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ cu_q,
+                                                    const int32_t* __restrict__ seq_lens,
+                                                    int num_reqs, int hkv, int group, int nhg,
+                                                    int kstep, int len_cap, long long max_items,
+                                                    int4* __restrict__ items,
+                                                    int* __restrict__ count,
+                                                    int* __restrict__ counters) {
+  __shared__ long long s_a[1024];
+  __shared__ long long s_b[1024];
+  __shared__ long long s_tot[2];
+  const int tid = threadIdx.x;
+  // pass 1: totals
+  long long pf = 0, dc = 0;
+  for (int r = tid; r < num_reqs; r += 1024) {
+    const int ql = cu_q[r + 1] - cu_q[r];
+    if (ql > 1) pf += (long long)hkv * cdiv(ql * group, kPrefillRows);
+    else if (ql == 1) dc += (long long)nhg * num_splits(min(seq_lens[r], len_cap), kstep);
+  }
+  s_a[tid] = pf;
+  s_b[tid] = dc;
+  __syncthreads();
+  for (int st = 512; st > 0; st >>= 1) {
+    if (tid < st) {
+      s_a[tid] += s_a[tid + st];
+      s_b[tid] += s_b[tid + st];
+    }
+    __syncthreads();
+  }
+  const long long total_pf = s_a[0];
+  const long long total = s_a[0] + s_b[0];
+  __syncthreads();
+  // More items than the workspace was sized for means the metadata broke a
+  // precondition (total_q or max_seq_len too small): run nothing.
+  if (total > max_items) {
+    if (tid == 0) *count = 0;
+    return;
+  }
+  if (tid == 0) {
+    *count = (int)total;
+    s_tot[0] = 0;
+    s_tot[1] = 0;
+  }
+  // pass 2: exclusive scans per chunk of 1024 requests, then emit
+  for (int base = 0; base < num_reqs; base += 1024) {
+    const int r = base + tid;
+    int ql = 0, L = 0;
+    long long npf = 0, ndc = 0;
+    if (r < num_reqs) {
+      ql = cu_q[r + 1] - cu_q[r];
+      L = min(seq_lens[r], len_cap);
+      if (ql > 1) npf = (long long)hkv * cdiv(ql * group, kPrefillRows);
+      else if (ql == 1) ndc = (long long)nhg * num_splits(L, kstep);
+    }
+    __syncthreads();
+    s_a[tid] = npf;
+    s_b[tid] = ndc;
+    __syncthreads();
+    for (int st = 1; st < 1024; st <<= 1) {  // inclusive Hillis-Steele scan
+      const long long xa = tid >= st ? s_a[tid - st] : 0;
+      const long long xb = tid >= st ? s_b[tid - st] : 0;
+      __syncthreads();
+      s_a[tid] += xa;
+      s_b[tid] += xb;
+      __syncthreads();
+    }
+    const long long off_pf = s_tot[0] + s_a[tid] - npf;
+    const long long off_dc = total_pf + s_tot[1] + s_b[tid] - ndc;
+    if (ql > 1) {
+      const int tiles = cdiv(ql * group, kPrefillRows);
+      for (int g = 0; g < hkv; ++g)
+        for (int k = 0; k < tiles; ++k) {
+          const long long l = off_pf + (long long)g * tiles + k;
+          items[xcd_position(l, total)] = make_int4(kItemPrefill, r, g, tiles - 1 - k);
+        }
+    } else if (ql == 1) {
+      const int S = num_splits(L, kstep);
+      for (int s = 0; s < S; ++s)
+        for (int hg = 0; hg < nhg; ++hg) {
+          const long long l = off_dc + (long long)s * nhg + hg;
+          items[xcd_position(l, total)] = make_int4(kItemDecode, r, hg, s);
+        }
+      for (int hg = 0; hg < nhg; ++hg) counters[r * nhg + hg] = 0;
+    }
+    __syncthreads();
+    if (tid == 1023) {
+      s_tot[0] += s_a[1023];
+      s_tot[1] += s_b[1023];
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+static AttnArgs make_args(const AttnHostArgs& h, const WorkspaceLayout& w) {
+  AttnArgs a{};
+  a.q = h.q;
+  a.cu_q = h.cu_seqlens_q;
+  a.q_pos = h.q_pos;
+  a.k_pool = h.k_pool;
+  a.v_pool = h.v_pool;
+  a.block_table = h.block_table;
+  a.bt_stride = h.block_table_stride;
+  a.seq_lens = h.seq_lens;
+  a.cu_k = h.cu_seqlens_k;
+  a.k_pos = h.k_pos;
+  a.cos_tab = h.cos_tab;
+  a.sin_tab = h.sin_tab;
+  a.max_pos = h.max_pos;
+  a.num_reqs = h.num_reqs;
+  a.hq = h.hq;
+  a.hkv = h.hkv;
+  a.group = h.hq / h.hkv;
+  a.num_blocks = h.num_blocks;
+  a.max_seq_len = h.max_seq_len;
+  a.s_max = w.s_max;
+  a.nhg = w.nhg;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)h.head_dim));
+  a.out = h.out;
+  unsigned char* ws = (unsigned char*)h.workspace;
+  a.ws_ml = (float2*)(ws + w.ml_off);
+  a.ws_o = (float*)(ws + w.o_off);
+  a.ws_cnt = (int*)(ws + w.counters_off);
+  a.items = (const int4*)(ws + w.items_off);
+  a.nitems = (const int*)(ws + w.count_off);
+  return a;
+}
+
+template <typename T, int D>
+static int launch_decode(const AttnArgs& a, hipStream_t s) {
+  const long long n = (long long)a.num_reqs * a.s_max * a.nhg;
+  if (n > 0x7fffffffLL) return PIC_EUNSUPPORTED;
+  hipLaunchKernelGGL((decode_kernel<T, D>), dim3((unsigned)n), dim3(kThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
+}
+
+template <typename T, int D>
+static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnHostArgs& h,
+                        hipStream_t s) {
+  if (w.max_items > 0x7fffffffLL) return PIC_EUNSUPPORTED;
+  unsigned char* ws = (unsigned char*)h.workspace;
+  const int len_cap = (int)min((long long)h.max_seq_len,
+                              (long long)h.block_table_stride * kBlockSize);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, h.cu_seqlens_q, h.seq_lens,
+                     h.num_reqs, h.hkv, h.hq / h.hkv, w.nhg, Cfg<T, D>::KSTEP, len_cap,
+                     w.max_items, (int4*)(ws + w.items_off), (int*)(ws + w.count_off),
+                     (int*)(ws + w.counters_off));
+  hipLaunchKernelGGL((mixed_kernel<T, D>), dim3((unsigned)w.max_items), dim3(kThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
+}
+
+}  // namespace pic
+
+using pic::AttnHostArgs;
+
+extern "C" int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               int block_table_stride, const int32_t* seq_lens,
+                               const int32_t* cu_seqlens_k, const int32_t* k_pos,
+                               const float* cos_tab, const float* sin_tab, int max_pos,
+                               int num_reqs, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int num_blocks, int max_seq_len, int dtype,
+                               void* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  AttnHostArgs h{q, nullptr, q_pos, k_pool, v_pool, block_table, block_table_stride, seq_lens,
+                 cu_seqlens_k, k_pos, cos_tab, sin_tab, max_pos, num_reqs, num_reqs, 1,
+                 num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len,
+                 dtype, out, workspace, workspace_bytes};
+  int st = pic::check_attn_common(h);
+  if (st || num_reqs == 0) return st;
+  const pic::WorkspaceLayout w = pic::workspace_layout(num_reqs, num_reqs, max_seq_len,
+                                                       num_q_heads, num_kv_heads, head_dim);
+  const pic::AttnArgs a = pic::make_args(h, w);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == PIC_BF16)
+    return head_dim == 128 ? pic::launch_decode<pic::bf16, 128>(a, s)
+                           : pic::launch_decode<pic::bf16, 64>(a, s);
+  return head_dim == 128 ? pic::launch_decode<float, 128>(a, s)
+                         : pic::launch_decode<float, 64>(a, s);
+}
+
+extern "C" int pic_attn_prefill(const void* q, const int32_t* cu_seqlens_q, const int32_t* q_pos,
+                                const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, int block_table_stride,
+                                const int32_t* seq_lens, const int32_t* cu_seqlens_k,
+                                const int32_t* k_pos, const float* cos_tab, const float* sin_tab,
+                                int max_pos, int num_reqs, int total_q, int max_q_len,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int num_blocks, int max_seq_len, int dtype, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  AttnHostArgs h{q, cu_seqlens_q, q_pos, k_pool, v_pool, block_table, block_table_stride,
+                 seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab, max_pos, num_reqs, total_q,
+                 max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                 max_seq_len, dtype, out, workspace, workspace_bytes};
+  int st = pic::check_attn_common(h);
+  if (st || num_reqs == 0 || total_q == 0) return st;
+  if (!cu_seqlens_q || max_q_len < 0) return PIC_EINVAL;
+  const pic::WorkspaceLayout w = pic::workspace_layout(num_reqs, total_q, max_seq_len,
+                                                       num_q_heads, num_kv_heads, head_dim);
+  const pic::AttnArgs a = pic::make_args(h, w);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == PIC_BF16)
+    return head_dim == 128 ? pic::launch_mixed<pic::bf16, 128>(a, w, h, s)
+                           : pic::launch_mixed<pic::bf16, 64>(a, w, h, s);
+  return head_dim == 128 ? pic::launch_mixed<float, 128>(a, w, h, s)
+                         : pic::launch_mixed<float, 64>(a, w, h, s);
+}

@@ -1,0 +1,42 @@
+// Host-side helpers shared by the entry points (plain C++, no HIP).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pic {
+
+struct AttnHostArgs {
+  const void* q;
+  const int32_t* cu_seqlens_q;
+  const int32_t* q_pos;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  int block_table_stride;
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_k;
+  const int32_t* k_pos;
+  const float* cos_tab;
+  const float* sin_tab;
+  int max_pos;
+  int num_reqs;
+  int total_q;
+  int max_q_len;
+  int hq;
+  int hkv;
+  int head_dim;
+  int block_size;
+  int num_blocks;
+  int max_seq_len;
+  int dtype;
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+int check_dtype_dims(int dtype, int head_dim, int block_size);
+int check_heads(int hq, int hkv);
+int check_attn_common(const AttnHostArgs& a);
+
+}  // namespace pic

@@ -1,0 +1,193 @@
+"""The C ABI without a GPU: symbols, host-side checks, workspace sizing, split policy.
+
+No call here launches a kernel: every call either fails validation before any
+launch or is pure host code.
+"""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import position_independent_kv_amd as pic
+from workloads import make_workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pic.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(pic_\w+)\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pic.library()
+    names = _declared()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(pic.EXPORTS)
+
+
+def test_status_strings():
+    for st in [0, -1, -2, -3, -4, 7]:
+        assert isinstance(pic.pic_status_string(st), str)
+    assert pic.pic_status_string(-3).startswith("PIC_EWORKSPACE")
+    assert pic.pic_version() >= 100
+
+
+def test_workspace_size_rules():
+    f = pic.pic_attn_workspace_size
+    assert f(64, 64, 4097, 32, 8, 128, pic.PIC_BF16) > 0
+    assert f(64, 64, 4097, 32, 8, 96, pic.PIC_BF16) == 0        # head_dim unsupported
+    assert f(64, 64, 4097, 30, 8, 128, pic.PIC_BF16) == 0       # Hq % Hkv
+    assert f(64, 64, 4097, 96, 2, 128, pic.PIC_BF16) == 0       # group 48 unsupported
+    assert f(1, 1, 1, 4, 4, 64, 7) == 0                        # dtype
+    # monotone in every bound
+    a = f(8, 100, 1000, 32, 8, 128, pic.PIC_BF16)
+    assert f(9, 100, 1000, 32, 8, 128, pic.PIC_BF16) >= a
+    assert f(8, 200, 1000, 32, 8, 128, pic.PIC_BF16) >= a
+    assert f(8, 100, 5000, 32, 8, 128, pic.PIC_BF16) >= a
+
+
+@pytest.mark.parametrize("dtype,kstep", [(pic.PIC_BF16, 32), (pic.PIC_F32, 16)])
+def test_split_policy(dtype, kstep):
+    for L in list(range(1, 3000)) + [4097, 8193, 131073, 131072, 65537]:
+        S = pic.pic_decode_num_splits(L, dtype)
+        c = pic.pic_decode_split_len(L, dtype)
+        assert c % kstep == 0
+        assert (S - 1) * c < L <= S * c          # every chunk non-empty, all keys covered
+        assert S <= -(-L // 512)                 # within the workspace bound
+        assert c <= 512 + kstep                  # balanced chunks near the target
+
+
+def _c_args(n):
+    return [None] * n
+
+
+def test_entry_points_reject_bad_arguments_before_launch():
+    lib = pic.library()
+    # rope table
+    assert lib.pic_rope_table(None, None, 10, 128, 1e4, None) == pic.PIC_EINVAL
+    buf = ctypes.c_void_p(1)  # never dereferenced: rejected before launch
+    assert lib.pic_rope_table(buf, buf, 10, 127, 1e4, None) == pic.PIC_EUNSUPPORTED
+    assert lib.pic_rope_table(buf, buf, 0, 128, 1e4, None) == pic.PIC_EINVAL
+    assert lib.pic_rope_table(buf, buf, 10, 128, -1.0, None) == pic.PIC_EINVAL
+    # cache write
+    assert lib.pic_cache_write(None, None, None, 0, 8, 128, 1, None, None, 4, 16, None) == 0
+    assert lib.pic_cache_write(None, None, None, 5, 8, 128, 1, None, None, 4, 16, None) == -1
+    assert lib.pic_cache_write(buf, buf, buf, 5, 8, 128, 1, buf, buf, 4, 32, None) == -2
+    assert lib.pic_cache_write(buf, buf, buf, 5, 8, 100, 1, buf, buf, 4, 16, None) == -2
+    assert lib.pic_cache_write(buf, buf, buf, 5, 8, 128, 3, buf, buf, 4, 16, None) == -2
+    # decode: null pointers, unsupported shapes, missing / short workspace
+    args = [buf] * 5 + [300] + [buf] * 5 + [4097, 4, 32, 8, 128, 16, 100, 4097, 1] + [buf, None, 0,
+                                                                                   None]
+    assert lib.pic_attn_decode(*args) == pic.PIC_EWORKSPACE
+    args2 = list(args)
+    args2[22] = 1000  # workspace_bytes
+    args2[21] = buf
+    assert lib.pic_attn_decode(*args2) == pic.PIC_EWORKSPACE
+    args3 = list(args)
+    args3[0] = None
+    assert lib.pic_attn_decode(*args3) == pic.PIC_EINVAL
+    args4 = list(args)
+    args4[13] = 30  # Hq not a multiple of Hkv
+    assert lib.pic_attn_decode(*args4) == pic.PIC_EUNSUPPORTED
+    args5 = list(args)
+    args5[5] = 10  # block table too narrow for max_seq_len
+    assert lib.pic_attn_decode(*args5) == pic.PIC_EINVAL
+    # empty batch is a no-op
+    args6 = list(args)
+    args6[12] = 0
+    assert lib.pic_attn_decode(*args6) == pic.PIC_OK
+    # prefill
+    pargs = [buf] * 6 + [300] + [buf] * 5 + [4097, 4, 40, 16, 32, 8, 128, 16, 100, 4097, 1] + [
+        buf, None, 0, None]
+    assert lib.pic_attn_prefill(*pargs) == pic.PIC_EWORKSPACE
+    pargs[1] = None
+    pargs[24] = buf
+    pargs[25] = 1 << 40
+    assert lib.pic_attn_prefill(*pargs) == pic.PIC_EINVAL
+
+
+def test_validate_metadata_accepts_configs():
+    for name in ["c1a", "c1d", "c2", "c3", "c4", "c5"]:
+        w = make_workload(name, values=False)
+        st, msg = pic.pic_validate_metadata(
+            None if w.kind == "decode" else w.cu_seqlens_q, w.q_pos, w.block_table, w.seq_lens,
+            w.cu_seqlens_k, w.k_pos, w.max_seq_len, w.max_pos, w.num_blocks)
+        assert st == pic.PIC_OK, (name, msg)
+
+
+def test_validate_metadata_catches_violations():
+    w = make_workload("c1a")
+    base = dict(cu_seqlens_q=w.cu_seqlens_q, q_pos=w.q_pos, block_table=w.block_table,
+                seq_lens=w.seq_lens, cu_seqlens_k=w.cu_seqlens_k, k_pos=w.k_pos,
+                max_seq_len=w.max_seq_len, max_pos=w.max_pos, num_blocks=w.num_blocks)
+
+    def check(**kw):
+        a = dict(base)
+        a.update(kw)
+        return pic.pic_validate_metadata(**a)
+
+    assert check()[0] == pic.PIC_OK
+    bt = w.block_table.copy()
+    bt[1, 2] = w.num_blocks
+    st, msg = check(block_table=bt)
+    assert st == pic.PIC_EINVAL and "block id" in msg
+    kp = w.k_pos.copy()
+    kp[3] = w.max_pos
+    assert "key position" in check(k_pos=kp)[1]
+    qp = w.q_pos.copy()
+    qp[0] = -1
+    assert "query position" in check(q_pos=qp)[1]
+    assert "seq_len" in check(max_seq_len=79)[1]
+    sl = w.seq_lens.copy()
+    sl[0] = 10
+    assert check(seq_lens=sl)[0] == pic.PIC_EINVAL
+    assert "stride" in check(block_table=w.block_table[:, :3])[1]
+
+
+def test_host_code_under_sanitizers(tmp_path):
+    """Build the host-only part with g++ -fsanitize=address,undefined and drive it."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    main = tmp_path / "main.cpp"
+    main.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "pic.h"
+int main() {
+  int fails = 0;
+  for (int s = -6; s <= 1; ++s) if (!pic_status_string(s)) ++fails;
+  for (int L = 0; L < 200000; L += 37) {
+    int S = pic_decode_num_splits(L, 1), c = pic_decode_split_len(L, 1);
+    if (L > 0 && ((S - 1) * c >= L || S * c < L)) ++fails;
+  }
+  if (pic_attn_workspace_size(1000, 100000, 200000, 64, 8, 128, 1) == 0) ++fails;
+  int cu_q[3] = {0, 2, 3}, q_pos[3] = {5, 6, 9}, bt[6] = {0, 1, 0, 2, 3, 1}, sl[2] = {7, 10};
+  int cu_k[3] = {0, 7, 17}, k_pos[17];
+  for (int i = 0; i < 17; ++i) k_pos[i] = i;
+  char msg[64];
+  if (pic_validate_metadata(cu_q, q_pos, bt, 3, sl, cu_k, k_pos, 2, 3, 10, 20, 4, 4, msg, 64) != 0) ++fails;
+  bt[4] = 9;
+  if (pic_validate_metadata(cu_q, q_pos, bt, 3, sl, cu_k, k_pos, 2, 3, 10, 20, 4, 4, msg, 8) == 0) ++fails;
+  if (strlen(msg) > 7) ++fails;
+  printf("fails=%d\n", fails);
+  return fails;
+}
+''')
+    exe = tmp_path / "host_test"
+    src = os.path.join(ROOT, "position_independent_kv_amd", "csrc", "pic_host.cpp")
+    cmd = [gxx, "-std=c++17", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", os.path.join(ROOT, "include"), src, str(main), "-o", str(exe)]
+    subprocess.run(cmd, check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "fails=0" in res.stdout

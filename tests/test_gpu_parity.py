@@ -1,0 +1,207 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Tolerances (max abs error on outputs of magnitude <~ 1): 1e-4 for float32
+inputs; 2e-2 for bfloat16 inputs, where the rotated keys and queries and the
+probabilities are rounded to bfloat16 before the matrix-core products and the
+output is rounded to bfloat16.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import position_independent_kv_amd as pic
+from tests.gpu_harness import (DeviceWorkload, oracle_outputs, oracle_pools, run_workload,
+                               select_rows, to_f64)
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _maxerr(a, b):
+    return float(np.abs(a - b).max())
+
+
+# ---------------------------------------------------------------------------
+# table and cache write
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("max_pos,d,base", [(2128, 64, 10000.0), (131073, 128, 500000.0),
+                                            (4097, 128, 500000.0)])
+def test_rope_table_within_one_ulp(max_pos, d, base):
+    torch = _torch()
+    c = torch.empty((max_pos, d // 2), dtype=torch.float32, device="cuda")
+    s = torch.empty_like(c)
+    pic.pic_rope_table(c, s, base)
+    rc, rs = oracle.rope_table(max_pos, d, base)
+    # Bound: one float32 ulp of the value, plus the float64 uncertainty of the
+    # angle itself (theta_i from two libm pow()s may differ by an ulp, and near
+    # a zero of cos or sin an angle error da moves the value by |da|).
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * oracle.rope_frequencies(d, base)[None]
+    slack = 4.0 * np.spacing(ang)
+    for what, got, ref in [("cos", c.cpu().numpy(), rc), ("sin", s.cpu().numpy(), rs)]:
+        ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+        ulp = np.minimum(ulp, np.spacing(np.nextafter(np.abs(ref).astype(np.float32),
+                                                      np.float32(0))).astype(np.float64))
+        ratio = np.abs(got.astype(np.float64) - ref) / (ulp + slack)
+        i = np.unravel_index(np.argmax(ratio), ratio.shape)
+        assert ratio[i] <= 1.0, (f"{what}[{i}] = {got[i]!r} vs fp64 {ref[i]!r}: "
+                                 f"{ratio[i]:.2f} x bound; {(ratio > 1).sum()} elements over")
+
+
+@pytest.mark.parametrize("name", ["c1a", "small_bf16"])
+def test_cache_write_readback_bit_exact(name):
+    torch = _torch()
+    w = make_workload("c1a") if name == "c1a" else make_workload(
+        "x", builder="decode", seed=11, R=5, seg_len=48, n_seg=3, n_shared=1, n_spans=5)
+    dw = DeviceWorkload(w)
+    dw.write_new_tokens()
+    torch.cuda.synchronize()
+    kp, vp = oracle_pools(w)
+    written = np.zeros(w.num_blocks * w.block_size, bool)
+    written[np.concatenate([w.ctx_slots, w.new_slots])] = True
+    wk = written.reshape(w.num_blocks, w.block_size)
+    if w.dtype == "bf16":
+        gk = dw.k_pool.view(torch.int16).cpu().numpy().view(np.uint16)
+        gv = dw.v_pool.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        gk = dw.k_pool.cpu().numpy()
+        gv = dw.v_pool.cpu().numpy()
+    for b in range(w.num_blocks):
+        for o in range(w.block_size):
+            if wk[b, o]:  # same bytes as the oracle's placement
+                for g_, o_ in [(gk[b, :, o, :], kp[b, :, o, :]), (gv[b, :, :, o], vp[b, :, :, o])]:
+                    assert np.array_equal(np.ascontiguousarray(g_).view(np.uint8),
+                                          np.ascontiguousarray(o_).view(np.uint8))
+            else:  # untouched slots keep the NaN fill
+                assert np.all(np.isnan(dw.k_pool[b, :, o, :].float().cpu().numpy()))
+                assert np.all(np.isnan(dw.v_pool[b, :, :, o].float().cpu().numpy()))
+
+
+# ---------------------------------------------------------------------------
+# the tiny fp32 config: one span shared at logical offsets 0 and 2048
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c1a", "c1b", "c1d"])
+def test_tiny_fp32_parity(name):
+    w = make_workload(name)
+    got = run_workload(w)
+    ref = oracle_outputs(w)
+    assert _maxerr(got, ref) <= TOL["f32"]
+
+
+def test_tiny_shared_span_two_offsets_agree():
+    """c1a: identical suffixes over one span at offsets 0 and 2048 -> same outputs."""
+    got = run_workload(make_workload("c1a"))
+    assert _maxerr(got[:16], got[16:]) <= 1e-4
+
+
+def test_tiny_decode_replay_matches_prefill():
+    a = run_workload(make_workload("c1a"))
+    d = run_workload(make_workload("c1d"))
+    assert _maxerr(a, d) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# small bf16 batches: full parity, several tiles, ragged tails
+# ---------------------------------------------------------------------------
+
+SMALL = {
+    "decode": dict(builder="decode", seed=21, R=9, seg_len=96, n_seg=4, n_shared=2, n_spans=6),
+    "decode_long": dict(builder="decode", seed=22, R=3, seg_len=1120, n_seg=2, n_shared=1,
+                        n_spans=3),
+    "decode_g8_d64": dict(builder="decode", seed=23, R=5, seg_len=64, n_seg=3, n_shared=1,
+                          n_spans=5, hq=16, hkv=2, d=64),
+    "decode_g1": dict(builder="decode", seed=24, R=4, seg_len=32, n_seg=2, n_shared=0,
+                      n_spans=0, hq=4, hkv=4),
+    "decode_f32_d128": dict(builder="decode", seed=25, R=4, seg_len=544, n_seg=2, n_shared=1,
+                            n_spans=4, dtype="f32"),
+    "prefill": dict(builder="prefill", seed=31, R=3, n_spans=5, span_len=48, per_req=2, q_len=70),
+    "prefill_long_q": dict(builder="prefill", seed=32, R=2, n_spans=3, span_len=160, per_req=2,
+                           q_len=300),
+    "prefill_g16": dict(builder="prefill", seed=33, R=2, n_spans=3, span_len=32, per_req=2,
+                        q_len=21, hq=32, hkv=2),
+    "prefill_f32_d128": dict(builder="prefill", seed=34, R=2, n_spans=3, span_len=64, per_req=2,
+                             q_len=40, dtype="f32"),
+    "mixed": dict(builder="mixed", seed=41, n_chunks=4, chunk=96, n_dec=10, per_dec=2),
+    "mixed_g2_d64": dict(builder="mixed", seed=42, n_chunks=3, chunk=160, n_dec=7, per_dec=2,
+                         hq=8, hkv=4, d=64),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_small_parity(case):
+    kw = dict(SMALL[case])
+    w = make_workload(case, **kw)
+    got = run_workload(w)
+    ref = oracle_outputs(w)
+    err = _maxerr(got, ref)
+    print(f"{case}: max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+# ---------------------------------------------------------------------------
+# full-size configs, sampled outputs
+# ---------------------------------------------------------------------------
+
+def _sampled(name, requests, rows=None):
+    w = make_workload(name)
+    got = run_workload(w)
+    ref = oracle_outputs(w, requests=requests, rows=rows)
+    err = _maxerr(select_rows(got, w, requests, rows), ref)
+    print(f"{name}: max abs err {err:.3e} on {len(ref)} rows")
+    assert np.isfinite(got).all()
+    assert err <= TOL[w.dtype]
+
+
+def test_full_c2_decode_sampled():
+    _sampled("c2", [0, 17, 63])
+
+
+def test_full_c2p_decode_sampled():
+    _sampled("c2p", [5, 40])
+
+
+def test_full_c3_prefill_sampled():
+    rows = {0: [0, 1, 255, 511], 5: [17, 300, 511]}
+    _sampled("c3", [0, 5], rows)
+
+
+def test_full_c4_long_decode_sampled():
+    _sampled("c4", [2])
+
+
+def test_full_c5_mixed_sampled():
+    w = make_workload("c5", values=False)
+    ql = w.q_lens()
+    pre = [int(r) for r in np.nonzero(ql > 1)[0][:2]]
+    dec = [int(r) for r in np.nonzero(ql == 1)[0][:3]]
+    rows = {pre[0]: [0, 1, 1000, 2047], pre[1]: [5, 2046]}
+    _sampled("c5", pre + dec, rows)
+
+
+# ---------------------------------------------------------------------------
+# sanity of the harness itself: a wrong input must fail the comparison
+# ---------------------------------------------------------------------------
+
+def test_negative_control_prerotated_keys_fail():
+    """Feeding keys already rotated to their positions (what a rotated cache
+    holds) into the position-free kernel must NOT match the oracle."""
+    w = make_workload("c1a")
+    kp, vp = oracle_pools(w)
+    B = w.block_size
+    rot = w.ctx_k.astype(np.float64)
+    # keys of the span as request A would have cached them (positions 0..63)
+    rot = oracle.rotate_half(rot, np.arange(64)[:, None], w.d, w.base).astype(np.float32)
+    w2 = make_workload("c1a")
+    w2.ctx_k = rot
+    got = run_workload(w2)
+    ref = oracle_outputs(w)
+    assert _maxerr(got, ref) > 1e-2

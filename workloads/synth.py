@@ -309,11 +309,13 @@ def _assign_spans(struct, n_req, uses_per_req, n_spans, uses_per_span):
 
 
 def _decode(name, seed, R, seg_len, n_seg, n_shared, n_spans, hq=32, hkv=8, d=128, B=16,
-            base=500000.0, description=""):
+            base=500000.0, description="", dtype="bf16"):
     """Decode batch: contexts of n_seg segments (n_shared of them shared spans) + new token."""
+    # spans are padded to block boundaries (MiniPIC §2.2, Padding primitive)
+    assert seg_len % B == 0, "composed segments must fill whole blocks"
     data = np.random.default_rng(seed)
     struct = np.random.default_rng(100 + seed)
-    pool = _Pool(hkv, d, B, "bf16", data)
+    pool = _Pool(hkv, d, B, dtype, data)
     spans = [pool.segment(seg_len) for _ in range(n_spans)]
     uses = (R * n_shared) // n_spans if n_spans else 0
     assign = _assign_spans(struct, R, n_shared, n_spans, uses) if n_shared else None
@@ -333,16 +335,17 @@ def _decode(name, seed, R, seg_len, n_seg, n_shared, n_spans, hq=32, hkv=8, d=12
         requests.append(dict(blocks=blocks, seq_len=L, k_pos=np.arange(L)))
     new_tokens = [(r, n_seg * seg_len) for r in range(R)]
     q_rows = [(r, n_seg * seg_len) for r in range(R)]
-    return _finish(name, "decode", "bf16", hq, hkv, d, B, base, pool, struct, data,
+    return _finish(name, "decode", dtype, hq, hkv, d, B, base, pool, struct, data,
                    requests, new_tokens, q_rows, description)
 
 
 def _chunked_prefill(seed=3, R=8, n_spans=16, span_len=1024, per_req=4, q_len=512,
-                     hq=32, hkv=8, d=128, B=16, base=500000.0):
+                     hq=32, hkv=8, d=128, B=16, base=500000.0, dtype="bf16"):
     """8 requests x (4 distinct seeded spans of 1024 in seeded order + 512 causal suffix queries)."""
+    assert span_len % B == 0, "composed spans must fill whole blocks"
     data = np.random.default_rng(seed)
     struct = np.random.default_rng(100 + seed)
-    pool = _Pool(hkv, d, B, "bf16", data)
+    pool = _Pool(hkv, d, B, dtype, data)
     spans = [pool.segment(span_len) for _ in range(n_spans)]
     requests, new_tokens, q_rows = [], [], []
     for r in range(R):
@@ -354,7 +357,7 @@ def _chunked_prefill(seed=3, R=8, n_spans=16, span_len=1024, per_req=4, q_len=51
         requests.append(dict(blocks=blocks, seq_len=L, k_pos=np.arange(L)))
         new_tokens += [(r, ctx + i) for i in range(q_len)]
         q_rows += [(r, ctx + i) for i in range(q_len)]
-    return _finish("c3", "prefill", "bf16", hq, hkv, d, B, base, pool, struct, data,
+    return _finish("c3", "prefill", dtype, hq, hkv, d, B, base, pool, struct, data,
                    requests, new_tokens, q_rows, _chunked_prefill.__doc__.strip())
 
 
@@ -379,12 +382,13 @@ def _long_decode(seed=4, R=4, n_spans=64, span_len=2048, hq=32, hkv=8, d=128, B=
 
 
 def _mixed(seed=5, n_chunks=16, chunk=2048, n_dec=128, per_dec=4, hq=32, hkv=8, d=128, B=16,
-           base=500000.0):
+           base=500000.0, dtype="bf16"):
     """One launch: 16 span-prefill chunks of 2048 (causal within the span) + 128 decodes of
     8192-token contexts built from 4 of those spans each; request order is shuffled."""
+    assert chunk % B == 0, "composed spans must fill whole blocks"
     data = np.random.default_rng(seed)
     struct = np.random.default_rng(100 + seed)
-    pool = _Pool(hkv, d, B, "bf16", data)
+    pool = _Pool(hkv, d, B, dtype, data)
     span_blocks = [pool.empty_blocks(chunk // B) for _ in range(n_chunks)]
     reqs = []
     for c in range(n_chunks):
@@ -406,7 +410,7 @@ def _mixed(seed=5, n_chunks=16, chunk=2048, n_dec=128, per_dec=4, hq=32, hkv=8, 
         else:
             new_tokens.append((idx, per_dec * chunk))
             q_rows.append((idx, per_dec * chunk))
-    return _finish("c5", "prefill", "bf16", hq, hkv, d, B, base, pool, struct, data,
+    return _finish("c5", "prefill", dtype, hq, hkv, d, B, base, pool, struct, data,
                    requests, new_tokens, q_rows, _mixed.__doc__.strip().replace("\n    ", " "))
 
 
