@@ -1,0 +1,282 @@
+"""Benchmark: one serving step of position-free paged attention on one MI355X.
+
+A step is the whole hot path over one batch: write the step's new (unrotated)
+K/V into the paged cache (pic_cache_write), then one attention launch over
+every request's context (pic_attn_decode for decode batches, pic_attn_prefill
+for prefill / mixed batches).  The rotary table is built once at setup
+(pic_rope_table) and timed separately.  Inputs are seeded synthetic data
+resident in HBM before the timed region.
+
+Default workload: 64 decode requests x (4096-token context + 1 new token),
+Llama-3-8B layer shape (32 q / 8 kv heads, d 128, bf16), half of every
+context in spans shared at different logical offsets.
+
+Prints ONE JSON line on stdout; everything else goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak (256 CU x 4096 flop/clk x 2.4 GHz)
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix peak
+
+WORKLOAD_TEXT = {
+    "c2": "decode 64 x (4096-token context + 1 new token), 2 of 4 1024-token segments shared "
+          "spans, Llama-3-8B layer (32q/8kv, d128), bf16",
+    "c2p": "decode 64 x (4096 + 1), all blocks private (control)",
+    "c3": "chunked prefill 8 x (4 shared 1024-token spans + 512 causal suffix queries)",
+    "c4": "long decode 4 x (131072-token context of 64 shared 2048-token spans + 1 new token)",
+    "c5": "mixed single launch: 16 x 2048-token causal span prefills + 128 decodes of 8192+1",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources: traffic counters are only valid for this exact code."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "position_independent_kv_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def step_counts(w, counts):
+    """Bytes of the whole step: attention's algorithmic bytes + the new tokens' K/V read+write."""
+    es = 2 if w.dtype == "bf16" else 4
+    cw = 2 * 2 * w.new_k.shape[0] * w.hkv * w.d * es + 4 * w.new_k.shape[0]
+    return counts["bytes"] + cw
+
+
+def time_config(name, steps, warmup, with_rows=False):
+    import torch
+
+    import position_independent_kv_amd as pic
+    from tests.gpu_harness import DeviceWorkload
+    from workloads import algorithmic_counts, make_workload
+
+    t = time.time()
+    w = make_workload(name)
+    counts = algorithmic_counts(w)
+    dw = DeviceWorkload(w)
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: built in {time.time() - t:.1f}s; "
+        f"{counts['bytes'] / 1e9:.3f} GB, {counts['flops'] / 1e12:.3f} TFLOP per attention call")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        dw.step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        dw.write_new_tokens()
+        ev[k][0].record(stream)
+        dw.attention()
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ms = (t1 - t0) * 1e3 / steps
+    res = dict(name=name, w=w, counts=counts, step_ms=step_ms, kernel_ms=kern_ms,
+               step_bytes=step_counts(w, counts))
+    if with_rows:
+        # the other rows of the path, timed on their own (same stream, events)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        cos = torch.empty_like(dw.cos)
+        sin = torch.empty_like(dw.sin)
+        e[0].record(stream)
+        for _ in range(5):
+            pic.pic_rope_table(cos, sin, w.base)
+        e[1].record(stream)
+        for _ in range(5):
+            dw.write_new_tokens()
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        res["rope_table_ms"] = e[0].elapsed_time(e[1]) / 5
+        res["cache_write_ms"] = e[1].elapsed_time(e[2]) / 5
+        assert torch.equal(cos, dw.cos) and torch.equal(sin, dw.sin)
+    del dw
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, counts, budget_s=12.0):
+    """The fp64 oracle on the host: a bounded sample of the same step."""
+    import oracle
+    from tests.oracle_harness import oracle_pools
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    kp, vp = oracle_pools(w)
+
+    def run(reqs):
+        t = time.perf_counter()
+        oracle.attention(w.q, w.cu_seqlens_q, w.q_pos, kp, vp, w.block_table, w.seq_lens,
+                         w.cu_seqlens_k, w.k_pos, w.base, w.block_size, requests=reqs)
+        return time.perf_counter() - t
+
+    t1 = run([0])
+    n = int(max(1, min(w.num_reqs, budget_s / max(t1, 1e-6))))
+    reqs = list(range(n))
+    dt = run(reqs)
+    frac_bytes = counts["kv_bytes"] * n / w.num_reqs  # KV dominates; the rest is per request too
+    frac = counts["bytes"] * n / w.num_reqs
+    _ = frac_bytes
+    cpu = os.popen("lscpu 2>/dev/null | grep 'Model name' | head -1").read().strip()
+    return {"value": frac / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {w.num_reqs} requests of the {w.name} attention call "
+                      f"({dt:.1f} s, numpy fp64, {threads} BLAS threads; {cpu})"}
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if still valid."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        data = json.load(f)
+    ent = data.get(kernel)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent["bytes_per_launch"]
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling the PMC byte counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {nbytes} bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--others", default="c2p,c3,c4,c5",
+                    help="comma list of further configs reported under 'configs' ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="only run a plain copy of this many bytes (PMC scaling run)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the per-GPU path is what one GPU can show; sharding is described in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return
+
+    main_res = time_config(args.config, args.steps, args.warmup, with_rows=True)
+    w, counts = main_res["w"], main_res["counts"]
+    decode = w.kind == "decode"
+    kernel = "decode_kernel" if decode else "mixed_kernel"
+    if decode:
+        achieved = counts["bytes"] / (main_res["kernel_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+        value = main_res["step_bytes"] / (main_res["step_ms"] * 1e-3) / 1e9
+        metric = "decode HBM GB/s"
+        unit = "GB/s"
+    else:
+        achieved = counts["flops"] / (main_res["kernel_ms"] * 1e-3) / 1e12
+        peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+        value = counts["flops"] / (main_res["step_ms"] * 1e-3) / 1e12
+        metric = "prefill TFLOP/s"
+        unit = "TFLOP/s"
+    tb = load_traffic(kernel + ":" + args.config)
+    roof["traffic"] = tb
+    roof["kernel"] = kernel
+    roof["kernel_ms"] = main_res["kernel_ms"]
+    roof["algorithmic_bytes"] = counts["bytes"]
+    roof["algorithmic_flops"] = counts["flops"]
+
+    others = {}
+    for name in [x for x in args.others.split(",") if x]:
+        if name == args.config:
+            continue
+        r = time_config(name, max(5, args.steps // 5), 2)
+        c = r["counts"]
+        others[name] = {
+            "workload": WORKLOAD_TEXT[name],
+            "kernel_ms": r["kernel_ms"], "step_ms": r["step_ms"],
+            "kernel_GBps": c["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9,
+            "kernel_hbm_frac": c["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_TFLOPs": c["flops"] / (r["kernel_ms"] * 1e-3) / 1e12,
+            "kernel_mfma_frac": c["flops"] / (r["kernel_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "unique_kv_bytes": c["unique_kv_bytes"], "algorithmic_bytes": c["bytes"],
+            "flops": c["flops"],
+        }
+        log(f"[bench] {name}: kernel {r['kernel_ms'] * 1e3:.1f} us, "
+            f"{others[name]['kernel_GBps']:.0f} GB/s, {others[name]['kernel_TFLOPs']:.1f} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t = time.time()
+        cpu = cpu_baseline(w, counts)
+        log(f"[bench] cpu baseline in {time.time() - t:.1f}s: {cpu}")
+
+    out = {
+        "metric": f"position-free paged attn: {metric}",
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q; no dataset or weights)",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
+                   "requests": w.num_reqs, "query_rows": w.total_q,
+                   "max_seq_len": w.max_seq_len, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "head_dim": w.d, "block_size": w.block_size, "rope_base": w.base,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "rows": {"rope_table_ms": main_res["rope_table_ms"],
+                 "cache_write_ms": main_res["cache_write_ms"],
+                 "attention_kernel_ms": main_res["kernel_ms"]},
+        "configs": others,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

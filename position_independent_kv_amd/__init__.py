@@ -20,7 +20,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpic.so")
+# PIC_LIBRARY may name another build of the same library (same ABI).
+LIB_PATH = os.environ.get("PIC_LIBRARY") or os.path.join(HERE, "libpic.so")
 
 PIC_OK, PIC_EINVAL, PIC_EUNSUPPORTED, PIC_EWORKSPACE, PIC_EHIP = 0, -1, -2, -3, -4
 PIC_F32, PIC_BF16 = 0, 1

@@ -37,7 +37,9 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
-#include "../../include/pic.h"
+#include <type_traits>
+
+#include "pic.h"
 #include "pic_common.hpp"
 #include "pic_device.hpp"
 #include "pic_host.hpp"
@@ -70,7 +72,6 @@ struct AttnArgs {
   void* out;
   float2* ws_ml;
   float* ws_o;
-  int* ws_cnt;
   const int4* items;
   const int* nitems;
 };
@@ -114,14 +115,42 @@ __device__ __forceinline__ void rotate_ops(OpT<T>* x, const float* cs, const flo
   using M = Mma<T>;
 #pragma unroll
   for (int c = 0; c < C::NH; ++c) {
+    float lo[C::KPL], hi[C::KPL];
 #pragma unroll
     for (int e = 0; e < C::KPL; ++e) {
-      const float lo = M::get(x[c], e);
-      const float hi = M::get(x[c + C::NH], e);
+      const float a = M::get(x[c], e);
+      const float b = M::get(x[c + C::NH], e);
       const float co = cs[c * C::KPL + e], si = sn[c * C::KPL + e];
-      M::set(x[c], e, lo * co - hi * si);
-      M::set(x[c + C::NH], e, hi * co + lo * si);
+      lo[e] = a * co - b * si;
+      hi[e] = b * co + a * si;
     }
+    x[c] = M::pack(lo);
+    x[c + C::NH] = M::pack(hi);
+  }
+}
+
+// Same rotation with the cos/sin values read from an LDS table row, one
+// chunk at a time (cs/sn point at the lane's first pair of the row).
+template <typename T, int D>
+__device__ __forceinline__ void rotate_from_lds(OpT<T>* x, const float* cs, const float* sn) {
+  using C = Cfg<T, D>;
+  using M = Mma<T>;
+  typedef Run<float, C::KPL> RF;
+#pragma unroll
+  for (int c = 0; c < C::NH; ++c) {
+    const typename RF::V cv = RF::load(cs + c * C::KCH);
+    const typename RF::V sv = RF::load(sn + c * C::KCH);
+    float lo[C::KPL], hi[C::KPL];
+#pragma unroll
+    for (int e = 0; e < C::KPL; ++e) {
+      const float a = M::get(x[c], e);
+      const float b = M::get(x[c + C::NH], e);
+      const float co = elem<float, C::KPL>(cv, e), si = elem<float, C::KPL>(sv, e);
+      lo[e] = a * co - b * si;
+      hi[e] = b * co + a * si;
+    }
+    x[c] = M::pack(lo);
+    x[c + C::NH] = M::pack(hi);
   }
 }
 
@@ -148,9 +177,14 @@ __device__ __forceinline__ void load_query(const AttnArgs& a, long long qrow, in
 // ---------------------------------------------------------------------------
 
 // s[t][i]: masked scores (base-2 units, -inf where masked) of keys
-// key_of(t, grp*4+i) for this lane's column.  Updates the running max m
-// (identical in the four lanes of a column) and the lane-partial sum l,
-// rescales acc, and overwrites s with the probabilities.
+// key_of(t, grp*4+i) for this lane's column.  Keeps a running base m per
+// column (identical in the column's four lanes) and a lane-partial sum l,
+// and overwrites s with 2^(s - m).  The base is only raised (and acc, l
+// rescaled) when some column's new maximum exceeds it by more than
+// kRescaleSlack, so most steps skip the rescale; the probabilities stay
+// <= 2^kRescaleSlack and the final o = acc / l is unchanged.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int NT, int ND>
 __device__ __forceinline__ void softmax_step(f32x4 (&s)[NT], f32x4 (&acc)[ND], float& m,
                                              float& l) {
@@ -161,9 +195,15 @@ __device__ __forceinline__ void softmax_step(f32x4 (&s)[NT], f32x4 (&acc)[ND], f
     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][i]);
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m, mx);
-  const float base = (m_new == -INFINITY) ? 0.0f : m_new;
-  const float alpha = fast_exp2(m - base);
+  if (__any(mx > m + kRescaleSlack)) {
+    const float m_new = fmaxf(m, mx);
+    const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) acc[dt] *= alpha;
+    m = m_new;
+  }
+  const float base = (m == -INFINITY) ? 0.0f : m;
   float psum = 0.0f;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -173,10 +213,7 @@ __device__ __forceinline__ void softmax_step(f32x4 (&s)[NT], f32x4 (&acc)[ND], f
       s[t][i] = p;
       psum += p;
     }
-  l = l * alpha + psum;
-  m = m_new;
-#pragma unroll
-  for (int dt = 0; dt < ND; ++dt) acc[dt] *= alpha;
+  l += psum;
 }
 
 // B operand of PV MFMA number mi: probabilities of keys grp*4*NT + mi*KPL + e.
@@ -184,13 +221,13 @@ template <typename T, int D>
 __device__ __forceinline__ typename Mma<T>::Op pack_probs(const f32x4 (&s)[Cfg<T, D>::NT],
                                                           int mi) {
   using C = Cfg<T, D>;
-  typename Mma<T>::Op p;
+  float p[C::KPL];
 #pragma unroll
   for (int e = 0; e < C::KPL; ++e) {
     const int idx = mi * C::KPL + e;
-    Mma<T>::set(p, e, s[idx / 4][idx % 4]);
+    p[e] = s[idx / 4][idx % 4];
   }
-  return p;
+  return Mma<T>::pack(p);
 }
 
 __device__ __forceinline__ float col_sum(float l) {
@@ -217,125 +254,73 @@ __device__ __forceinline__ void store4(T* p, f32x4 v, float scale) {
 // decode: one wave = (request r, kv head g, keys [k0, k1)), q row qrow
 // ---------------------------------------------------------------------------
 
+// Per-lane addresses of one decode step: the block and offset of the key row
+// each score tile's A operand needs, and the block of each PV run.
+template <int NT>
+struct KAddr {
+  int blk[NT];
+  int off[NT];
+};
+template <int NPV>
+struct VAddr {
+  int blk[NPV];
+};
+
 template <typename T, int D>
-__device__ void decode_wave(const AttnArgs& a, int r, int g, long long qrow, int k0, int k1,
-                            int L, f32x4 (&acc)[Cfg<T, D>::ND], float& m_run, float& l_run) {
+__device__ __forceinline__ void k_addr(const int32_t* bt, int kb, int L, int row16, int nb_max,
+                                       KAddr<Cfg<T, D>::NT>& A) {
+  using C = Cfg<T, D>;
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t) {
+    const int kc = min(kb + key_of<C::NT>(t, row16), L - 1);
+    A.blk[t] = clampi(bt[kc >> 4], 0, nb_max);
+    A.off[t] = kc & 15;
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void v_addr(const int32_t* bt, int kb, int L, int grp, int nb_max,
+                                       VAddr<Cfg<T, D>::NPV>& A) {
+  using C = Cfg<T, D>;
+#pragma unroll
+  for (int mi = 0; mi < C::NPV; ++mi) {
+    const int vkc = min(kb + grp * 4 * C::NT + mi * C::KPL, L - 1);
+    A.blk[mi] = clampi(bt[vkc >> 4], 0, nb_max);
+  }
+}
+
+// LDS of a decode workgroup: the cos/sin rows of the current and the next
+// step (one row per key of the step), shared by the workgroup's kv heads.
+template <typename T, int D>
+struct DecodeSmem {
+  static constexpr int KSTEP = Cfg<T, D>::KSTEP;
+  static constexpr int TLD = D / 2 + 4;  // padded row: spreads the 16 rows a load reads over banks
+  float cs[2][KSTEP][TLD];
+  float sn[2][KSTEP][TLD];
+};
+
+// One decode work item: request r, key chunk s, kv heads hg*4 .. hg*4+3 (one
+// per wave).  All four waves walk the same keys, so each step's table rows
+// are fetched once per workgroup (one step ahead, double-buffered in LDS) and
+// every wave reads its own K and V rows straight from the pools.  With one
+// chunk the wave writes the output row; otherwise it writes a normalised
+// partial and (max, sum) that combine_kernel merges.  Uniform across the
+// workgroup.
+template <typename T, int D>
+__device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long qrow,
+                            unsigned char* smem_raw) {
   using C = Cfg<T, D>;
   using M = Mma<T>;
   typedef typename M::Op Op;
-  const int lane = threadIdx.x & 63;
-  const int row16 = lane & 15;
-  const int grp = lane >> 4;
-  const int G = a.group;
-
-  Op qop[C::NC];
-  const bool qvalid = row16 < G;
-  load_query<T, D>(a, qrow, g * G + (qvalid ? row16 : 0), a.q_pos[qrow], qvalid, grp, qop);
-
-  const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
-  const int32_t* kp = a.k_pos + a.cu_k[r];
-  const T* kpool = (const T*)a.k_pool;
-  const T* vpool = (const T*)a.v_pool;
-  const int nb_max = a.num_blocks - 1;
-  const int pmax = a.max_pos - 1;
-
-#pragma unroll
-  for (int dt = 0; dt < C::ND; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  m_run = -INFINITY;
-  l_run = 0.0f;
-
-  for (int kb = k0; kb < k1; kb += C::KSTEP) {
-    f32x4 s[C::NT];
-    // scores: lane loads and rotates the key of its A row in each tile
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
-      const int kc = min(kb + key_of<C::NT>(t, row16), L - 1);
-      const int blk = clampi(bt[kc >> 4], 0, nb_max);
-      const int pos = clampi(kp[kc], 0, pmax);
-      const T* krow = kpool + (((size_t)blk * a.hkv + g) * kBlockSize + (kc & 15)) * D +
-                      grp * C::KPL;
-      Op kop[C::NC];
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) kop[c] = M::load(krow + c * C::KCH);
-      float cs[C::NH * C::KPL], sn[C::NH * C::KPL];
-      load_trig<T, D>(a, pos, grp, cs, sn);
-      rotate_ops<T, D>(kop, cs, sn);
-      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) s[t] = M::run(kop[c], qop[c], s[t]);
-    }
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + key_of<C::NT>(t, grp * 4 + i);
-        s[t][i] = key < k1 ? s[t][i] * a.scale_log2 : -INFINITY;
-      }
-    softmax_step<C::NT, C::ND>(s, acc, m_run, l_run);
-    // O^T += V^T P^T
-#pragma unroll
-    for (int mi = 0; mi < C::NPV; ++mi) {
-      const Op p = pack_probs<T, D>(s, mi);
-      const int vkey = kb + grp * 4 * C::NT + mi * C::KPL;  // first of KPL keys
-      const int vkc = min(vkey, L - 1);
-      const int vblk = clampi(bt[vkc >> 4], 0, nb_max);
-      const T* vrow = vpool + (((size_t)vblk * a.hkv + g) * D + row16) * kBlockSize + (vkey & 15);
-      const bool tail = vkey + C::KPL > L;
-#pragma unroll
-      for (int dt = 0; dt < C::ND; ++dt) {
-        Op v = M::load(vrow + (size_t)dt * 16 * kBlockSize);
-        if (tail) {
-#pragma unroll
-          for (int e = 0; e < C::KPL; ++e)
-            if (vkey + e >= L) M::set(v, e, 0.0f);
-        }
-        acc[dt] = M::run(v, p, acc[dt]);
-      }
-    }
-  }
-}
-
-// Merge the S chunk partials of (request r, kv head g) into the output row.
-template <typename T, int D>
-__device__ void combine_wave(const AttnArgs& a, int r, int g, long long qrow, int S) {
-  const int lane = threadIdx.x & 63;
-  const int G = a.group;
-  constexpr int PER = D / 64;  // output elements per lane
-  for (int col = 0; col < G; ++col) {
-    const size_t pbase = (((size_t)r * a.hkv + g) * a.s_max) * G + col;  // + s * G
-    float mstar = -INFINITY;
-    for (int s = 0; s < S; ++s) mstar = fmaxf(mstar, a.ws_ml[pbase + (size_t)s * G].x);
-    float o[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = 0.0f;
-    float wsum = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float2 ml = a.ws_ml[pbase + (size_t)s * G];
-      const float w = ml.y * fast_exp2(ml.x - mstar);
-      wsum += w;
-      const float* op = a.ws_o + (pbase + (size_t)s * G) * D + lane * PER;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) o[e] += w * op[e];
-    }
-    const float inv = 1.0f / wsum;
-    T* out = (T*)a.out + ((size_t)qrow * a.hq + g * G + col) * D + lane * PER;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) out[e] = (T)(o[e] * inv);
-  }
-}
-
-// One decode work item: request r, kv heads hg*4 .. hg*4+3 (one per wave),
-// key chunk s.  Uniform across the workgroup.
-template <typename T, int D>
-__device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long qrow,
-                            int* s_flag) {
-  using C = Cfg<T, D>;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  DecodeSmem<T, D>& sm = *reinterpret_cast<DecodeSmem<T, D>*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int row16 = lane & 15;
   const int grp = lane >> 4;
   const int g = hg * kWaves + wave;
   const bool active = g < a.hkv;
+  const int ga = active ? g : 0;  // a valid head for the loads of an idle wave
   const int G = a.group;
   const int L = seq_len_of(a, r);
   const int S = num_splits(L, C::KSTEP);
@@ -350,43 +335,225 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   const int chunk = split_len(L, C::KSTEP);
   const int k0 = s * chunk;
   const int k1 = min(L, k0 + chunk);
+
+  Op qop[C::NC];
+  const bool qvalid = row16 < G;
+  load_query<T, D>(a, qrow, ga * G + (qvalid ? row16 : 0), a.q_pos[qrow], qvalid, grp, qop);
+
+  const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
+  const int32_t* kp = a.k_pos + a.cu_k[r];
+  const T* kpool = (const T*)a.k_pool;
+  const T* vpool = (const T*)a.v_pool;
+  const int nb_max = a.num_blocks - 1;
+  const int pmax = a.max_pos - 1;
+  const size_t head_k = (size_t)ga * kBlockSize * D;
+  const size_t head_v = (size_t)ga * D * kBlockSize;
+  const size_t blk_stride = (size_t)a.hkv * kBlockSize * D;
+
+  // table staging: thread -> (key of the step, TPT consecutive pairs)
+  constexpr int TPT = C::KSTEP * (D / 2) / kThreads;
+  constexpr int TPK = (D / 2) / TPT;
+  typedef Run<float, TPT> RF;
+  const int skey = tid / TPK;
+  const int spart = (tid % TPK) * TPT;
+  typename RF::V rc, rs;
+  auto stage_load = [&](int kb) {
+    const int kc = min(kb + skey, L - 1);
+    const size_t row = (size_t)clampi(kp[kc], 0, pmax) * (D / 2) + spart;
+    rc = RF::load(a.cos_tab + row);
+    rs = RF::load(a.sin_tab + row);
+  };
+  auto stage_store = [&](int buf) {
+    RF::store(&sm.cs[buf][skey][spart], rc);
+    RF::store(&sm.sn[buf][skey][spart], rs);
+  };
+
+  auto load_k = [&](const KAddr<C::NT>& ka, Op (&dst)[C::NT][C::NC]) {
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+      const T* krow = kpool + ka.blk[t] * blk_stride + head_k + (size_t)ka.off[t] * D +
+                      grp * C::KPL;
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) dst[t][c] = M::load(krow + c * C::KCH);
+    }
+  };
+
+  // prologue: step k0's table rows (to LDS) and addresses
+  KAddr<C::NT> ka;
+  VAddr<C::NPV> va;
+  stage_load(k0);
+  k_addr<T, D>(bt, k0, L, row16, nb_max, ka);
+  v_addr<T, D>(bt, k0, L, grp, nb_max, va);
+  stage_store(0);
+  __syncthreads();
+
   f32x4 acc[C::ND];
-  float m_run = -INFINITY, l_run = 0.0f;
 #pragma unroll
   for (int dt = 0; dt < C::ND; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (active) decode_wave<T, D>(a, r, g, qrow, k0, k1, L, acc, m_run, l_run);
-  const float l_tot = col_sum(l_run);
-  if (S == 1) {
-    if (active && row16 < G) {
-      T* out = (T*)a.out + ((size_t)qrow * a.hq + g * G + row16) * D + grp * 4;
-      const float inv = 1.0f / l_tot;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  // One step: keys kb .. kb+KSTEP-1, table rows in LDS buffer `buf`.  Every
+  // load of the step (K rows, V runs) and of the next step (table rows,
+  // addresses) is issued before the math.  TAIL: the step reaches past the
+  // chunk's last key (mask those scores, zero those V slots).
+  auto step = [&](int kb, int buf, auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const bool more = kb + C::KSTEP < k1;
+    Op kop[C::NT][C::NC];
+    Op vop[C::NPV][C::ND];
+    load_k(ka, kop);
 #pragma unroll
-      for (int dt = 0; dt < C::ND; ++dt) store4<T>(out + dt * 16, acc[dt], inv);
+    for (int mi = 0; mi < C::NPV; ++mi) {
+      const int vkey = kb + grp * 4 * C::NT + mi * C::KPL;
+      const T* vrow = vpool + va.blk[mi] * blk_stride + head_v + (size_t)row16 * kBlockSize +
+                      (vkey & 15);
+#pragma unroll
+      for (int dt = 0; dt < C::ND; ++dt) vop[mi][dt] = M::load(vrow + (size_t)dt * 16 * kBlockSize);
     }
+    if (more) {
+      stage_load(kb + C::KSTEP);
+      k_addr<T, D>(bt, kb + C::KSTEP, L, row16, nb_max, ka);
+      v_addr<T, D>(bt, kb + C::KSTEP, L, grp, nb_max, va);
+    }
+
+    f32x4 sc[C::NT];
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+      const int krow = key_of<C::NT>(t, row16);
+      rotate_from_lds<T, D>(kop[t], &sm.cs[buf][krow][grp * C::KPL],
+                            &sm.sn[buf][krow][grp * C::KPL]);
+      sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) sc[t] = M::run(kop[t][c], qop[c], sc[t]);
+    }
+    // the other table buffer was last read before the previous barrier
+    if (more) stage_store(buf ^ 1);
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (TAIL) {
+          const int key = kb + key_of<C::NT>(t, grp * 4 + i);
+          sc[t][i] = key < k1 ? sc[t][i] * a.scale_log2 : -INFINITY;
+        } else {
+          sc[t][i] *= a.scale_log2;
+        }
+      }
+    softmax_step<C::NT, C::ND>(sc, acc, m_run, l_run);
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int mi = 0; mi < C::NPV; ++mi) {
+        const int vkey = kb + grp * 4 * C::NT + mi * C::KPL;
+#pragma unroll
+        for (int dt = 0; dt < C::ND; ++dt)
+#pragma unroll
+          for (int e = 0; e < C::KPL; ++e)
+            if (vkey + e >= L) M::set(vop[mi][dt], e, 0.0f);
+      }
+    }
+#pragma unroll
+    for (int mi = 0; mi < C::NPV; ++mi) {
+      const Op p = pack_probs<T, D>(sc, mi);
+#pragma unroll
+      for (int dt = 0; dt < C::ND; ++dt) acc[dt] = M::run(vop[mi][dt], p, acc[dt]);
+    }
+    __syncthreads();
+  };
+
+  using Full = std::false_type;
+  using Tail = std::true_type;
+  // LDS table buffers alternate 0/1; only a chunk's last step can be a tail
+  int buf = 0;
+  for (int kb = k0; kb < k1; kb += C::KSTEP) {
+    if (kb + C::KSTEP <= k1) step(kb, buf, Full{}); else step(kb, buf, Tail{});
+    buf ^= 1;
+  }
+
+  const float l_tot = col_sum(l_run);
+  if (!active || row16 >= G) return;
+  const float inv = 1.0f / l_tot;
+  if (S == 1) {
+    T* out = (T*)a.out + ((size_t)qrow * a.hq + g * G + row16) * D + grp * 4;
+#pragma unroll
+    for (int dt = 0; dt < C::ND; ++dt) store4<T>(out + dt * 16, acc[dt], inv);
     return;
   }
-  if (active && row16 < G) {
-    const size_t pidx = (((size_t)r * a.hkv + g) * a.s_max + s) * G + row16;
-    const float inv = 1.0f / l_tot;
-    float* op = a.ws_o + pidx * D + grp * 4;
+  const size_t pidx = (((size_t)r * a.hkv + g) * a.s_max + s) * G + row16;
+  float* po = a.ws_o + pidx * D + grp * 4;
 #pragma unroll
-    for (int dt = 0; dt < C::ND; ++dt) *reinterpret_cast<f32x4*>(op + dt * 16) = acc[dt] * inv;
-    if (grp == 0) a.ws_ml[pidx] = make_float2(m_run, l_tot);
+  for (int dt = 0; dt < C::ND; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = acc[dt] * inv;
+  if (grp == 0) a.ws_ml[pidx] = make_float2(m_run, l_tot);
+}
+
+// Merge the chunk partials of every multi-chunk q_len == 1 request:
+// o = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m).  One
+// workgroup per (request, kv head); threads take (column, 8 consecutive d)
+// pairs, and threads beyond those pairs take every SG-th chunk in parallel.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a) {
+  constexpr int EPT = 8;
+  __shared__ __attribute__((aligned(16))) float gm[kThreads * EPT];
+  __shared__ float2 gml[kThreads];
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x / a.hkv;
+  const int g = blockIdx.x % a.hkv;
+  if (a.cu_q && a.cu_q[r + 1] - a.cu_q[r] != 1) return;
+  const long long qrow = a.cu_q ? (long long)a.cu_q[r] : (long long)r;
+  const int L = seq_len_of(a, r);
+  const int S = num_splits(L, Cfg<T, D>::KSTEP);
+  if (L <= 0 || S <= 1) return;
+  const int G = a.group;
+  const int pairs = G * (D / EPT);
+  const int SG = max(1, kThreads / pairs);
+  const int sg = tid / pairs;
+  const int pc = tid % pairs;
+  const int col = pc / (D / EPT);
+  const int d0 = (pc % (D / EPT)) * EPT;
+  const size_t pbase = ((size_t)r * a.hkv + g) * a.s_max;
+  float pm = -INFINITY, pl = 0.0f;
+  float po[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) po[e] = 0.0f;
+  if (sg < SG) {
+#pragma unroll 4
+    for (int ss = sg; ss < S; ss += SG) {
+      const float2 ml = a.ws_ml[(pbase + ss) * G + col];
+      const float* src = a.ws_o + ((pbase + ss) * G + col) * D + d0;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+      const float mn = fmaxf(pm, ml.x);
+      const float a0 = fast_exp2(pm - mn), a1 = ml.y * fast_exp2(ml.x - mn);
+      pl = pl * a0 + a1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        po[e] = po[e] * a0 + a1 * x0[e];
+        po[e + 4] = po[e + 4] * a0 + a1 * x1[e];
+      }
+      pm = mn;
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) gm[tid * EPT + e] = po[e];
+    gml[tid] = make_float2(pm, pl);
   }
-  // Publish the partials, then count this chunk in.  The workgroup that
-  // brings the count to S merges all chunks and re-arms the counter.
-  __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = atomicAdd(&a.ws_cnt[r * a.nhg + hg], 1);
-    *s_flag = (old == S - 1);
+  if (tid >= pairs) return;
+  float mm = -INFINITY;
+  for (int j = 0; j < SG; ++j) mm = fmaxf(mm, gml[j * pairs + tid].x);
+  float ll = 0.0f, oo[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) oo[e] = 0.0f;
+  for (int j = 0; j < SG; ++j) {
+    const float2 ml = gml[j * pairs + tid];
+    if (ml.y == 0.0f) continue;  // a chunk group with no chunk
+    const float w = fast_exp2(ml.x - mm);
+    ll += w * ml.y;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) oo[e] += w * gm[(j * pairs + tid) * EPT + e];
   }
-  __syncthreads();
-  if (*s_flag) {
-    __threadfence();
-    if (active) combine_wave<T, D>(a, r, g, qrow, S);
-    if (threadIdx.x == 0) a.ws_cnt[r * a.nhg + hg] = 0;
-  }
+  const float inv = 1.0f / ll;
+  T* dst = (T*)a.out + ((size_t)qrow * a.hq + g * G + col) * D + d0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) dst[e] = (T)(oo[e] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -588,46 +755,51 @@ __device__ __forceinline__ long long xcd_position(long long l, long long n) {
 }
 
 // Decode-only launch: logical item = (chunk s, request r, head group hg),
-// chunk-major so all requests' chunk s (same key positions in a batch of
-// equal-shaped contexts) run on one XCD.
+// head group fastest, then request: the workgroups that read the same table
+// rows (the same key positions) run on one XCD and share its L2.
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
-  __shared__ int s_flag;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(DecodeSmem<T, D>)];
   const long long n = (long long)gridDim.x;
   const long long l = xcd_logical(blockIdx.x, n);
   const int hg = (int)(l % a.nhg);
   const long long rs = l / a.nhg;
   const int r = (int)(rs % a.num_reqs);
   const int s = (int)(rs / a.num_reqs);
-  decode_item<T, D>(a, r, hg, s, r, &s_flag);
+  decode_item<T, D>(a, r, hg, s, r, smem);
 }
+
+template <typename T, int D>
+struct MixedSmem {
+  static constexpr int BYTES = PrefillSmem<T, D>::BYTES > (int)sizeof(DecodeSmem<T, D>)
+                                   ? PrefillSmem<T, D>::BYTES
+                                   : (int)sizeof(DecodeSmem<T, D>);
+};
 
 // Mixed launch over the planner's work list.
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads, 2) mixed_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[PrefillSmem<T, D>::BYTES];
-  __shared__ int s_flag;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[MixedSmem<T, D>::BYTES];
   if ((int)blockIdx.x >= *a.nitems) return;
   const int4 it = a.items[blockIdx.x];
   if (it.x == kItemPrefill) {
     prefill_tile<T, D>(a, it.y, it.z, it.w, smem);
   } else {
-    decode_item<T, D>(a, it.y, it.z, it.w, (long long)a.cu_q[it.y], &s_flag);
+    decode_item<T, D>(a, it.y, it.z, it.w, (long long)a.cu_q[it.y], smem);
   }
 }
 
 // Planner: one workgroup of 1024 threads turns (cu_seqlens_q, seq_lens) into
 // the work list.  Prefill tiles first (per request and kv head, last tile
 // first: the later query rows see more keys), then the chunks of q_len == 1
-// requests; each item is written at its XCD dispatch position.  Also zeroes
-// the split-combine counters of the decode requests.
+// requests (per chunk, the kv-head groups); each item is written at its XCD
+// dispatch position.
 __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ cu_q,
                                                     const int32_t* __restrict__ seq_lens,
                                                     int num_reqs, int hkv, int group, int nhg,
                                                     int kstep, int len_cap, long long max_items,
                                                     int4* __restrict__ items,
-                                                    int* __restrict__ count,
-                                                    int* __restrict__ counters) {
+                                                    int* __restrict__ count) {
   __shared__ long long s_a[1024];
   __shared__ long long s_b[1024];
   __shared__ long long s_tot[2];
@@ -702,7 +874,6 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
           const long long l = off_dc + (long long)s * nhg + hg;
           items[xcd_position(l, total)] = make_int4(kItemDecode, r, hg, s);
         }
-      for (int hg = 0; hg < nhg; ++hg) counters[r * nhg + hg] = 0;
     }
     __syncthreads();
     if (tid == 1023) {
@@ -745,17 +916,24 @@ static AttnArgs make_args(const AttnHostArgs& h, const WorkspaceLayout& w) {
   unsigned char* ws = (unsigned char*)h.workspace;
   a.ws_ml = (float2*)(ws + w.ml_off);
   a.ws_o = (float*)(ws + w.o_off);
-  a.ws_cnt = (int*)(ws + w.counters_off);
   a.items = (const int4*)(ws + w.items_off);
   a.nitems = (const int*)(ws + w.count_off);
   return a;
 }
 
 template <typename T, int D>
+static void launch_combine(const AttnArgs& a, hipStream_t s) {
+  if (a.s_max > 1)
+    hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)(a.num_reqs * a.hkv)),
+                       dim3(kThreads), 0, s, a);
+}
+
+template <typename T, int D>
 static int launch_decode(const AttnArgs& a, hipStream_t s) {
   const long long n = (long long)a.num_reqs * a.s_max * a.nhg;
-  if (n > 0x7fffffffLL) return PIC_EUNSUPPORTED;
+  if (n > 0x7fffffffLL || (long long)a.num_reqs * a.hkv > 0x7fffffffLL) return PIC_EUNSUPPORTED;
   hipLaunchKernelGGL((decode_kernel<T, D>), dim3((unsigned)n), dim3(kThreads), 0, s, a);
+  launch_combine<T, D>(a, s);
   return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }
 
@@ -768,9 +946,9 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
                               (long long)h.block_table_stride * kBlockSize);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, h.cu_seqlens_q, h.seq_lens,
                      h.num_reqs, h.hkv, h.hq / h.hkv, w.nhg, Cfg<T, D>::KSTEP, len_cap,
-                     w.max_items, (int4*)(ws + w.items_off), (int*)(ws + w.count_off),
-                     (int*)(ws + w.counters_off));
+                     w.max_items, (int4*)(ws + w.items_off), (int*)(ws + w.count_off));
   hipLaunchKernelGGL((mixed_kernel<T, D>), dim3((unsigned)w.max_items), dim3(kThreads), 0, s, a);
+  launch_combine<T, D>(a, s);
   return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }
 

@@ -11,7 +11,7 @@
 // so tokens that share a block write neighbouring bytes of each d row.
 #include <hip/hip_runtime.h>
 
-#include "../../include/pic.h"
+#include "pic.h"
 #include "pic_common.hpp"
 
 namespace pic {

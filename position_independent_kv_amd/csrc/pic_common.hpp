@@ -13,7 +13,7 @@ constexpr int kBlockSize = 16;      // tokens per KV block
 constexpr int kWaves = 4;           // waves (of 64 lanes) per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPrefillRows = 128;   // query rows (tokens x group heads) per prefill tile
-constexpr int kSplitTarget = 512;   // target keys per decode chunk
+constexpr int kSplitTarget = 1024;  // target keys per decode chunk (one workgroup)
 constexpr int kMaxGroup = 16;       // q heads per kv head held in one MFMA column tile
 
 // Keys consumed per inner step: two 16-key MFMA tiles for bf16, one for fp32.
@@ -21,15 +21,19 @@ constexpr int kstep_for(int dtype) { return dtype == 1 ? 32 : 16; }
 
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Keys per decode chunk for a request with L keys: chunks of about
-// kSplitTarget keys, balanced, rounded up to whole inner steps.  A pure
-// function of L, so a request is split the same way in any batch.
+// Key chunks of a request with L keys: round(L / kSplitTarget) chunks (at
+// least one), of equal length rounded up to whole inner steps, so chunks stay
+// within [0.67, 1.5] x the target.  A pure function of L: a request is split
+// the same way in any batch, so its result does not depend on the batch.
+constexpr int num_chunks_target(int L) {
+  return L <= 0 ? 1 : ((L + kSplitTarget / 2) / kSplitTarget > 0 ? (L + kSplitTarget / 2) / kSplitTarget : 1);
+}
 constexpr int split_len(int L, int kstep) {
-  return L <= 0 ? kstep : cdiv(cdiv(L, cdiv(L, kSplitTarget)), kstep) * kstep;
+  return L <= 0 ? kstep : cdiv(cdiv(L, num_chunks_target(L)), kstep) * kstep;
 }
 constexpr int num_splits(int L, int kstep) { return L <= 0 ? 1 : cdiv(L, split_len(L, kstep)); }
 // Upper bound of num_splits over all L <= max_len.
-constexpr int max_splits(int max_len) { return max_len <= 0 ? 1 : cdiv(max_len, kSplitTarget); }
+constexpr int max_splits(int max_len) { return max_len <= 0 ? 1 : cdiv(max_len, kSplitTarget) + 1; }
 
 // Work-list item kinds (the mixed launch).
 constexpr int kItemPrefill = 0;
@@ -39,7 +43,6 @@ constexpr int kItemDecode = 1;
 struct WorkspaceLayout {
   size_t count_off;     // int: number of work items written by the planner
   size_t items_off;     // int4[max_items]: work list
-  size_t counters_off;  // int[num_reqs * nhg]: split-combine arrival counters
   size_t ml_off;        // float2[num_reqs * hkv * s_max * group]: (max, sum) per chunk
   size_t o_off;         // float[num_reqs * hkv * s_max * group * head_dim]: chunk outputs
   size_t total;
@@ -65,8 +68,6 @@ inline WorkspaceLayout workspace_layout(int num_reqs, int total_q, int max_seq_l
   off = align_up(off + 16, 256);
   w.items_off = off;
   off = align_up(off + (size_t)w.max_items * 16, 256);
-  w.counters_off = off;
-  off = align_up(off + (size_t)num_reqs * w.nhg * 4, 256);
   const size_t parts = (size_t)num_reqs * hkv * w.s_max * group;
   w.ml_off = off;
   off = align_up(off + parts * 8, 256);

@@ -47,6 +47,11 @@ struct Mma<bf16> {
     for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
     return z;
   }
+  // 8 floats -> 8 bf16 (round to nearest even), converted two at a time
+  static __device__ __forceinline__ Op pack(const float* f) {
+    const vec<float, 8> v = {f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]};
+    return __builtin_convertvector(v, Op);
+  }
 };
 
 template <>
@@ -61,6 +66,7 @@ struct Mma<float> {
   static __device__ __forceinline__ float get(const Op& v, int) { return v; }
   static __device__ __forceinline__ void set(Op& v, int, float x) { v = x; }
   static __device__ __forceinline__ Op zero() { return 0.0f; }
+  static __device__ __forceinline__ Op pack(const float* f) { return f[0]; }
 };
 
 template <typename T>

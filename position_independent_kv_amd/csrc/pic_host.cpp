@@ -5,7 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/pic.h"
+#include "pic.h"
 #include "pic_common.hpp"
 #include "pic_host.hpp"
 

@@ -8,7 +8,7 @@
 // the table is stored in float32.
 #include <hip/hip_runtime.h>
 
-#include "../../include/pic.h"
+#include "pic.h"
 #include "pic_common.hpp"
 
 namespace pic {

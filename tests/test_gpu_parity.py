@@ -11,8 +11,8 @@ import pytest
 
 import oracle
 import position_independent_kv_amd as pic
-from tests.gpu_harness import (DeviceWorkload, oracle_outputs, oracle_pools, run_workload,
-                               select_rows, to_f64)
+from tests.gpu_harness import DeviceWorkload, run_workload
+from tests.oracle_harness import oracle_outputs, oracle_pools, select_rows
 from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
