@@ -254,59 +254,34 @@ __device__ __forceinline__ void store4(T* p, f32x4 v, float scale) {
 // decode: one wave = (request r, kv head g, keys [k0, k1)), q row qrow
 // ---------------------------------------------------------------------------
 
-// Per-lane addresses of one decode step: the block and offset of the key row
-// each score tile's A operand needs, and the block of each PV run.
-template <int NT>
-struct KAddr {
-  int blk[NT];
-  int off[NT];
-};
-template <int NPV>
-struct VAddr {
-  int blk[NPV];
-};
+// Upper bound of split_len: a chunk never exceeds 1.5x the split target
+// (rounded up to whole steps).
+constexpr int kMaxChunk = kSplitTarget + kSplitTarget / 2 + 32;
 
-template <typename T, int D>
-__device__ __forceinline__ void k_addr(const int32_t* bt, int kb, int L, int row16, int nb_max,
-                                       KAddr<Cfg<T, D>::NT>& A) {
-  using C = Cfg<T, D>;
-#pragma unroll
-  for (int t = 0; t < C::NT; ++t) {
-    const int kc = min(kb + key_of<C::NT>(t, row16), L - 1);
-    A.blk[t] = clampi(bt[kc >> 4], 0, nb_max);
-    A.off[t] = kc & 15;
-  }
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void v_addr(const int32_t* bt, int kb, int L, int grp, int nb_max,
-                                       VAddr<Cfg<T, D>::NPV>& A) {
-  using C = Cfg<T, D>;
-#pragma unroll
-  for (int mi = 0; mi < C::NPV; ++mi) {
-    const int vkc = min(kb + grp * 4 * C::NT + mi * C::KPL, L - 1);
-    A.blk[mi] = clampi(bt[vkc >> 4], 0, nb_max);
-  }
-}
-
-// LDS of a decode workgroup: the cos/sin rows of the current and the next
-// step (one row per key of the step), shared by the workgroup's kv heads.
+// LDS of a decode workgroup: the chunk's key positions and block ids, and
+// the cos/sin rows of two steps (one row per key of the step, padded so the
+// 16 rows one read instruction touches fall in different banks).
 template <typename T, int D>
 struct DecodeSmem {
   static constexpr int KSTEP = Cfg<T, D>::KSTEP;
-  static constexpr int TLD = D / 2 + 4;  // padded row: spreads the 16 rows a load reads over banks
+  static constexpr int TLD = D / 2 + 4;
   float cs[2][KSTEP][TLD];
   float sn[2][KSTEP][TLD];
+  int pos[kMaxChunk];
+  int blk[kMaxChunk / kBlockSize + 2];
 };
 
 // One decode work item: request r, key chunk s, kv heads hg*4 .. hg*4+3 (one
-// per wave).  All four waves walk the same keys, so each step's table rows
-// are fetched once per workgroup (one step ahead, double-buffered in LDS) and
-// every wave reads its own K and V rows straight from the pools.  With one
-// chunk the wave writes the output row; otherwise it writes a normalised
-// partial and (max, sum) that combine_kernel merges.  Uniform across the
-// workgroup.
-template <typename T, int D>
+// per wave).  All four waves walk the same keys: each step's cos/sin rows are
+// fetched once per workgroup and shared through LDS, while every wave reads
+// its own head's K rows and V runs from the pools into registers.  NB steps
+// of loads are kept in flight (a ring of NB register buffers): the loads of
+// step j+NB are issued as soon as step j has consumed its buffer.  The
+// chunk's block ids and key positions are staged in LDS first, so no
+// address lookup ever waits behind the data loads.  With one chunk the wave
+// writes the output row; otherwise it writes a normalised partial and
+// (max, sum) that combine_kernel merges.  Uniform across the workgroup.
+template <typename T, int D, int NB>
 __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long qrow,
                             unsigned char* smem_raw) {
   using C = Cfg<T, D>;
@@ -335,20 +310,35 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   const int chunk = split_len(L, C::KSTEP);
   const int k0 = s * chunk;
   const int k1 = min(L, k0 + chunk);
+  const int nsteps = cdiv(k1 - k0, C::KSTEP);
+
+  // chunk metadata -> LDS: positions of keys k0.., block ids of blocks k0/16..
+  {
+    const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
+    const int32_t* kp = a.k_pos + a.cu_k[r];
+    const int nk = nsteps * C::KSTEP;
+    for (int j = tid; j < nk; j += kThreads)
+      sm.pos[j] = clampi(kp[min(k0 + j, L - 1)], 0, a.max_pos - 1);
+    const int nbk = nk / kBlockSize;
+    for (int j = tid; j < nbk; j += kThreads)
+      sm.blk[j] = clampi(bt[min((k0 >> 4) + j, (L - 1) >> 4)], 0, a.num_blocks - 1);
+  }
 
   Op qop[C::NC];
   const bool qvalid = row16 < G;
   load_query<T, D>(a, qrow, ga * G + (qvalid ? row16 : 0), a.q_pos[qrow], qvalid, grp, qop);
+  __syncthreads();
 
-  const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
-  const int32_t* kp = a.k_pos + a.cu_k[r];
   const T* kpool = (const T*)a.k_pool;
   const T* vpool = (const T*)a.v_pool;
-  const int nb_max = a.num_blocks - 1;
-  const int pmax = a.max_pos - 1;
   const size_t head_k = (size_t)ga * kBlockSize * D;
   const size_t head_v = (size_t)ga * D * kBlockSize;
   const size_t blk_stride = (size_t)a.hkv * kBlockSize * D;
+  // this lane's key block inside a step (the K row of its A-operand row, the
+  // V run of its lane group) for steps that span two blocks (bf16)
+  const int kblk_sel = (key_of<C::NT>(0, row16) >= kBlockSize) ? 1 : 0;
+  const int vblk_sel = (grp * 4 * C::NT >= kBlockSize) ? 1 : 0;
+  const int vkey_off = (grp * 4 * C::NT) & 15;
 
   // table staging: thread -> (key of the step, TPT consecutive pairs)
   constexpr int TPT = C::KSTEP * (D / 2) / kThreads;
@@ -356,117 +346,102 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   typedef Run<float, TPT> RF;
   const int skey = tid / TPK;
   const int spart = (tid % TPK) * TPT;
-  typename RF::V rc, rs;
-  auto stage_load = [&](int kb) {
-    const int kc = min(kb + skey, L - 1);
-    const size_t row = (size_t)clampi(kp[kc], 0, pmax) * (D / 2) + spart;
-    rc = RF::load(a.cos_tab + row);
-    rs = RF::load(a.sin_tab + row);
-  };
-  auto stage_store = [&](int buf) {
-    RF::store(&sm.cs[buf][skey][spart], rc);
-    RF::store(&sm.sn[buf][skey][spart], rs);
-  };
 
-  auto load_k = [&](const KAddr<C::NT>& ka, Op (&dst)[C::NT][C::NC]) {
+  struct Group {
+    Op k[C::NT][C::NC];
+    Op v[C::NPV][C::ND];
+    typename RF::V c, sn;
+  };
+  Group grpbuf[NB];
+
+  // issue every load of step j (relative to k0) into a register group
+  auto issue = [&](int j, Group& gb) {
+    const int kb = j * C::KSTEP;  // offset in the chunk
+    const int b0 = sm.blk[kb >> 4];
+    const int b1 = sm.blk[min((kb >> 4) + 1, nsteps * C::KSTEP / kBlockSize - 1)];
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
-      const T* krow = kpool + ka.blk[t] * blk_stride + head_k + (size_t)ka.off[t] * D +
-                      grp * C::KPL;
+      const int kk = key_of<C::NT>(t, row16);
+      const int blk = (kblk_sel ? b1 : b0);
+      const T* krow = kpool + (size_t)blk * blk_stride + head_k +
+                      (size_t)((kb + kk) & 15) * D + grp * C::KPL;
 #pragma unroll
-      for (int c = 0; c < C::NC; ++c) dst[t][c] = M::load(krow + c * C::KCH);
+      for (int c = 0; c < C::NC; ++c) gb.k[t][c] = M::load(krow + c * C::KCH);
     }
+#pragma unroll
+    for (int mi = 0; mi < C::NPV; ++mi) {
+      const int blk = (vblk_sel ? b1 : b0);
+      const T* vrow = vpool + (size_t)blk * blk_stride + head_v + (size_t)row16 * kBlockSize +
+                      ((vkey_off + mi * C::KPL) & 15);
+#pragma unroll
+      for (int dt = 0; dt < C::ND; ++dt) gb.v[mi][dt] = M::load(vrow + (size_t)dt * 16 * kBlockSize);
+    }
+    const size_t row = (size_t)sm.pos[kb + skey] * (D / 2) + spart;
+    gb.c = RF::load(a.cos_tab + row);
+    gb.sn = RF::load(a.sin_tab + row);
   };
-
-  // prologue: step k0's table rows (to LDS) and addresses
-  KAddr<C::NT> ka;
-  VAddr<C::NPV> va;
-  stage_load(k0);
-  k_addr<T, D>(bt, k0, L, row16, nb_max, ka);
-  v_addr<T, D>(bt, k0, L, grp, nb_max, va);
-  stage_store(0);
-  __syncthreads();
 
   f32x4 acc[C::ND];
 #pragma unroll
   for (int dt = 0; dt < C::ND; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // One step: keys kb .. kb+KSTEP-1, table rows in LDS buffer `buf`.  Every
-  // load of the step (K rows, V runs) and of the next step (table rows,
-  // addresses) is issued before the math.  TAIL: the step reaches past the
-  // chunk's last key (mask those scores, zero those V slots).
-  auto step = [&](int kb, int buf, auto tail_tag) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
-    const bool more = kb + C::KSTEP < k1;
-    Op kop[C::NT][C::NC];
-    Op vop[C::NPV][C::ND];
-    load_k(ka, kop);
 #pragma unroll
-    for (int mi = 0; mi < C::NPV; ++mi) {
-      const int vkey = kb + grp * 4 * C::NT + mi * C::KPL;
-      const T* vrow = vpool + va.blk[mi] * blk_stride + head_v + (size_t)row16 * kBlockSize +
-                      (vkey & 15);
-#pragma unroll
-      for (int dt = 0; dt < C::ND; ++dt) vop[mi][dt] = M::load(vrow + (size_t)dt * 16 * kBlockSize);
-    }
-    if (more) {
-      stage_load(kb + C::KSTEP);
-      k_addr<T, D>(bt, kb + C::KSTEP, L, row16, nb_max, ka);
-      v_addr<T, D>(bt, kb + C::KSTEP, L, grp, nb_max, va);
-    }
+  for (int b = 0; b < NB; ++b)
+    if (b < nsteps) issue(b, grpbuf[b]);
 
+  // step j with its loads in group gb; buf: LDS table slot
+  auto step = [&](int j, Group& gb) {
+    const int buf = j & 1;
+    const int kb = k0 + j * C::KSTEP;  // absolute key index
+    RF::store(&sm.cs[buf][skey][spart], gb.c);
+    RF::store(&sm.sn[buf][skey][spart], gb.sn);
+    __syncthreads();
     f32x4 sc[C::NT];
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
       const int krow = key_of<C::NT>(t, row16);
-      rotate_from_lds<T, D>(kop[t], &sm.cs[buf][krow][grp * C::KPL],
+      rotate_from_lds<T, D>(gb.k[t], &sm.cs[buf][krow][grp * C::KPL],
                             &sm.sn[buf][krow][grp * C::KPL]);
       sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < C::NC; ++c) sc[t] = M::run(kop[t][c], qop[c], sc[t]);
+      for (int c = 0; c < C::NC; ++c) sc[t] = M::run(gb.k[t][c], qop[c], sc[t]);
     }
-    // the other table buffer was last read before the previous barrier
-    if (more) stage_store(buf ^ 1);
 #pragma unroll
     for (int t = 0; t < C::NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (TAIL) {
-          const int key = kb + key_of<C::NT>(t, grp * 4 + i);
-          sc[t][i] = key < k1 ? sc[t][i] * a.scale_log2 : -INFINITY;
-        } else {
-          sc[t][i] *= a.scale_log2;
-        }
+        const int key = kb + key_of<C::NT>(t, grp * 4 + i);
+        sc[t][i] = key < k1 ? sc[t][i] * a.scale_log2 : -INFINITY;
       }
     softmax_step<C::NT, C::ND>(sc, acc, m_run, l_run);
-    if constexpr (TAIL) {
+    // slots at or beyond L hold no data: clear those V elements (bit mask,
+    // all ones except in a request's last step)
 #pragma unroll
-      for (int mi = 0; mi < C::NPV; ++mi) {
-        const int vkey = kb + grp * 4 * C::NT + mi * C::KPL;
+    for (int mi = 0; mi < C::NPV; ++mi) {
+      const int vkey = kb + grp * 4 * C::NT + mi * C::KPL;
+      const int nvalid = L - vkey;
+      if (nvalid < C::KPL) {
 #pragma unroll
         for (int dt = 0; dt < C::ND; ++dt)
 #pragma unroll
           for (int e = 0; e < C::KPL; ++e)
-            if (vkey + e >= L) M::set(vop[mi][dt], e, 0.0f);
+            if (e >= nvalid) M::set(gb.v[mi][dt], e, 0.0f);
       }
     }
 #pragma unroll
     for (int mi = 0; mi < C::NPV; ++mi) {
       const Op p = pack_probs<T, D>(sc, mi);
 #pragma unroll
-      for (int dt = 0; dt < C::ND; ++dt) acc[dt] = M::run(vop[mi][dt], p, acc[dt]);
+      for (int dt = 0; dt < C::ND; ++dt) acc[dt] = M::run(gb.v[mi][dt], p, acc[dt]);
     }
-    __syncthreads();
+    if (j + NB < nsteps) issue(j + NB, gb);
   };
 
-  using Full = std::false_type;
-  using Tail = std::true_type;
-  // LDS table buffers alternate 0/1; only a chunk's last step can be a tail
-  int buf = 0;
-  for (int kb = k0; kb < k1; kb += C::KSTEP) {
-    if (kb + C::KSTEP <= k1) step(kb, buf, Full{}); else step(kb, buf, Tail{});
-    buf ^= 1;
+  for (int j0 = 0; j0 < nsteps; j0 += NB) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (j0 + b < nsteps) step(j0 + b, grpbuf[b]);
   }
 
   const float l_tot = col_sum(l_run);
@@ -754,6 +729,10 @@ __device__ __forceinline__ long long xcd_position(long long l, long long n) {
   return k * 8 + x;
 }
 
+// Steps of K/V loads each decode wave keeps in flight.  Measured on MI355X:
+// one step at two waves per SIMD beats deeper rings at one wave per SIMD.
+constexpr int kDecodeDepth = 1;
+
 // Decode-only launch: logical item = (chunk s, request r, head group hg),
 // head group fastest, then request: the workgroups that read the same table
 // rows (the same key positions) run on one XCD and share its L2.
@@ -766,7 +745,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
   const long long rs = l / a.nhg;
   const int r = (int)(rs % a.num_reqs);
   const int s = (int)(rs / a.num_reqs);
-  decode_item<T, D>(a, r, hg, s, r, smem);
+  decode_item<T, D, kDecodeDepth>(a, r, hg, s, r, smem);
 }
 
 template <typename T, int D>
@@ -785,7 +764,7 @@ __global__ void __launch_bounds__(kThreads, 2) mixed_kernel(AttnArgs a) {
   if (it.x == kItemPrefill) {
     prefill_tile<T, D>(a, it.y, it.z, it.w, smem);
   } else {
-    decode_item<T, D>(a, it.y, it.z, it.w, (long long)a.cu_q[it.y], smem);
+    decode_item<T, D, 1>(a, it.y, it.z, it.w, (long long)a.cu_q[it.y], smem);
   }
 }
 

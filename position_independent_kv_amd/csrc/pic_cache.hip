@@ -5,10 +5,9 @@
 // rewritten.  This is a pure scatter: the stored bytes are the input bytes.
 //
 // K goes to k_pool[block][h][offset][d] (one contiguous row per token and
-// head): a flat, coalesced 16-byte copy.  V goes to v_pool[block][h][d][offset]
-// (transposed inside the block so that the attention kernels read runs of
-// consecutive keys as matrix-core operands): lanes take consecutive tokens,
-// so tokens that share a block write neighbouring bytes of each d row.
+// head); V goes to v_pool[block][h][d][offset] (transposed inside the block so
+// that the attention kernels read runs of consecutive keys as matrix-core
+// operands).  One launch writes both.
 #include <hip/hip_runtime.h>
 
 #include "pic.h"
@@ -16,14 +15,20 @@
 
 namespace pic {
 
-// One thread per (token, head, 16-byte chunk of the row).
+// One thread per (token, head, 16-byte chunk of the row): the K chunk is one
+// 16-byte store into the token's row; the V chunk's elements go to
+// consecutive d rows of the block, each at the token's offset.  Consecutive
+// threads take consecutive chunks, so a K row is written by neighbouring
+// lanes, and tokens that fill one block write neighbouring bytes of each V
+// row.
 template <typename T>
-__global__ void __launch_bounds__(256) cache_write_k_kernel(const T* __restrict__ k,
-                                                            const int32_t* __restrict__ slots,
-                                                            long long num_tokens, int hkv,
-                                                            int head_dim,
-                                                            T* __restrict__ k_pool,
-                                                            long long num_slots) {
+__global__ void __launch_bounds__(256) cache_write_kernel(const T* __restrict__ k,
+                                                          const T* __restrict__ v,
+                                                          const int32_t* __restrict__ slots,
+                                                          long long num_tokens, int hkv,
+                                                          int head_dim, T* __restrict__ k_pool,
+                                                          T* __restrict__ v_pool,
+                                                          long long num_slots) {
   constexpr int VEC = 16 / sizeof(T);
   const int chunks = head_dim / VEC;
   const long long n = num_tokens * hkv * chunks;
@@ -37,41 +42,14 @@ __global__ void __launch_bounds__(256) cache_write_k_kernel(const T* __restrict_
     if (slot < 0 || slot >= num_slots) continue;
     const long long blk = slot / kBlockSize;
     const int off = (int)(slot % kBlockSize);
-    const uint4 x = *reinterpret_cast<const uint4*>(k + th * head_dim + c * VEC);
+    const uint4 xk = *reinterpret_cast<const uint4*>(k + th * head_dim + c * VEC);
+    const uint4 xv = *reinterpret_cast<const uint4*>(v + th * head_dim + c * VEC);
     *reinterpret_cast<uint4*>(k_pool + ((blk * hkv + h) * kBlockSize + off) * head_dim +
-                              c * VEC) = x;
-  }
-}
-
-// One wave per (64 consecutive tokens, head); lane = token.
-template <typename T>
-__global__ void __launch_bounds__(256) cache_write_v_kernel(const T* __restrict__ v,
-                                                            const int32_t* __restrict__ slots,
-                                                            long long num_tokens, int hkv,
-                                                            int head_dim,
-                                                            T* __restrict__ v_pool,
-                                                            long long num_slots) {
-  constexpr int VEC = 16 / sizeof(T);
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const long long waves_total = (long long)gridDim.x * 4;
-  const long long tiles = ((num_tokens + 63) / 64) * hkv;
-  for (long long w = (long long)blockIdx.x * 4 + wave; w < tiles; w += waves_total) {
-    const int h = (int)(w % hkv);
-    const long long t = (w / hkv) * 64 + lane;
-    if (t >= num_tokens) continue;
-    const long long slot = slots[t];
-    if (slot < 0 || slot >= num_slots) continue;
-    const long long blk = slot / kBlockSize;
-    const int off = (int)(slot % kBlockSize);
-    const T* src = v + (t * hkv + h) * head_dim;
-    T* dst = v_pool + (blk * hkv + h) * (long long)head_dim * kBlockSize + off;
-    for (int e = 0; e < head_dim; e += VEC) {
-      const uint4 x = *reinterpret_cast<const uint4*>(src + e);
-      const T* xs = reinterpret_cast<const T*>(&x);
+                              c * VEC) = xk;
+    T* dst = v_pool + ((blk * hkv + h) * head_dim + c * VEC) * kBlockSize + off;
+    const T* xs = reinterpret_cast<const T*>(&xv);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) dst[(long long)(e + j) * kBlockSize] = xs[j];
-    }
+    for (int j = 0; j < VEC; ++j) dst[j * kBlockSize] = xs[j];
   }
 }
 
@@ -79,16 +57,11 @@ template <typename T>
 static int launch_cache_write(const void* k, const void* v, const int32_t* slots, int n, int hkv,
                               int d, void* kp, void* vp, long long num_slots, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
-  const long long nk = (long long)n * hkv * (d / VEC);
-  long long bk = (nk + 255) / 256;
-  if (bk > 65536) bk = 65536;
-  hipLaunchKernelGGL(cache_write_k_kernel<T>, dim3((unsigned)bk), dim3(256), 0, s,
-                     (const T*)k, slots, (long long)n, hkv, d, (T*)kp, num_slots);
-  const long long tiles = ((long long)(n + 63) / 64) * hkv;
-  long long bv = (tiles + 3) / 4;
-  if (bv > 65536) bv = 65536;
-  hipLaunchKernelGGL(cache_write_v_kernel<T>, dim3((unsigned)bv), dim3(256), 0, s,
-                     (const T*)v, slots, (long long)n, hkv, d, (T*)vp, num_slots);
+  const long long nt = (long long)n * hkv * (d / VEC);
+  long long blocks = (nt + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(cache_write_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, s, (const T*)k,
+                     (const T*)v, slots, (long long)n, hkv, d, (T*)kp, (T*)vp, num_slots);
   return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }
 

@@ -13,7 +13,7 @@ constexpr int kBlockSize = 16;      // tokens per KV block
 constexpr int kWaves = 4;           // waves (of 64 lanes) per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPrefillRows = 128;   // query rows (tokens x group heads) per prefill tile
-constexpr int kSplitTarget = 1024;  // target keys per decode chunk (one workgroup)
+constexpr int kSplitTarget = 384;   // target keys per decode chunk (one workgroup)
 constexpr int kMaxGroup = 16;       // q heads per kv head held in one MFMA column tile
 
 // Keys consumed per inner step: two 16-key MFMA tiles for bf16, one for fp32.

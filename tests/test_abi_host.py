@@ -62,9 +62,9 @@ def test_split_policy(dtype, kstep):
         c = pic.pic_decode_split_len(L, dtype)
         assert c % kstep == 0
         assert (S - 1) * c < L <= S * c          # every chunk non-empty, all keys covered
-        assert S <= -(-L // 1024) + 1            # within the workspace bound
-        assert S <= max(1, (L + 512) // 1024)    # at most round(L / 1024) chunks
-        assert c <= 1536 + kstep                 # chunks stay near the 1024-key target
+        assert S <= -(-L // 384) + 1             # within the workspace bound
+        assert S <= max(1, (L + 192) // 384)     # at most round(L / 384) chunks
+        assert c <= 576 + kstep                  # chunks stay near the 384-key target
 
 
 def _c_args(n):

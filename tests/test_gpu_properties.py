@@ -1,0 +1,317 @@
+"""GPU properties that must hold bit for bit (indexing, sharing, batching).
+
+Each check compares two runs of the HIP library (through the C ABI) whose
+results must be identical bytes, or compares against stored values chosen so
+the floating-point result is exact (the needle).  The sharing checks follow
+MiniPIC §2.1: one physical block serves several requests at different
+offsets, never mutated by attention.
+"""
+
+import numpy as np
+import pytest
+
+import position_independent_kv_amd as pic
+from tests.gpu_harness import DeviceWorkload, i32, to_torch
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _bits(t):
+    torch = _torch()
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _same_bits(a, b):
+    torch = _torch()
+    return torch.equal(_bits(a), _bits(b))
+
+
+SMALL_DEC = dict(builder="decode", seed=51, R=10, seg_len=400, n_seg=3, n_shared=1, n_spans=5)
+SMALL_PRE = dict(builder="prefill", seed=52, R=3, n_spans=4, span_len=160, per_req=2, q_len=90)
+SMALL_MIX = dict(builder="mixed", seed=53, n_chunks=3, chunk=128, n_dec=9, per_dec=2)
+
+
+def _fresh(kw, name="x"):
+    w = make_workload(name, **dict(kw))
+    dw = DeviceWorkload(w)
+    dw.write_new_tokens()
+    return w, dw
+
+
+# ---------------------------------------------------------------------------
+# needle: a single huge score makes the output exactly that slot's V row
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d,G", [("bf16", 128, 4), ("f32", 64, 1), ("bf16", 64, 8)])
+def test_needle_every_slot_decode(dtype, d, G):
+    """Request r puts one non-zero key at slot j_r; all other keys are zero.
+    Query and needle key share one logical position, so the rotation cancels
+    in the score (rotations preserve dot products) and the score is
+    |q|^2 * c / sqrt(d) ~ 200: every other weight underflows to 0 and the
+    output must equal V[j_r] bit for bit.  j_r sweeps every offset inside a
+    block, block boundaries, chunk boundaries and the last slot."""
+    torch = _torch()
+    rng = np.random.default_rng(7)
+    hkv = 2
+    hq = hkv * G
+    B = 16
+    L = 1500                                     # several decode chunks
+    slots = sorted(set(list(range(0, 48)) + [383, 384, 385, 575, 576, 767, 768, 1023, 1024,
+                                            1100, 1311, 1312, 1498, 1499]))
+    R = len(slots)
+    nb_req = -(-L // B)
+    nblocks = R * nb_req + 3
+    perm = rng.permutation(nblocks)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k_pool = torch.zeros((nblocks, hkv, B, d), dtype=tdt, device="cuda")
+    v_pool = torch.randn((nblocks, hkv, d, B), dtype=torch.float32, device="cuda").to(tdt)
+    block_table = np.zeros((R, nb_req), np.int32)
+    for r in range(R):
+        block_table[r] = perm[r * nb_req:(r + 1) * nb_req]
+    t_pos = 5000
+    k_pos = rng.integers(0, 9000, size=(R, L)).astype(np.int32)
+    qv = torch.randn((R, hkv, d), dtype=torch.float32)
+    q = qv[:, :, None, :].expand(R, hkv, G, d).reshape(R, hq, d).contiguous()
+    q = q.to(tdt)
+    qf = q.float().view(R, hkv, G, d)[:, :, 0, :]
+    for r, j in enumerate(slots):
+        k_pos[r, j] = t_pos
+        c = 200.0 * np.sqrt(d) / float((qf[r] * qf[r]).sum(-1).min())
+        blk, off = int(block_table[r, j // B]), j % B
+        k_pool[blk, :, off, :] = (qf[r] * c).to(tdt).cuda()
+    cos = torch.empty((9001, d // 2), dtype=torch.float32, device="cuda")
+    sin = torch.empty_like(cos)
+    pic.pic_rope_table(cos, sin, 500000.0)
+    seq = np.full(R, L, np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(seq)]).astype(np.int32)
+    out = torch.empty((R, hq, d), dtype=tdt, device="cuda")
+    ws = torch.zeros(pic.pic_attn_workspace_size(R, R, L, hq, hkv, d, tdt), dtype=torch.uint8,
+                     device="cuda")
+    pic.pic_attn_decode(q.cuda(), i32(np.full(R, t_pos)), k_pool, v_pool, i32(block_table),
+                        i32(seq), i32(cu_k), i32(k_pos.reshape(-1)), cos, sin, L, out, ws)
+    torch.cuda.synchronize()
+    for r, j in enumerate(slots):
+        blk, off = int(block_table[r, j // B]), j % B
+        for h in range(hq):
+            want = v_pool[blk, h // G, :, off]
+            assert _same_bits(out[r, h], want), (r, j, h)
+
+
+def test_needle_prefill_rows():
+    """Prefill: rows that can see the needle slot return V[j] exactly."""
+    torch = _torch()
+    rng = np.random.default_rng(8)
+    hkv, G, d, B = 2, 4, 128, 16
+    hq = hkv * G
+    L, ql = 200, 70
+    needles = [0, 17, 130, 131, 150, 199]
+    R = len(needles)
+    nb_req = -(-L // B)
+    nblocks = R * nb_req
+    perm = rng.permutation(nblocks)
+    k_pool = torch.zeros((nblocks, hkv, B, d), dtype=torch.bfloat16, device="cuda")
+    v_pool = torch.randn((nblocks, hkv, d, B), device="cuda").to(torch.bfloat16)
+    block_table = perm.reshape(R, nb_req).astype(np.int32)
+    t_pos = 777
+    k_pos = rng.integers(0, 1000, size=(R, L)).astype(np.int32)
+    qv = torch.randn((hkv, d))
+    q1 = qv[:, None, :].expand(hkv, G, d).reshape(hq, d)
+    q = q1[None].expand(R * ql, hq, d).contiguous().to(torch.bfloat16)
+    qf = q[0].float().view(hkv, G, d)[:, 0, :]
+    c = 200.0 * np.sqrt(d) / float((qf * qf).sum(-1).min())
+    for r, j in enumerate(needles):
+        k_pos[r, j] = t_pos
+        k_pool[int(block_table[r, j // B]), :, j % B, :] = (qf * c).to(torch.bfloat16).cuda()
+    q_pos = np.full(R * ql, t_pos, np.int32)
+    cos = torch.empty((1001, d // 2), dtype=torch.float32, device="cuda")
+    sin = torch.empty_like(cos)
+    pic.pic_rope_table(cos, sin, 500000.0)
+    seq = np.full(R, L, np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(seq)]).astype(np.int32)
+    cu_q = (np.arange(R + 1) * ql).astype(np.int32)
+    out = torch.empty_like(q.cuda())
+    ws = torch.zeros(pic.pic_attn_workspace_size(R, R * ql, L, hq, hkv, d, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    pic.pic_attn_prefill(q.cuda(), i32(cu_q), i32(q_pos), k_pool, v_pool, i32(block_table),
+                         i32(seq), i32(cu_k), i32(k_pos.reshape(-1)), cos, sin, ql, L, out, ws)
+    torch.cuda.synchronize()
+    checked = 0
+    for r, j in enumerate(needles):
+        blk, off = int(block_table[r, j // B]), j % B
+        for i in range(ql):
+            if j <= L - ql + i:     # the row sees the needle
+                for h in range(hq):
+                    assert _same_bits(out[r * ql + i, h], v_pool[blk, h // G, :, off]), (r, j, i, h)
+                checked += 1
+    assert checked > 0
+
+
+# ---------------------------------------------------------------------------
+# sharing and layout invariance (bit-exact)
+# ---------------------------------------------------------------------------
+
+def _rerun(dw, decode=None):
+    torch = _torch()
+    out = torch.empty_like(dw.out)
+    dw.attention(decode=decode, out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("kw", [SMALL_DEC, SMALL_PRE, SMALL_MIX], ids=["decode", "prefill", "mixed"])
+def test_shared_blocks_equal_private_copies(kw):
+    """Giving every request private copies of the blocks it references (no
+    sharing at all) changes no output bit."""
+    torch = _torch()
+    w, dw = _fresh(kw)
+    base = _rerun(dw)
+    nb = -(-w.seq_lens.astype(np.int64) // w.block_size)
+    stride = int(nb.max())
+    new_bt = np.zeros((w.num_reqs, stride), np.int32)
+    src = []
+    for r in range(w.num_reqs):
+        for i in range(int(nb[r])):
+            new_bt[r, i] = len(src)
+            src.append(int(w.block_table[r, i]))
+    idx = torch.tensor(src, dtype=torch.long, device="cuda")
+    dw.k_pool = dw.k_pool.index_select(0, idx).contiguous()
+    dw.v_pool = dw.v_pool.index_select(0, idx).contiguous()
+    dw.block_table = i32(new_bt)
+    got = _rerun(dw)
+    assert _same_bits(got, base)
+
+
+@pytest.mark.parametrize("kw", [SMALL_DEC, SMALL_MIX], ids=["decode", "mixed"])
+def test_physical_block_permutation_invariance(kw):
+    torch = _torch()
+    w, dw = _fresh(kw)
+    base = _rerun(dw)
+    perm = np.random.default_rng(3).permutation(w.num_blocks)
+    inv = np.argsort(perm)
+    # new_pool[perm[b]] = pool[b]
+    dw.k_pool = dw.k_pool.index_select(0, torch.tensor(inv, device="cuda")).contiguous()
+    dw.v_pool = dw.v_pool.index_select(0, torch.tensor(inv, device="cuda")).contiguous()
+    dw.block_table = i32(perm[w.block_table])
+    got = _rerun(dw)
+    assert _same_bits(got, base)
+
+
+@pytest.mark.parametrize("kw", [SMALL_DEC, SMALL_MIX], ids=["decode", "mixed"])
+def test_attention_never_writes_the_pools(kw):
+    torch = _torch()
+    w, dw = _fresh(kw)
+    k0, v0 = dw.k_pool.clone(), dw.v_pool.clone()
+    _rerun(dw)
+    _rerun(dw)
+    assert _same_bits(dw.k_pool, k0) and _same_bits(dw.v_pool, v0)
+
+
+def test_request_alone_equals_request_in_batch():
+    """A request's decode output does not depend on the rest of the batch."""
+    torch = _torch()
+    w, dw = _fresh(SMALL_DEC)
+    base = _rerun(dw)
+    for r in [0, 4, w.num_reqs - 1]:
+        L = int(w.seq_lens[r])
+        one = torch.empty((1, w.hq, w.d), dtype=dw.dtype, device="cuda")
+        ws = torch.zeros(pic.pic_attn_workspace_size(1, 1, L, w.hq, w.hkv, w.d, dw.dtype),
+                         dtype=torch.uint8, device="cuda")
+        k0 = int(w.cu_seqlens_k[r])
+        pic.pic_attn_decode(dw.q[r:r + 1].contiguous(), dw.q_pos[r:r + 1].contiguous(),
+                            dw.k_pool, dw.v_pool, dw.block_table[r:r + 1].contiguous(),
+                            dw.seq_lens[r:r + 1].contiguous(), i32(np.array([0, L])),
+                            dw.k_pos[k0:k0 + L].contiguous(), dw.cos, dw.sin, L, one, ws)
+        torch.cuda.synchronize()
+        assert _same_bits(one[0], base[r]), r
+
+
+def test_decode_launch_equals_mixed_launch():
+    """The same decode batch through pic_attn_decode and pic_attn_prefill."""
+    w, dw = _fresh(SMALL_DEC)
+    a = _rerun(dw, decode=True)
+    b = _rerun(dw, decode=False)
+    assert _same_bits(a, b)
+
+
+def test_prefill_request_alone_equals_in_mixed_batch():
+    torch = _torch()
+    w, dw = _fresh(SMALL_MIX)
+    base = _rerun(dw)
+    ql = w.q_lens()
+    r = int(np.nonzero(ql > 1)[0][0])
+    q0, q1 = int(w.cu_seqlens_q[r]), int(w.cu_seqlens_q[r + 1])
+    L = int(w.seq_lens[r])
+    k0 = int(w.cu_seqlens_k[r])
+    one = torch.empty((q1 - q0, w.hq, w.d), dtype=dw.dtype, device="cuda")
+    ws = torch.zeros(pic.pic_attn_workspace_size(1, q1 - q0, L, w.hq, w.hkv, w.d, dw.dtype),
+                     dtype=torch.uint8, device="cuda")
+    pic.pic_attn_prefill(dw.q[q0:q1].contiguous(), i32(np.array([0, q1 - q0])),
+                         dw.q_pos[q0:q1].contiguous(), dw.k_pool, dw.v_pool,
+                         dw.block_table[r:r + 1].contiguous(), dw.seq_lens[r:r + 1].contiguous(),
+                         i32(np.array([0, L])), dw.k_pos[k0:k0 + L].contiguous(), dw.cos, dw.sin,
+                         q1 - q0, L, one, ws)
+    torch.cuda.synchronize()
+    assert _same_bits(one, base[q0:q1])
+
+
+def test_workspace_reuse_across_calls_and_shapes():
+    torch = _torch()
+    w, dw = _fresh(SMALL_DEC)
+    a = _rerun(dw)
+    w2, dw2 = _fresh(SMALL_MIX)
+    # the mixed batch borrows the first workspace if it is large enough
+    need = pic.pic_attn_workspace_size(w2.num_reqs, w2.total_q, w2.max_seq_len, w2.hq, w2.hkv,
+                                       w2.d, dw2.dtype)
+    if dw.workspace.numel() >= need:
+        dw2.workspace = dw.workspace
+    _rerun(dw2)
+    b = _rerun(dw)
+    c = _rerun(dw)
+    assert _same_bits(a, b) and _same_bits(b, c)
+
+
+# ---------------------------------------------------------------------------
+# degenerate shapes
+# ---------------------------------------------------------------------------
+
+def test_empty_batch_and_empty_context():
+    torch = _torch()
+    w, dw = _fresh(SMALL_DEC)
+    # zero requests: no-op, no error
+    pic.pic_attn_decode(dw.q[:0], dw.q_pos[:0], dw.k_pool, dw.v_pool, dw.block_table[:0],
+                        dw.seq_lens[:0], dw.cu_k[:1], dw.k_pos, dw.cos, dw.sin, w.max_seq_len,
+                        dw.out[:0], dw.workspace)
+    # a request with seq_len 0 gets a zero row; its neighbours are unaffected
+    base = _rerun(dw)
+    sl = w.seq_lens.copy()
+    sl[2] = 0
+    cu = np.concatenate([[0], np.cumsum(sl)]).astype(np.int32)
+    kp = np.concatenate([w.k_pos[w.cu_seqlens_k[r]:w.cu_seqlens_k[r] + sl[r]]
+                         for r in range(w.num_reqs)]).astype(np.int32)
+    dw.seq_lens, dw.cu_k, dw.k_pos = i32(sl), i32(cu), i32(kp)
+    got = _rerun(dw)
+    assert torch.count_nonzero(got[2].float()) == 0
+    keep = [r for r in range(w.num_reqs) if r != 2]
+    assert _same_bits(got[keep], base[keep])
+
+
+def test_single_key_context():
+    """seq_len 1: the output is that key's V row exactly (softmax of one score)."""
+    torch = _torch()
+    w, dw = _fresh(SMALL_DEC)
+    sl = np.ones(w.num_reqs, np.int32)
+    cu = np.arange(w.num_reqs + 1, dtype=np.int32)
+    kp = np.array([w.k_pos[w.cu_seqlens_k[r]] for r in range(w.num_reqs)], np.int32)
+    dw.seq_lens, dw.cu_k, dw.k_pos = i32(sl), i32(cu), i32(kp)
+    got = _rerun(dw)
+    G = w.hq // w.hkv
+    for r in range(w.num_reqs):
+        blk = int(w.block_table[r, 0])
+        for h in range(w.hq):
+            assert _same_bits(got[r, h], dw.v_pool[blk, h // G, :, 0]), (r, h)
