@@ -704,6 +704,310 @@ __device__ void prefill_tile(const AttnArgs& a, int r, int g, int tile, unsigned
 }
 
 // ---------------------------------------------------------------------------
+// bf16 prefill tile on 32x32x16 MFMAs: request r, kv head g, query rows
+// [tile*ROWS, tile*ROWS + ROWS), ROWS = 4 waves x 32 x NCB
+// ---------------------------------------------------------------------------
+
+template <int D, int NCB>
+struct Pf {
+  static constexpr int KSTEP = 64;                 // keys per step
+  static constexpr int ROWS = kWaves * 32 * NCB;   // query rows per tile
+  static constexpr int NCH = D / 16;               // 16-wide d chunks (MFMA K)
+  static constexpr int NHC = NCH / 2;              // chunks of the first half of d
+  static constexpr int NDB = D / 32;               // 32-row d blocks of O^T
+  static constexpr int KLD = D + 8;                // LDS K row stride (bf16)
+  static constexpr int VLD = KSTEP + 8;            // LDS V^T row stride (bf16)
+  static constexpr int STAGE = KSTEP * KLD + D * VLD;  // bf16 elements per LDS stage
+  static constexpr int BYTES = 2 * STAGE * 2;      // two stages
+  static constexpr int KPT = KSTEP * (D / 2) / kThreads;  // rotation pairs per thread
+  static constexpr int KTPK = (D / 2) / KPT;              // threads per key
+  static constexpr int VPT = KSTEP * D / kThreads;        // V elements per thread
+  static constexpr int VTPR = KSTEP / VPT;                // threads per V^T row
+  static_assert(VPT % kBlockSize == 0, "a thread stages whole 16-key V runs");
+};
+
+// One prefill tile, bf16.  Each 64-key step is gathered from the paged pools
+// once per workgroup: every thread loads its share of K rows, cos/sin rows and
+// V^T runs into registers one step ahead (the loads fly while the previous
+// step computes), then rotates its K pairs and writes K and V^T into the
+// other half of a double-buffered LDS stage.  One barrier per step.  Each
+// wave owns 32*NCB query rows (the B operand, rotated once) and runs
+// 2*NCB*NCH score MFMAs and 4*NCB*NDB PV MFMAs per step.  Steps that lie
+// wholly below the causal diagonal skip the mask.
+template <int D, int NCB>
+__device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
+                                  unsigned char* smem) {
+  using P = Pf<D, NCB>;
+  typedef Mma32::Op Op;
+  typedef Mma32::Acc Acc;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int hh = lane >> 5;
+  const int G = a.group;
+  const int q0 = a.cu_q[r];
+  const int ql = a.cu_q[r + 1] - q0;
+  const int L = seq_len_of(a, r);
+  const int nrows = ql * G;
+  const int trow0 = tile * P::ROWS;
+  const int first_tok = trow0 / G;
+  const int last_tok = min((trow0 + P::ROWS - 1) / G, ql - 1);
+  const int kend = min(L, L - ql + last_tok + 1);  // slots any row of the tile sees
+  const int kfull = max(0, L - ql + first_tok + 1);  // slots every row of the tile sees
+  const int nsteps = cdiv(kend, P::KSTEP);
+
+  // rotated query operands (B of S^T = K Q^T), one per column block and d chunk
+  Op qop[NCB][P::NCH];
+  int lim[NCB], tok_of[NCB], head_of[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int n = trow0 + wave * 32 * NCB + cb * 32 + col;
+    const bool valid = n < nrows;
+    const int nn = valid ? n : 0;
+    tok_of[cb] = nn / G;
+    head_of[cb] = nn % G;
+    lim[cb] = valid ? L - ql + tok_of[cb] : -1;
+    const bf16* qp = (const bf16*)a.q + (((size_t)q0 + tok_of[cb]) * a.hq + g * G + head_of[cb]) * D +
+                     hh * 8;
+    const int pos = clampi(a.q_pos[q0 + tok_of[cb]], 0, a.max_pos - 1);
+    const float* cr = a.cos_tab + (size_t)pos * (D / 2) + hh * 8;
+    const float* sr = a.sin_tab + (size_t)pos * (D / 2) + hh * 8;
+#pragma unroll
+    for (int c = 0; c < P::NCH; ++c) qop[cb][c] = *reinterpret_cast<const Op*>(qp + c * 16);
+#pragma unroll
+    for (int c = 0; c < P::NHC; ++c) {
+      const vec<float, 8> cv = *reinterpret_cast<const vec<float, 8>*>(cr + c * 16);
+      const vec<float, 8> sv = *reinterpret_cast<const vec<float, 8>*>(sr + c * 16);
+      float lo[8], hi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)qop[cb][c][e], y = (float)qop[cb][c + P::NHC][e];
+        lo[e] = x * cv[e] - y * sv[e];
+        hi[e] = y * cv[e] + x * sv[e];
+      }
+      qop[cb][c] = Mma<bf16>::pack(lo);
+      qop[cb][c + P::NHC] = Mma<bf16>::pack(hi);
+    }
+    if (!valid) {
+#pragma unroll
+      for (int c = 0; c < P::NCH; ++c) qop[cb][c] = Mma<bf16>::zero();
+    }
+  }
+
+  bf16* stage0 = reinterpret_cast<bf16*>(smem);
+  const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
+  const int32_t* kp = a.k_pos + a.cu_k[r];
+  const bf16* kpool = (const bf16*)a.k_pool;
+  const bf16* vpool = (const bf16*)a.v_pool;
+  const int nb_max = a.num_blocks - 1;
+  const int pmax = a.max_pos - 1;
+  const size_t blk_stride = (size_t)a.hkv * kBlockSize * D;
+
+  // staging: thread -> (key, KPT pairs) for K and the table, (d row, VPT keys) for V
+  const int skey = tid / P::KTPK;
+  const int si0 = (tid % P::KTPK) * P::KPT;
+  const int vd = tid / P::VTPR;
+  const int vk0 = (tid % P::VTPR) * P::VPT;
+  typedef vec<bf16, P::KPT> KV;
+  typedef vec<float, P::KPT> TV;
+  typedef vec<bf16, kBlockSize> VR;
+  KV klo, khi;
+  TV tc, ts;
+  VR vr[P::VPT / kBlockSize];
+  // addresses of a step (block ids, position): looked up one step before the
+  // step's data loads are issued, so those never wait on the lookup
+  struct StepMeta {
+    int kblk, koff, pos;
+    int vblk[P::VPT / kBlockSize];
+  };
+  auto load_meta = [&](int kb, StepMeta& sm_) {
+    const int kc = min(kb + skey, L - 1);
+    sm_.kblk = bt[kc >> 4];
+    sm_.koff = kc & 15;
+    sm_.pos = kp[kc];
+#pragma unroll
+    for (int u = 0; u < P::VPT / kBlockSize; ++u)
+      sm_.vblk[u] = bt[min(kb + vk0 + u * kBlockSize, L - 1) >> 4];
+  };
+  auto load_step = [&](const StepMeta& sm_) {
+    const int blk = clampi(sm_.kblk, 0, nb_max);
+    const int pos = clampi(sm_.pos, 0, pmax);
+    const bf16* src = kpool + blk * blk_stride + ((size_t)g * kBlockSize + sm_.koff) * D + si0;
+    klo = *reinterpret_cast<const KV*>(src);
+    khi = *reinterpret_cast<const KV*>(src + D / 2);
+    tc = *reinterpret_cast<const TV*>(a.cos_tab + (size_t)pos * (D / 2) + si0);
+    ts = *reinterpret_cast<const TV*>(a.sin_tab + (size_t)pos * (D / 2) + si0);
+#pragma unroll
+    for (int u = 0; u < P::VPT / kBlockSize; ++u) {
+      const int vb = clampi(sm_.vblk[u], 0, nb_max);
+      vr[u] = *reinterpret_cast<const VR*>(vpool + vb * blk_stride +
+                                           ((size_t)g * D + vd) * kBlockSize);
+    }
+  };
+  auto store_step = [&](int kb, bf16* st, auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    float lo[P::KPT], hi[P::KPT];
+#pragma unroll
+    for (int e = 0; e < P::KPT; ++e) {
+      const float x = (float)klo[e], y = (float)khi[e];
+      lo[e] = x * tc[e] - y * ts[e];
+      hi[e] = y * tc[e] + x * ts[e];
+    }
+    bf16* kd = st + skey * P::KLD + si0;
+#pragma unroll
+    for (int e0 = 0; e0 < P::KPT; e0 += 8) {
+      *reinterpret_cast<Op*>(kd + e0) = Mma<bf16>::pack(lo + e0);
+      *reinterpret_cast<Op*>(kd + D / 2 + e0) = Mma<bf16>::pack(hi + e0);
+    }
+    bf16* vdst = st + P::KSTEP * P::KLD + vd * P::VLD + vk0;
+#pragma unroll
+    for (int u = 0; u < P::VPT / kBlockSize; ++u) {
+      VR x = vr[u];
+      if constexpr (TAIL) {  // slots at or beyond L hold no data
+        const int key0 = kb + vk0 + u * kBlockSize;
+#pragma unroll
+        for (int e = 0; e < kBlockSize; ++e)
+          if (key0 + e >= L) x[e] = (bf16)0.0f;
+      }
+      *reinterpret_cast<VR*>(vdst + u * kBlockSize) = x;
+    }
+  };
+
+  Acc o[P::NDB][NCB];
+  float m_run[NCB], l_run[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+    for (int db = 0; db < P::NDB; ++db) o[db][cb] = Acc{};
+    m_run[cb] = -INFINITY;
+    l_run[cb] = 0.0f;
+  }
+
+  // staging of step kb: only a step that reaches past L needs the V zeroing
+  auto store_any = [&](int kb, bf16* st) {
+    if (kb + P::KSTEP > L) store_step(kb, st, std::true_type{});
+    else store_step(kb, st, std::false_type{});
+  };
+  StepMeta meta;  // addresses of the step after the one being loaded
+  if (nsteps > 0) {
+    load_meta(0, meta);
+    load_step(meta);
+    if (nsteps > 1) load_meta(P::KSTEP, meta);
+    store_any(0, stage0);
+  }
+  __syncthreads();
+
+  // steps wholly below the causal diagonal of every row skip the mask
+  auto step = [&](int j, auto mask_tag) {
+    constexpr bool MASKED = decltype(mask_tag)::value;
+    const int kb = j * P::KSTEP;
+    const bf16* st = stage0 + (j & 1) * P::STAGE;
+    if (j + 1 < nsteps) {
+      load_step(meta);
+      if (j + 2 < nsteps) load_meta(kb + 2 * P::KSTEP, meta);
+    }
+
+    // S^T = K_rot Q_rot^T for the step's two 32-key blocks
+    Acc sc[2][NCB];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) sc[kb2][cb] = Acc{};
+      const bf16* krow = st + (kb2 * 32 + key32(col)) * P::KLD + hh * 8;
+#pragma unroll
+      for (int c = 0; c < P::NCH; ++c) {
+        const Op ka = *reinterpret_cast<const Op*>(krow + c * 16);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) sc[kb2][cb] = Mma32::run(ka, qop[cb][c], sc[kb2][cb]);
+      }
+    }
+
+    // causal mask (masked steps only), online softmax per column (scores kept
+    // raw: the base-2 scale is folded into the exponent's FMA), probabilities
+    // -> bf16 B operands
+    Op pb[2][2][NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          if constexpr (MASKED) {
+            const int key = kb + kb2 * 32 + key32(8 * (v >> 2) + 4 * hh + (v & 3));
+            if (key > lim[cb]) sc[kb2][cb][v] = -INFINITY;
+          }
+          mx = fmaxf(mx, sc[kb2][cb][v]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+      if (__any(mx > m_run[cb] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run[cb], mx);
+        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run[cb] - m_new);
+        l_run[cb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < P::NDB; ++db) o[db][cb] *= alpha;
+        m_run[cb] = m_new;
+      }
+      const float nbase = m_run[cb] == -INFINITY ? 0.0f : -m_run[cb];
+      float psum = 0.0f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = fast_exp2(fmaf(sc[kb2][cb][8 * m + e], a.scale_log2, nbase));
+            psum += p[e];
+          }
+          pb[kb2][m][cb] = Mma<bf16>::pack(p);
+        }
+      l_run[cb] += psum;
+    }
+
+    // O^T += V^T P^T
+    const bf16* vs = st + P::KSTEP * P::KLD;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int db = 0; db < P::NDB; ++db) {
+          const Op va = *reinterpret_cast<const Op*>(vs + (db * 32 + col) * P::VLD + kb2 * 32 +
+                                                     16 * m + 8 * hh);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) o[db][cb] = Mma32::run(va, pb[kb2][m][cb], o[db][cb]);
+        }
+
+    if (j + 1 < nsteps) store_any(kb + P::KSTEP, stage0 + ((j + 1) & 1) * P::STAGE);
+    __syncthreads();
+  };
+
+  // the leading steps lie below every row's causal limit: no mask there
+  const int jfull = min(nsteps, kfull / P::KSTEP);
+  for (int j = 0; j < jfull; ++j) step(j, std::false_type{});
+  for (int j = jfull; j < nsteps; ++j) step(j, std::true_type{});
+
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const float l_tot = l_run[cb] + __shfl_xor(l_run[cb], 32);
+    if (lim[cb] < 0) continue;
+    const float inv = 1.0f / l_tot;
+    bf16* out = (bf16*)a.out + (((size_t)q0 + tok_of[cb]) * a.hq + g * G + head_of[cb]) * D;
+#pragma unroll
+    for (int db = 0; db < P::NDB; ++db)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        vec<bf16, 4> w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[db][cb][4 * v4 + i] * inv);
+        *reinterpret_cast<vec<bf16, 4>*>(out + db * 32 + 8 * v4 + 4 * hh) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // kernels
 // ---------------------------------------------------------------------------
 
@@ -748,11 +1052,18 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
   decode_item<T, D, kDecodeDepth>(a, r, hg, s, r, smem);
 }
 
+// Column blocks (of 32 query rows) per wave in the bf16 prefill tile.
+constexpr int kPrefillNCB = 1;
+
+template <typename T, int D>
+constexpr int prefill_rows() {
+  return sizeof(T) == 2 ? Pf<D, kPrefillNCB>::ROWS : kPrefillRows;
+}
+
 template <typename T, int D>
 struct MixedSmem {
-  static constexpr int BYTES = PrefillSmem<T, D>::BYTES > (int)sizeof(DecodeSmem<T, D>)
-                                   ? PrefillSmem<T, D>::BYTES
-                                   : (int)sizeof(DecodeSmem<T, D>);
+  static constexpr int PB = sizeof(T) == 2 ? Pf<D, kPrefillNCB>::BYTES : PrefillSmem<T, D>::BYTES;
+  static constexpr int BYTES = PB > (int)sizeof(DecodeSmem<T, D>) ? PB : (int)sizeof(DecodeSmem<T, D>);
 };
 
 // Mixed launch over the planner's work list.
@@ -762,7 +1073,11 @@ __global__ void __launch_bounds__(kThreads, 2) mixed_kernel(AttnArgs a) {
   if ((int)blockIdx.x >= *a.nitems) return;
   const int4 it = a.items[blockIdx.x];
   if (it.x == kItemPrefill) {
-    prefill_tile<T, D>(a, it.y, it.z, it.w, smem);
+    if constexpr (sizeof(T) == 2) {
+      prefill_tile_bf16<D, kPrefillNCB>(a, it.y, it.z, it.w, smem);
+    } else {
+      prefill_tile<T, D>(a, it.y, it.z, it.w, smem);
+    }
   } else {
     decode_item<T, D, 1>(a, it.y, it.z, it.w, (long long)a.cu_q[it.y], smem);
   }
@@ -776,7 +1091,8 @@ __global__ void __launch_bounds__(kThreads, 2) mixed_kernel(AttnArgs a) {
 __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ cu_q,
                                                     const int32_t* __restrict__ seq_lens,
                                                     int num_reqs, int hkv, int group, int nhg,
-                                                    int kstep, int len_cap, long long max_items,
+                                                    int kstep, int rows, int len_cap,
+                                                    long long max_items,
                                                     int4* __restrict__ items,
                                                     int* __restrict__ count) {
   __shared__ long long s_a[1024];
@@ -787,7 +1103,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   long long pf = 0, dc = 0;
   for (int r = tid; r < num_reqs; r += 1024) {
     const int ql = cu_q[r + 1] - cu_q[r];
-    if (ql > 1) pf += (long long)hkv * cdiv(ql * group, kPrefillRows);
+    if (ql > 1) pf += (long long)hkv * cdiv(ql * group, rows);
     else if (ql == 1) dc += (long long)nhg * num_splits(min(seq_lens[r], len_cap), kstep);
   }
   s_a[tid] = pf;
@@ -822,7 +1138,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
     if (r < num_reqs) {
       ql = cu_q[r + 1] - cu_q[r];
       L = min(seq_lens[r], len_cap);
-      if (ql > 1) npf = (long long)hkv * cdiv(ql * group, kPrefillRows);
+      if (ql > 1) npf = (long long)hkv * cdiv(ql * group, rows);
       else if (ql == 1) ndc = (long long)nhg * num_splits(L, kstep);
     }
     __syncthreads();
@@ -840,7 +1156,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
     const long long off_pf = s_tot[0] + s_a[tid] - npf;
     const long long off_dc = total_pf + s_tot[1] + s_b[tid] - ndc;
     if (ql > 1) {
-      const int tiles = cdiv(ql * group, kPrefillRows);
+      const int tiles = cdiv(ql * group, rows);
       for (int g = 0; g < hkv; ++g)
         for (int k = 0; k < tiles; ++k) {
           const long long l = off_pf + (long long)g * tiles + k;
@@ -924,7 +1240,8 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
   const int len_cap = (int)min((long long)h.max_seq_len,
                               (long long)h.block_table_stride * kBlockSize);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, h.cu_seqlens_q, h.seq_lens,
-                     h.num_reqs, h.hkv, h.hq / h.hkv, w.nhg, Cfg<T, D>::KSTEP, len_cap,
+                     h.num_reqs, h.hkv, h.hq / h.hkv, w.nhg, Cfg<T, D>::KSTEP,
+                     prefill_rows<T, D>(), len_cap,
                      w.max_items, (int4*)(ws + w.items_off), (int*)(ws + w.count_off));
   hipLaunchKernelGGL((mixed_kernel<T, D>), dim3((unsigned)w.max_items), dim3(kThreads), 0, s, a);
   launch_combine<T, D>(a, s);

@@ -72,6 +72,26 @@ struct Mma<float> {
 template <typename T>
 using OpT = typename Mma<T>::Op;
 
+// v_mfma_f32_32x32x16_bf16.  Lane layout (lane = 32 * h + c, h in {0, 1}):
+//   A (32 rows x 16): lane holds A[c][8h .. 8h+7]
+//   B (16 x 32 cols): lane holds B[8h .. 8h+7][c]
+//   C (32 x 32)     : lane holds C[8*(v/4) + 4h + v%4][c], v = 0..15
+struct Mma32 {
+  typedef vec<bf16, 8> Op;
+  typedef vec<float, 16> Acc;
+  static __device__ __forceinline__ Acc run(Op a, Op b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Key (within a 32-key block) held in C row rho, chosen so that PV MFMA m's
+// B operand -- K elements 8h..8h+7 -- is the lane's C values v = 8m..8m+7 and
+// covers the 8 consecutive keys 16m + 8h .. 16m + 8h + 7.
+__device__ __forceinline__ int key32(int rho) {
+  const int j = rho >> 3, h = (rho >> 2) & 1, i = rho & 3;
+  return 16 * (j >> 1) + 8 * h + 4 * (j & 1) + i;
+}
+
 // N contiguous elements, loaded / stored as one vector access when N > 1.
 template <typename T, int N>
 struct Run {
