@@ -184,6 +184,10 @@ __device__ __forceinline__ void load_query(const AttnArgs& a, long long qrow, in
 // kRescaleSlack, so most steps skip the rescale; the probabilities stay
 // <= 2^kRescaleSlack and the final o = acc / l is unchanged.
 constexpr float kRescaleSlack = 8.0f;
+// Largest probability sum of one 32-key block that the prefill tile's first
+// pass accepts (2^32): with it no accumulator can overflow for any finite
+// bf16 value below 2^70.
+constexpr float kPBig = 4294967296.0f;
 
 template <int NT, int ND>
 __device__ __forceinline__ void softmax_step(f32x4 (&s)[NT], f32x4 (&acc)[ND], float& m,
@@ -271,9 +275,10 @@ struct DecodeSmem {
   int blk[kMaxChunk / kBlockSize + 2];
 };
 
-// One decode work item: request r, key chunk s, kv heads hg*4 .. hg*4+3 (one
-// per wave).  All four waves walk the same keys: each step's cos/sin rows are
-// fetched once per workgroup and shared through LDS, while every wave reads
+// One decode work item: request r, key chunk s, kv heads hg*NW .. hg*NW+NW-1
+// (one per wave of the NW-wave workgroup).  All waves walk the same keys:
+// each step's cos/sin rows are fetched once per workgroup and shared through
+// LDS, while every wave reads
 // its own head's K rows and V runs from the pools into registers.  NB steps
 // of loads are kept in flight (a ring of NB register buffers): the loads of
 // step j+NB are issued as soon as step j has consumed its buffer.  The
@@ -281,7 +286,7 @@ struct DecodeSmem {
 // address lookup ever waits behind the data loads.  With one chunk the wave
 // writes the output row; otherwise it writes a normalised partial and
 // (max, sum) that combine_kernel merges.  Uniform across the workgroup.
-template <typename T, int D, int NB>
+template <typename T, int D, int NB, int NW>
 __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long qrow,
                             unsigned char* smem_raw) {
   using C = Cfg<T, D>;
@@ -293,7 +298,8 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   const int lane = tid & 63;
   const int row16 = lane & 15;
   const int grp = lane >> 4;
-  const int g = hg * kWaves + wave;
+  constexpr int NTH = NW * 64;
+  const int g = hg * NW + wave;
   const bool active = g < a.hkv;
   const int ga = active ? g : 0;  // a valid head for the loads of an idle wave
   const int G = a.group;
@@ -317,10 +323,10 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
     const int32_t* kp = a.k_pos + a.cu_k[r];
     const int nk = nsteps * C::KSTEP;
-    for (int j = tid; j < nk; j += kThreads)
+    for (int j = tid; j < nk; j += NTH)
       sm.pos[j] = clampi(kp[min(k0 + j, L - 1)], 0, a.max_pos - 1);
     const int nbk = nk / kBlockSize;
-    for (int j = tid; j < nbk; j += kThreads)
+    for (int j = tid; j < nbk; j += NTH)
       sm.blk[j] = clampi(bt[min((k0 >> 4) + j, (L - 1) >> 4)], 0, a.num_blocks - 1);
   }
 
@@ -341,7 +347,8 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   const int vkey_off = (grp * 4 * C::NT) & 15;
 
   // table staging: thread -> (key of the step, TPT consecutive pairs)
-  constexpr int TPT = C::KSTEP * (D / 2) / kThreads;
+  constexpr int TPT = C::KSTEP * (D / 2) / NTH;
+  static_assert(TPT >= 1, "at least one table pair per thread");
   constexpr int TPK = (D / 2) / TPT;
   typedef Run<float, TPT> RF;
   const int skey = tid / TPK;
@@ -705,39 +712,77 @@ __device__ void prefill_tile(const AttnArgs& a, int r, int g, int tile, unsigned
 
 // ---------------------------------------------------------------------------
 // bf16 prefill tile on 32x32x16 MFMAs: request r, kv head g, query rows
-// [tile*ROWS, tile*ROWS + ROWS), ROWS = 4 waves x 32 x NCB
+// [tile*ROWS, tile*ROWS + ROWS), ROWS = 32 per wave
 // ---------------------------------------------------------------------------
 
-template <int D, int NCB>
+// Scheduling groups (mask bits of __builtin_amdgcn_sched_group_barrier).
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgDsWrite = 0x200;
+
+// Eight MFMAs, each followed by R LDS reads and V vector instructions.
+template <int R, int V>
+__device__ __forceinline__ void sched_phase() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, R, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, V, 0);
+  }
+}
+
+// Order of one prefill step: score MFMAs with softmax work, PV MFMAs with
+// staging work.
+__device__ __forceinline__ void sched_interleave() {
+  sched_phase<2, 6>();
+  sched_phase<1, 5>();
+  sched_phase<2, 6>();
+  sched_phase<1, 5>();
+}
+
+template <int D, int NW>
 struct Pf {
-  static constexpr int KSTEP = 64;                 // keys per step
-  static constexpr int ROWS = kWaves * 32 * NCB;   // query rows per tile
+  static constexpr int NTH = NW * 64;              // threads
+  static constexpr int KSTEP = 64;                 // keys per step (two 32-key blocks)
+  static constexpr int ROWS = NW * 32;             // query rows per tile
   static constexpr int NCH = D / 16;               // 16-wide d chunks (MFMA K)
   static constexpr int NHC = NCH / 2;              // chunks of the first half of d
   static constexpr int NDB = D / 32;               // 32-row d blocks of O^T
   static constexpr int KLD = D + 8;                // LDS K row stride (bf16)
   static constexpr int VLD = KSTEP + 8;            // LDS V^T row stride (bf16)
-  static constexpr int STAGE = KSTEP * KLD + D * VLD;  // bf16 elements per LDS stage
-  static constexpr int BYTES = 2 * STAGE * 2;      // two stages
-  static constexpr int KPT = KSTEP * (D / 2) / kThreads;  // rotation pairs per thread
-  static constexpr int KTPK = (D / 2) / KPT;              // threads per key
-  static constexpr int VPT = KSTEP * D / kThreads;        // V elements per thread
-  static constexpr int VTPR = KSTEP / VPT;                // threads per V^T row
-  static_assert(VPT % kBlockSize == 0, "a thread stages whole 16-key V runs");
+  static constexpr int QLD = D + 8;                // LDS row stride of the query operand
+  static constexpr int KBUF = KSTEP * KLD;         // bf16 elements of one K stage
+  static constexpr int VBUF = D * VLD;             // bf16 elements of one V^T stage
+  static constexpr int NKB = 3, NVB = 2;           // K and V^T stages
+  static constexpr int V_OFF = NKB * KBUF;
+  static constexpr int Q_OFF = V_OFF + NVB * VBUF;
+  static constexpr int BYTES = (Q_OFF + ROWS * QLD) * 2;
+  static constexpr int KPT = KSTEP * (D / 2) / NTH;  // rotation pairs per thread
+  static constexpr int KTPK = (D / 2) / KPT;         // threads per key
+  static constexpr int VPT = KSTEP * D / NTH;        // V^T elements per thread
+  static constexpr int VTPR = KSTEP / VPT;           // threads per V^T row
+  static constexpr int VR = VPT < kBlockSize ? VPT : kBlockSize;  // keys per V load
+  static constexpr int NVR = VPT / VR;                             // V loads per thread
+  static_assert(KPT % 4 == 0 && KPT <= D / 2, "whole 8-byte K pieces per thread");
+  static_assert(VPT % VR == 0 && kBlockSize % VR == 0, "V runs stay inside one block");
 };
 
-// One prefill tile, bf16.  Each 64-key step is gathered from the paged pools
-// once per workgroup: every thread loads its share of K rows, cos/sin rows and
-// V^T runs into registers one step ahead (the loads fly while the previous
-// step computes), then rotates its K pairs and writes K and V^T into the
-// other half of a double-buffered LDS stage.  One barrier per step.  Each
-// wave owns 32*NCB query rows (the B operand, rotated once) and runs
-// 2*NCB*NCH score MFMAs and 4*NCB*NDB PV MFMAs per step.  Steps that lie
-// wholly below the causal diagonal skip the mask.
-template <int D, int NCB>
+// One prefill tile, bf16, software-pipelined over 32-key blocks so each wave
+// always has matrix and vector work in flight together: the score MFMAs of
+// block b+1 run while block b is exponentiated, and the PV MFMAs of block b
+// run while the next K step is rotated into LDS.
+//
+// Staging: each 64-key step is gathered from the paged pools once per
+// workgroup.  Every thread loads its share of K rows, cos/sin rows and V^T
+// runs into registers one step before they are written; K is rotated on the
+// way into LDS.  K is staged two steps ahead (three K stages: the block
+// being exponentiated may be re-read, the next block is being multiplied,
+// and the step after is being written), V^T one step ahead (two stages).
+// One barrier per step.  The rotated query rows (the B operand, pre-scaled
+// by log2(e)/sqrt(d) so scores come out in base-2 units) sit in a per-wave
+// LDS slice.  Steps that lie wholly below the causal diagonal skip the mask.
+template <int D, int NW>
 __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
                                   unsigned char* smem) {
-  using P = Pf<D, NCB>;
+  using P = Pf<D, NW>;
   typedef Mma32::Op Op;
   typedef Mma32::Acc Acc;
   const int tid = threadIdx.x;
@@ -756,25 +801,23 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
   const int kend = min(L, L - ql + last_tok + 1);  // slots any row of the tile sees
   const int kfull = max(0, L - ql + first_tok + 1);  // slots every row of the tile sees
   const int nsteps = cdiv(kend, P::KSTEP);
+  bf16* const lds = reinterpret_cast<bf16*>(smem);
 
-  // rotated query operands (B of S^T = K Q^T), one per column block and d chunk
-  Op qop[NCB][P::NCH];
-  int lim[NCB], tok_of[NCB], head_of[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int n = trow0 + wave * 32 * NCB + cb * 32 + col;
-    const bool valid = n < nrows;
-    const int nn = valid ? n : 0;
-    tok_of[cb] = nn / G;
-    head_of[cb] = nn % G;
-    lim[cb] = valid ? L - ql + tok_of[cb] : -1;
-    const bf16* qp = (const bf16*)a.q + (((size_t)q0 + tok_of[cb]) * a.hq + g * G + head_of[cb]) * D +
-                     hh * 8;
-    const int pos = clampi(a.q_pos[q0 + tok_of[cb]], 0, a.max_pos - 1);
+  // query row of this lane's column, its causal limit, and its LDS slice
+  const int n = trow0 + wave * 32 + col;
+  const bool valid = n < nrows;
+  const int tok = (valid ? n : 0) / G;
+  const int head = (valid ? n : 0) % G;
+  const int lim = valid ? L - ql + tok : -1;  // last visible key slot of this row
+  bf16* const qs = lds + P::Q_OFF + (wave * 32 + col) * P::QLD + hh * 8;
+  {
+    Op qop[P::NCH];
+    const bf16* qp = (const bf16*)a.q + (((size_t)q0 + tok) * a.hq + g * G + head) * D + hh * 8;
+    const int pos = clampi(a.q_pos[q0 + tok], 0, a.max_pos - 1);
     const float* cr = a.cos_tab + (size_t)pos * (D / 2) + hh * 8;
     const float* sr = a.sin_tab + (size_t)pos * (D / 2) + hh * 8;
 #pragma unroll
-    for (int c = 0; c < P::NCH; ++c) qop[cb][c] = *reinterpret_cast<const Op*>(qp + c * 16);
+    for (int c = 0; c < P::NCH; ++c) qop[c] = *reinterpret_cast<const Op*>(qp + c * 16);
 #pragma unroll
     for (int c = 0; c < P::NHC; ++c) {
       const vec<float, 8> cv = *reinterpret_cast<const vec<float, 8>*>(cr + c * 16);
@@ -782,228 +825,343 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
       float lo[8], hi[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = (float)qop[cb][c][e], y = (float)qop[cb][c + P::NHC][e];
-        lo[e] = x * cv[e] - y * sv[e];
-        hi[e] = y * cv[e] + x * sv[e];
+        const float x = (float)qop[c][e], y = (float)qop[c + P::NHC][e];
+        lo[e] = (x * cv[e] - y * sv[e]) * a.scale_log2;
+        hi[e] = (y * cv[e] + x * sv[e]) * a.scale_log2;
       }
-      qop[cb][c] = Mma<bf16>::pack(lo);
-      qop[cb][c + P::NHC] = Mma<bf16>::pack(hi);
+      qop[c] = Mma<bf16>::pack(lo);
+      qop[c + P::NHC] = Mma<bf16>::pack(hi);
     }
-    if (!valid) {
 #pragma unroll
-      for (int c = 0; c < P::NCH; ++c) qop[cb][c] = Mma<bf16>::zero();
-    }
+    for (int c = 0; c < P::NCH; ++c)
+      *reinterpret_cast<Op*>(qs + c * 16) = valid ? qop[c] : Mma<bf16>::zero();
   }
 
-  bf16* stage0 = reinterpret_cast<bf16*>(smem);
   const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
   const int32_t* kp = a.k_pos + a.cu_k[r];
-  const bf16* kpool = (const bf16*)a.k_pool;
-  const bf16* vpool = (const bf16*)a.v_pool;
   const int nb_max = a.num_blocks - 1;
   const int pmax = a.max_pos - 1;
-  const size_t blk_stride = (size_t)a.hkv * kBlockSize * D;
+  const size_t blk_bytes = (size_t)a.hkv * kBlockSize * D * sizeof(bf16);
 
-  // staging: thread -> (key, KPT pairs) for K and the table, (d row, VPT keys) for V
+  // staging: thread -> (key skey, pairs si0..si0+KPT) for K and the table,
+  // (d row vd, keys vk0..vk0+VPT) for V^T.  Every step starts at a multiple
+  // of 64, so a thread always reads the same row of a block (skey % 16) and
+  // the same key offset of a V run: the per-step address is block base plus a
+  // fixed per-thread offset.  A key at or beyond L reads a valid slot of the
+  // last block (its score is masked, its V zeroed); a step past the end
+  // re-reads valid slots and is never used.
   const int skey = tid / P::KTPK;
   const int si0 = (tid % P::KTPK) * P::KPT;
   const int vd = tid / P::VTPR;
   const int vk0 = (tid % P::VTPR) * P::VPT;
+  const char* kthr = (const char*)a.k_pool +
+                     (((size_t)g * kBlockSize + (skey & 15)) * D + si0) * sizeof(bf16);
+  const char* cthr = (const char*)(a.cos_tab + si0);
+  const char* sthr = (const char*)(a.sin_tab + si0);
+  const char* vthr = (const char*)a.v_pool +
+                     (((size_t)g * D + vd) * kBlockSize + (vk0 & 15)) * sizeof(bf16);
   typedef vec<bf16, P::KPT> KV;
   typedef vec<float, P::KPT> TV;
-  typedef vec<bf16, kBlockSize> VR;
+  typedef vec<bf16, P::VR> VRun;
   KV klo, khi;
   TV tc, ts;
-  VR vr[P::VPT / kBlockSize];
-  // addresses of a step (block ids, position): looked up one step before the
-  // step's data loads are issued, so those never wait on the lookup
-  struct StepMeta {
-    int kblk, koff, pos;
-    int vblk[P::VPT / kBlockSize];
-  };
-  auto load_meta = [&](int kb, StepMeta& sm_) {
+  VRun vr[P::NVR];
+  // Addresses (block ids, position) of the next loads, looked up one step
+  // before those loads are issued: kmeta_* / vmeta_* hold the ones in use,
+  // the *_nx copies the ones being fetched.  Lookups are issued before the
+  // data loads of a step, so waiting for a lookup never waits for data (the
+  // load counter completes in issue order).
+  int kmeta_blk, kmeta_pos, vmeta_blk[P::NVR];
+  int kmeta_blk_nx, kmeta_pos_nx, vmeta_blk_nx[P::NVR];
+  auto kmeta = [&](int kb) {
     const int kc = min(kb + skey, L - 1);
-    sm_.kblk = bt[kc >> 4];
-    sm_.koff = kc & 15;
-    sm_.pos = kp[kc];
-#pragma unroll
-    for (int u = 0; u < P::VPT / kBlockSize; ++u)
-      sm_.vblk[u] = bt[min(kb + vk0 + u * kBlockSize, L - 1) >> 4];
+    kmeta_blk_nx = bt[kc >> 4];
+    kmeta_pos_nx = kp[kc];
   };
-  auto load_step = [&](const StepMeta& sm_) {
-    const int blk = clampi(sm_.kblk, 0, nb_max);
-    const int pos = clampi(sm_.pos, 0, pmax);
-    const bf16* src = kpool + blk * blk_stride + ((size_t)g * kBlockSize + sm_.koff) * D + si0;
-    klo = *reinterpret_cast<const KV*>(src);
-    khi = *reinterpret_cast<const KV*>(src + D / 2);
-    tc = *reinterpret_cast<const TV*>(a.cos_tab + (size_t)pos * (D / 2) + si0);
-    ts = *reinterpret_cast<const TV*>(a.sin_tab + (size_t)pos * (D / 2) + si0);
+  auto vmeta = [&](int kb) {
 #pragma unroll
-    for (int u = 0; u < P::VPT / kBlockSize; ++u) {
-      const int vb = clampi(sm_.vblk[u], 0, nb_max);
-      vr[u] = *reinterpret_cast<const VR*>(vpool + vb * blk_stride +
-                                           ((size_t)g * D + vd) * kBlockSize);
+    for (int u = 0; u < P::NVR; ++u) vmeta_blk_nx[u] = bt[min(kb + vk0 + u * P::VR, L - 1) >> 4];
+  };
+  auto kmeta_use = [&]() {
+    kmeta_blk = kmeta_blk_nx;
+    kmeta_pos = kmeta_pos_nx;
+  };
+  auto vmeta_use = [&]() {
+#pragma unroll
+    for (int u = 0; u < P::NVR; ++u) vmeta_blk[u] = vmeta_blk_nx[u];
+  };
+  auto kload = [&]() {
+    const unsigned blk = (unsigned)clampi(kmeta_blk, 0, nb_max);
+    const unsigned pos = (unsigned)clampi(kmeta_pos, 0, pmax);
+    const char* src = kthr + (size_t)blk * blk_bytes;
+    klo = *reinterpret_cast<const KV*>(src);
+    khi = *reinterpret_cast<const KV*>(src + D);  // + D/2 elements
+    tc = *reinterpret_cast<const TV*>(cthr + (size_t)pos * (D * 2));  // D/2 floats per row
+    ts = *reinterpret_cast<const TV*>(sthr + (size_t)pos * (D * 2));
+  };
+  auto vload = [&]() {
+#pragma unroll
+    for (int u = 0; u < P::NVR; ++u) {
+      const unsigned vb = (unsigned)clampi(vmeta_blk[u], 0, nb_max);
+      vr[u] = *reinterpret_cast<const VRun*>(vthr + (size_t)vb * blk_bytes);
     }
   };
-  auto store_step = [&](int kb, bf16* st, auto tail_tag) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
-    float lo[P::KPT], hi[P::KPT];
+  auto kstore = [&](int step) {  // rotate the loaded K piece into K stage `step`
+    KV lo, hi;
 #pragma unroll
     for (int e = 0; e < P::KPT; ++e) {
       const float x = (float)klo[e], y = (float)khi[e];
-      lo[e] = x * tc[e] - y * ts[e];
-      hi[e] = y * tc[e] + x * ts[e];
+      lo[e] = (bf16)(x * tc[e] - y * ts[e]);
+      hi[e] = (bf16)(y * tc[e] + x * ts[e]);
     }
-    bf16* kd = st + skey * P::KLD + si0;
+    bf16* kd = lds + (step % P::NKB) * P::KBUF + skey * P::KLD + si0;
+    *reinterpret_cast<KV*>(kd) = lo;
+    *reinterpret_cast<KV*>(kd + D / 2) = hi;
+  };
+  auto vstore = [&](int step) {  // the loaded V^T runs into V stage `step`
+    const int kb = step * P::KSTEP;
+    bf16* vdst = lds + P::V_OFF + (step % P::NVB) * P::VBUF + vd * P::VLD + vk0;
+    if (kb + P::KSTEP > L) {  // slots at or beyond L hold no data
 #pragma unroll
-    for (int e0 = 0; e0 < P::KPT; e0 += 8) {
-      *reinterpret_cast<Op*>(kd + e0) = Mma<bf16>::pack(lo + e0);
-      *reinterpret_cast<Op*>(kd + D / 2 + e0) = Mma<bf16>::pack(hi + e0);
-    }
-    bf16* vdst = st + P::KSTEP * P::KLD + vd * P::VLD + vk0;
+      for (int u = 0; u < P::NVR; ++u) {
+        VRun x = vr[u];
+        const int key0 = kb + vk0 + u * P::VR;
 #pragma unroll
-    for (int u = 0; u < P::VPT / kBlockSize; ++u) {
-      VR x = vr[u];
-      if constexpr (TAIL) {  // slots at or beyond L hold no data
-        const int key0 = kb + vk0 + u * kBlockSize;
-#pragma unroll
-        for (int e = 0; e < kBlockSize; ++e)
+        for (int e = 0; e < P::VR; ++e)
           if (key0 + e >= L) x[e] = (bf16)0.0f;
+        *reinterpret_cast<VRun*>(vdst + u * P::VR) = x;
       }
-      *reinterpret_cast<VR*>(vdst + u * kBlockSize) = x;
+    } else {
+#pragma unroll
+      for (int u = 0; u < P::NVR; ++u) *reinterpret_cast<VRun*>(vdst + u * P::VR) = vr[u];
     }
   };
 
-  Acc o[P::NDB][NCB];
-  float m_run[NCB], l_run[NCB];
+  // S^T - m of one 32-key block (h) of K stage `step` (negm: -m in every
+  // element, the chain's start), d chunk by d chunk, the operands of chunk
+  // c+1 read while chunk c multiplies
+  auto qk_block = [&](int step, int h, const Acc& negm) {
+    const bf16* kr = lds + (step % P::NKB) * P::KBUF + (h * 32 + key32(col)) * P::KLD + hh * 8;
+    Op ka = *reinterpret_cast<const Op*>(kr);
+    Op qb = *reinterpret_cast<const Op*>(qs);
+    Acc sc = negm;
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-    for (int db = 0; db < P::NDB; ++db) o[db][cb] = Acc{};
-    m_run[cb] = -INFINITY;
-    l_run[cb] = 0.0f;
-  }
-
-  // staging of step kb: only a step that reaches past L needs the V zeroing
-  auto store_any = [&](int kb, bf16* st) {
-    if (kb + P::KSTEP > L) store_step(kb, st, std::true_type{});
-    else store_step(kb, st, std::false_type{});
+    for (int c = 0; c < P::NCH; ++c) {
+      Op nka, nqb;
+      if (c + 1 < P::NCH) {
+        nka = *reinterpret_cast<const Op*>(kr + (c + 1) * 16);
+        nqb = *reinterpret_cast<const Op*>(qs + (c + 1) * 16);
+      }
+      sc = Mma32::run(ka, qb, sc);
+      if (c + 1 < P::NCH) {
+        ka = nka;
+        qb = nqb;
+      }
+    }
+    return sc;
   };
-  StepMeta meta;  // addresses of the step after the one being loaded
-  if (nsteps > 0) {
-    load_meta(0, meta);
-    load_step(meta);
-    if (nsteps > 1) load_meta(P::KSTEP, meta);
-    store_any(0, stage0);
-  }
-  __syncthreads();
-
-  // steps wholly below the causal diagonal of every row skip the mask
-  auto step = [&](int j, auto mask_tag) {
-    constexpr bool MASKED = decltype(mask_tag)::value;
-    const int kb = j * P::KSTEP;
-    const bf16* st = stage0 + (j & 1) * P::STAGE;
-    if (j + 1 < nsteps) {
-      load_step(meta);
-      if (j + 2 < nsteps) load_meta(kb + 2 * P::KSTEP, meta);
+  // C element v of this lane holds key kb + 8*hh + kc(v) of the block (kc: a
+  // compile-time constant, from key32)
+  auto mask_block = [&](Acc& sc, int kb) {  // kb: first key of the block
+    const int t = lim - kb - 8 * hh;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int kc = 16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3);
+      if (kc > t) sc[v] = -INFINITY;
     }
-
-    // S^T = K_rot Q_rot^T for the step's two 32-key blocks
-    Acc sc[2][NCB];
+  };
+  auto col_max = [&](const Acc& sc) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) sc[kb2][cb] = Acc{};
-      const bf16* krow = st + (kb2 * 32 + key32(col)) * P::KLD + hh * 8;
-#pragma unroll
-      for (int c = 0; c < P::NCH; ++c) {
-        const Op ka = *reinterpret_cast<const Op*>(krow + c * 16);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) sc[kb2][cb] = Mma32::run(ka, qop[cb][c], sc[kb2][cb]);
-      }
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+    return fmaxf(mx, __shfl_xor(mx, 32));
+  };
+  // the first K stages and V stage; the next loads' addresses
+  auto prologue = [&](bool with_v) {
+    kmeta(0);
+    kmeta_use();
+    kload();
+    if (with_v) {
+      vmeta(0);
+      vmeta_use();
+      vload();
     }
-
-    // causal mask (masked steps only), online softmax per column (scores kept
-    // raw: the base-2 scale is folded into the exponent's FMA), probabilities
-    // -> bf16 B operands
-    Op pb[2][2][NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          if constexpr (MASKED) {
-            const int key = kb + kb2 * 32 + key32(8 * (v >> 2) + 4 * hh + (v & 3));
-            if (key > lim[cb]) sc[kb2][cb][v] = -INFINITY;
-          }
-          mx = fmaxf(mx, sc[kb2][cb][v]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-      if (__any(mx > m_run[cb] + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run[cb], mx);
-        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_run[cb] - m_new);
-        l_run[cb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < P::NDB; ++db) o[db][cb] *= alpha;
-        m_run[cb] = m_new;
-      }
-      const float nbase = m_run[cb] == -INFINITY ? 0.0f : -m_run[cb];
-      float psum = 0.0f;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = fast_exp2(fmaf(sc[kb2][cb][8 * m + e], a.scale_log2, nbase));
-            psum += p[e];
-          }
-          pb[kb2][m][cb] = Mma<bf16>::pack(p);
-        }
-      l_run[cb] += psum;
-    }
-
-    // O^T += V^T P^T
-    const bf16* vs = st + P::KSTEP * P::KLD;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int db = 0; db < P::NDB; ++db) {
-          const Op va = *reinterpret_cast<const Op*>(vs + (db * 32 + col) * P::VLD + kb2 * 32 +
-                                                     16 * m + 8 * hh);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) o[db][cb] = Mma32::run(va, pb[kb2][m][cb], o[db][cb]);
-        }
-
-    if (j + 1 < nsteps) store_any(kb + P::KSTEP, stage0 + ((j + 1) & 1) * P::STAGE);
+    kstore(0);
+    if (with_v) vstore(0);
+    kmeta(P::KSTEP);
+    kmeta_use();
+    kload();
+    kstore(1);
+    kmeta(2 * P::KSTEP);
+    if (with_v) vmeta(P::KSTEP);
     __syncthreads();
   };
+  const int jfull = min(nsteps, kfull / P::KSTEP);  // steps below every row's diagonal
 
-  // the leading steps lie below every row's causal limit: no mask there
-  const int jfull = min(nsteps, kfull / P::KSTEP);
-  for (int j = 0; j < jfull; ++j) step(j, std::false_type{});
-  for (int j = jfull; j < nsteps; ++j) step(j, std::true_type{});
-
+  // Exact column max over all visible keys (only for the rare second pass).
+  auto row_max = [&]() {
+    float mx = -INFINITY;
+    if (nsteps <= 0) return mx;
+    prologue(false);
+    const Acc zero = Acc{};
+    for (int j = 0; j < nsteps; ++j) {
+      kmeta_use();
+      kmeta((j + 3) * P::KSTEP);
+      kload();
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const float l_tot = l_run[cb] + __shfl_xor(l_run[cb], 32);
-    if (lim[cb] < 0) continue;
+      for (int h = 0; h < 2; ++h) {
+        Acc sc = qk_block(j, h, zero);
+        if (j >= jfull) mask_block(sc, j * P::KSTEP + h * 32);
+        mx = fmaxf(mx, col_max(sc));
+      }
+      kstore(j + 2);
+      __syncthreads();
+    }
+    return mx;
+  };
+
+  // One pass of the tile.  The softmax reference m is fixed for the whole
+  // pass: the exact column max of the first block (pass 1) or of all keys
+  // (pass 2, m_given).  Scores arrive from the MFMAs as s*log2(e)/sqrt(d) - m,
+  // so p = 2^score with no per-step max, compare or rescale.  Any m gives the
+  // same normalised result; pass 1 only fails when a later score exceeds m
+  // by so much that some block's probability sum passes kPBig (or o or l
+  // stop being finite), and then the tile is redone as pass 2, whose
+  // probabilities are all <= 1.  Returns false (nothing written) on failure.
+  auto attend = [&](bool exact, float m_given) {
+    Acc o[P::NDB];
+#pragma unroll
+    for (int db = 0; db < P::NDB; ++db) o[db] = Acc{};
+    float l_run = 0.0f;
+    bool bad = false;
+    const vec<bf16, 2> ones = {(bf16)1.0f, (bf16)1.0f};
+    Op pb[2];
+    // probabilities of one block -> two bf16 B operands; the running sum adds
+    // those bf16 values (the ones the PV product uses)
+    auto softmax_block = [&](const Acc& sc) {
+      float ls = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sc[8 * m + e]);
+        pb[m] = Mma<bf16>::pack(pv);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const vec<bf16, 2> pp = {pb[m][e], pb[m][e + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
+        }
+      }
+      bad |= !(ls <= kPBig);
+      l_run += ls;
+    };
+    // O^T += V^T P^T for block h of V stage `step`: two 16-key groups, the
+    // second group's operands read as the first group's multiply issue
+    auto pv_block = [&](int step, int h) {
+      const bf16* vb =
+          lds + P::V_OFF + (step % P::NVB) * P::VBUF + col * P::VLD + h * 32 + 8 * hh;
+      Op va[P::NDB];
+#pragma unroll
+      for (int db = 0; db < P::NDB; ++db)
+        va[db] = *reinterpret_cast<const Op*>(vb + db * 32 * P::VLD);
+#pragma unroll
+      for (int db = 0; db < P::NDB; ++db) {
+        o[db] = Mma32::run(va[db], pb[0], o[db]);
+        va[db] = *reinterpret_cast<const Op*>(vb + db * 32 * P::VLD + 16);
+      }
+#pragma unroll
+      for (int db = 0; db < P::NDB; ++db) o[db] = Mma32::run(va[db], pb[1], o[db]);
+    };
+
+    Acc negm;
+    Acc s_next;
+    if (nsteps > 0) {
+      prologue(true);
+      float m;
+      if (exact) {
+        m = m_given == -INFINITY ? 0.0f : m_given;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) negm[v] = -m;
+        s_next = qk_block(0, 0, negm);
+      } else {
+        s_next = qk_block(0, 0, Acc{});
+        Acc t = s_next;
+        if (jfull == 0) mask_block(t, 0);
+        const float mx = col_max(t);
+        m = mx == -INFINITY ? 0.0f : mx;  // a column with no visible key keeps 0
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          negm[v] = -m;
+          s_next[v] -= m;
+        }
+      }
+    }
+
+    // step j: blocks (j, 0) and (j, 1); the score MFMAs of the next block run
+    // while a block is exponentiated, the PV MFMAs of a block while the next
+    // data is staged.  Stages K j+2 and V j+1.
+    auto step = [&](int j, auto mask_tag) {
+      constexpr bool MASKED = decltype(mask_tag)::value;
+      const int kb = j * P::KSTEP;
+      kmeta_use();
+      vmeta_use();
+      kmeta(kb + 3 * P::KSTEP);
+      vmeta(kb + 2 * P::KSTEP);
+      kload();  // K step j+2 (past the end: valid slots, never used)
+      vload();  // V step j+1
+      // keep the loads at the top of the step: they have the whole step to land
+      __builtin_amdgcn_sched_barrier(0);
+
+      Acc s_cur = s_next;
+      if constexpr (MASKED) mask_block(s_cur, kb);
+      s_next = qk_block(j, 1, negm);
+      softmax_block(s_cur);
+      pv_block(j, 0);
+
+      s_cur = s_next;
+      if constexpr (MASKED) mask_block(s_cur, kb + 32);
+      s_next = qk_block(j + 1, 0, negm);
+      softmax_block(s_cur);
+      pv_block(j, 1);
+
+      kstore(j + 2);
+      vstore(j + 1);
+      // Instruction order for the step (the wave issues in order, so a
+      // dependent MFMA chain would otherwise hold back the vector work
+      // behind it): each score MFMA of the next block is followed by a slice
+      // of the current block's softmax, each PV MFMA by a slice of the
+      // staging work.
+      sched_interleave();
+      __syncthreads();
+    };
+    for (int j = 0; j < jfull; ++j) step(j, std::false_type{});
+    for (int j = jfull; j < nsteps; ++j) step(j, std::true_type{});
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    bad |= !(l_tot < INFINITY);
+#pragma unroll
+    for (int db = 0; db < P::NDB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) bad |= !(fabsf(o[db][v]) < INFINITY);
+    if (!exact && __syncthreads_or(bad && valid)) return false;
+    if (!valid) return true;
     const float inv = 1.0f / l_tot;
-    bf16* out = (bf16*)a.out + (((size_t)q0 + tok_of[cb]) * a.hq + g * G + head_of[cb]) * D;
+    bf16* out = (bf16*)a.out + (((size_t)q0 + tok) * a.hq + g * G + head) * D;
 #pragma unroll
     for (int db = 0; db < P::NDB; ++db)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         vec<bf16, 4> w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[db][cb][4 * v4 + i] * inv);
+        for (int i = 0; i < 4; ++i) w[i] = (bf16)(o[db][4 * v4 + i] * inv);
         *reinterpret_cast<vec<bf16, 4>*>(out + db * 32 + 8 * v4 + 4 * hh) = w;
       }
+    return true;
+  };
+
+  if (!attend(false, 0.0f)) {
+    const float m = row_max();
+    attend(true, m);
   }
 }
 
@@ -1049,37 +1207,46 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
   const long long rs = l / a.nhg;
   const int r = (int)(rs % a.num_reqs);
   const int s = (int)(rs / a.num_reqs);
-  decode_item<T, D, kDecodeDepth>(a, r, hg, s, r, smem);
+  decode_item<T, D, kDecodeDepth, kWaves>(a, r, hg, s, r, smem);
 }
 
-// Column blocks (of 32 query rows) per wave in the bf16 prefill tile.
-constexpr int kPrefillNCB = 1;
+// Waves per workgroup of the mixed launch.  bf16: eight, so a prefill tile
+// holds 256 query rows and each staged (rotated) K step feeds twice the MFMA
+// work of a four-wave tile; a decode item then covers eight kv heads.  fp32
+// keeps four-wave workgroups.
+template <typename T>
+constexpr int mixed_waves() {
+  return sizeof(T) == 2 ? 8 : kWaves;
+}
 
 template <typename T, int D>
 constexpr int prefill_rows() {
-  return sizeof(T) == 2 ? Pf<D, kPrefillNCB>::ROWS : kPrefillRows;
+  return sizeof(T) == 2 ? Pf<D, mixed_waves<T>()>::ROWS : kPrefillRows;
 }
 
 template <typename T, int D>
 struct MixedSmem {
-  static constexpr int PB = sizeof(T) == 2 ? Pf<D, kPrefillNCB>::BYTES : PrefillSmem<T, D>::BYTES;
+  static constexpr int PB =
+      sizeof(T) == 2 ? Pf<D, mixed_waves<T>()>::BYTES : PrefillSmem<T, D>::BYTES;
   static constexpr int BYTES = PB > (int)sizeof(DecodeSmem<T, D>) ? PB : (int)sizeof(DecodeSmem<T, D>);
 };
 
 // Mixed launch over the planner's work list.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads, 2) mixed_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
+    mixed_kernel(AttnArgs a) {
+  constexpr int NW = mixed_waves<T>();
   __shared__ __attribute__((aligned(16))) unsigned char smem[MixedSmem<T, D>::BYTES];
   if ((int)blockIdx.x >= *a.nitems) return;
   const int4 it = a.items[blockIdx.x];
   if (it.x == kItemPrefill) {
     if constexpr (sizeof(T) == 2) {
-      prefill_tile_bf16<D, kPrefillNCB>(a, it.y, it.z, it.w, smem);
+      prefill_tile_bf16<D, NW>(a, it.y, it.z, it.w, smem);
     } else {
       prefill_tile<T, D>(a, it.y, it.z, it.w, smem);
     }
   } else {
-    decode_item<T, D, 1>(a, it.y, it.z, it.w, (long long)a.cu_q[it.y], smem);
+    decode_item<T, D, 1, NW>(a, it.y, it.z, it.w, (long long)a.cu_q[it.y], smem);
   }
 }
 
@@ -1240,10 +1407,11 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
   const int len_cap = (int)min((long long)h.max_seq_len,
                               (long long)h.block_table_stride * kBlockSize);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, h.cu_seqlens_q, h.seq_lens,
-                     h.num_reqs, h.hkv, h.hq / h.hkv, w.nhg, Cfg<T, D>::KSTEP,
-                     prefill_rows<T, D>(), len_cap,
+                     h.num_reqs, h.hkv, h.hq / h.hkv, cdiv(h.hkv, mixed_waves<T>()),
+                     Cfg<T, D>::KSTEP, prefill_rows<T, D>(), len_cap,
                      w.max_items, (int4*)(ws + w.items_off), (int*)(ws + w.count_off));
-  hipLaunchKernelGGL((mixed_kernel<T, D>), dim3((unsigned)w.max_items), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((mixed_kernel<T, D>), dim3((unsigned)w.max_items),
+                     dim3(64 * mixed_waves<T>()), 0, s, a);
   launch_combine<T, D>(a, s);
   return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }

@@ -47,7 +47,7 @@ struct WorkspaceLayout {
   size_t o_off;         // float[num_reqs * hkv * s_max * group * head_dim]: chunk outputs
   size_t total;
   int s_max;            // chunks per request, upper bound
-  int nhg;              // kv-head groups of kWaves heads
+  int nhg;              // kv-head groups of kWaves heads (an upper bound for wider groups)
   long long max_items;  // work-list capacity
 };
 

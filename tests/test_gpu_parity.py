@@ -147,6 +147,93 @@ def test_small_parity(case):
     assert err <= TOL[w.dtype]
 
 
+def _first_block_gap_log2(w):
+    """Per request, the largest (over query rows and q heads) amount, in
+    log2 units, by which a visible score beyond key slot 31 exceeds the
+    maximum over the row's visible slots 0..31 (fp64, from the oracle's
+    rotation)."""
+    kp, vp = oracle_pools(w)
+    G = w.hq // w.hkv
+    ql = w.q_lens()
+    q0 = np.concatenate([[0], np.cumsum(ql)[:-1]])
+    q = oracle.bf16_bits_to_f64(w.q)
+    gaps = []
+    for r in range(w.num_reqs):
+        L = int(w.seq_lens[r])
+        kt, _ = oracle.gather_request(kp, vp, w.block_table[r], L, w.block_size)
+        kpos = w.k_pos[w.cu_seqlens_k[r]:w.cu_seqlens_k[r] + L]
+        krot = oracle.rotate_half(oracle.bf16_bits_to_f64(kt), kpos[:, None], w.d, w.base)
+        rows = slice(int(q0[r]), int(q0[r] + ql[r]))
+        qrot = oracle.rotate_half(q[rows], w.q_pos[rows][:, None], w.d, w.base)
+        gap = -np.inf
+        for h in range(w.hq):
+            s = qrot[:, h, :] @ krot[:, h // G, :].T / np.sqrt(w.d) * np.log2(np.e)
+            lim = L - int(ql[r]) + np.arange(int(ql[r]))
+            vis = np.arange(L)[None, :] <= lim[:, None]
+            s = np.where(vis, s, -np.inf)
+            gap = max(gap, float(np.max(s[:, 32:].max(axis=1) - s[:, :32].max(axis=1))))
+        gaps.append(gap)
+    return np.asarray(gaps)
+
+
+@pytest.mark.parametrize("factor,min_gap", [(10.0, 40.0), (60.0, 200.0)])
+def test_prefill_outlier_key_takes_exact_pass(factor, min_gap):
+    """The first suffix key of each request scaled up: some rows then score
+    that key far above everything in their first 32 slots (factor 10: ~43
+    log2 units, past the 2^32 per-block probability bound; factor 60: ~270,
+    an overflow), so the tile's single-pass softmax (reference = the first
+    block's max) fails and the tile is recomputed with the exact row maximum.
+    The result must still match the oracle.  Unscaled, the gaps are ~4-5."""
+    from workloads.synth import f32_to_bf16_bits
+    w = make_workload("outlier", **dict(SMALL["prefill"]))
+    first = np.concatenate([[0], np.cumsum(w.q_lens())[:-1]])
+    nk = w.new_k.copy()
+    f = (nk[first].astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+    nk[first] = f32_to_bf16_bits(f)
+    w.new_k = nk
+    gaps = _first_block_gap_log2(w)
+    assert (gaps > min_gap).all(), gaps  # every request exercises the second pass
+    got = run_workload(w)
+    assert np.isfinite(got).all()
+    # With keys this large, rounding the rotated operands to bfloat16 (the
+    # kernel's documented precision) moves the big logits by O(0.1), so the
+    # reference is the oracle's attention over those rounded operands: keys
+    # and queries rotated by the oracle, rounded to bfloat16 (queries after
+    # the log2(e)/sqrt(d) pre-scale the kernel applies, then scaled back
+    # exactly), and passed at position 0, where the rotation is the identity.
+    ref = _oracle_on_rounded_operands(w)
+    err = _maxerr(got, ref)
+    exact = _maxerr(got, oracle_outputs(w))
+    print(f"outlier x{factor}: gaps {np.round(gaps, 1)}, max abs err {err:.3e} "
+          f"(vs the unrounded oracle {exact:.3e})")
+    assert err <= TOL[w.dtype]
+
+
+def _oracle_on_rounded_operands(w):
+    from workloads.synth import f32_to_bf16_bits
+
+    def bf(x):
+        return oracle.bf16_bits_to_f64(f32_to_bf16_bits(np.asarray(x, np.float32)))
+
+    kp, vp = oracle_pools(w)
+    ql = w.q_lens()
+    q0 = np.concatenate([[0], np.cumsum(ql)[:-1]])
+    q = oracle.bf16_bits_to_f64(w.q)
+    c = np.log2(np.e) / np.sqrt(w.d)
+    out = np.zeros((w.total_q, w.hq, w.d))
+    for r in range(w.num_reqs):
+        L = int(w.seq_lens[r])
+        kt, vt = oracle.gather_request(kp, vp, w.block_table[r], L, w.block_size)
+        kpos = w.k_pos[w.cu_seqlens_k[r]:w.cu_seqlens_k[r] + L]
+        krot = bf(oracle.rotate_half(oracle.bf16_bits_to_f64(kt), kpos[:, None], w.d, w.base))
+        rows = slice(int(q0[r]), int(q0[r] + ql[r]))
+        qrot = bf(oracle.rotate_half(q[rows], w.q_pos[rows][:, None], w.d, w.base) * c) / c
+        out[rows] = oracle.attention_request(qrot, np.zeros(int(ql[r]), np.int64), krot,
+                                             oracle.bf16_bits_to_f64(vt), np.zeros(L, np.int64),
+                                             int(ql[r]), w.base, w.hkv)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # full-size configs, sampled outputs
 # ---------------------------------------------------------------------------
