@@ -1250,11 +1250,29 @@ __global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
   }
 }
 
+// Dispatch position of item i of one list when the prefill list (P items)
+// and the decode list (D items) are merged evenly: item i of a list of n
+// sits at virtual time (2i+1)/(2n), prefill first on ties.  Spreading the
+// HBM-bound decode chunks among the MFMA-bound prefill tiles keeps both
+// kinds of work running side by side on different compute units.
+__device__ __forceinline__ long long merge_pos(long long i, long long P, long long D, bool prefill) {
+  if (prefill) {
+    // decode items k with (2k+1) P < (2i+1) D
+    const long long num = (2 * i + 1) * D - P;
+    const long long c = num <= 0 ? 0 : min(D, (num + 2 * P - 1) / (2 * P));
+    return i + c;
+  }
+  // prefill items j with (2j+1) D <= (2i+1) P
+  const long long num = (2 * i + 1) * P - D;
+  const long long e = num < 0 ? 0 : min(P, num / (2 * D) + 1);
+  return i + e;
+}
+
 // Planner: one workgroup of 1024 threads turns (cu_seqlens_q, seq_lens) into
-// the work list.  Prefill tiles first (per request and kv head, last tile
-// first: the later query rows see more keys), then the chunks of q_len == 1
-// requests (per chunk, the kv-head groups); each item is written at its XCD
-// dispatch position.
+// the work list: the prefill tiles (per request and kv head, last tile first:
+// the later query rows see more keys) merged evenly with the chunks of
+// q_len == 1 requests (per chunk, the kv-head groups); each item is written
+// at its XCD dispatch position.
 __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ cu_q,
                                                     const int32_t* __restrict__ seq_lens,
                                                     int num_reqs, int hkv, int group, int nhg,
@@ -1284,7 +1302,8 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
     __syncthreads();
   }
   const long long total_pf = s_a[0];
-  const long long total = s_a[0] + s_b[0];
+  const long long total_dc = s_b[0];
+  const long long total = total_pf + total_dc;
   __syncthreads();
   // More items than the workspace was sized for means the metadata broke a
   // precondition (total_q or max_seq_len too small): run nothing.
@@ -1321,19 +1340,19 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
       __syncthreads();
     }
     const long long off_pf = s_tot[0] + s_a[tid] - npf;
-    const long long off_dc = total_pf + s_tot[1] + s_b[tid] - ndc;
+    const long long off_dc = s_tot[1] + s_b[tid] - ndc;
     if (ql > 1) {
       const int tiles = cdiv(ql * group, rows);
       for (int g = 0; g < hkv; ++g)
         for (int k = 0; k < tiles; ++k) {
-          const long long l = off_pf + (long long)g * tiles + k;
+          const long long l = merge_pos(off_pf + (long long)g * tiles + k, total_pf, total_dc, true);
           items[xcd_position(l, total)] = make_int4(kItemPrefill, r, g, tiles - 1 - k);
         }
     } else if (ql == 1) {
       const int S = num_splits(L, kstep);
       for (int s = 0; s < S; ++s)
         for (int hg = 0; hg < nhg; ++hg) {
-          const long long l = off_dc + (long long)s * nhg + hg;
+          const long long l = merge_pos(off_dc + (long long)s * nhg + hg, total_pf, total_dc, false);
           items[xcd_position(l, total)] = make_int4(kItemDecode, r, hg, s);
         }
     }
