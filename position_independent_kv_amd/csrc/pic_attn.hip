@@ -1177,10 +1177,11 @@ __device__ __forceinline__ long long xcd_logical(long long b, long long n) {
   const long long x = b % 8, k = b / 8;
   return x * q + min(x, rem) + k;
 }
-// Inverse of xcd_logical: dispatch position of logical item l.
-__device__ __forceinline__ long long xcd_position(long long l, long long n) {
-  const long long q = n / 8, rem = n % 8;
-  long long x, k;
+// Inverse of xcd_logical: dispatch position of logical item l (l < n < 2^31,
+// so 32-bit arithmetic).
+__device__ __forceinline__ unsigned xcd_position(unsigned l, unsigned n) {
+  const unsigned q = n / 8, rem = n % 8;
+  unsigned x, k;
   if (l < rem * (q + 1)) {
     x = l / (q + 1);
     k = l % (q + 1);
@@ -1282,8 +1283,12 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
                                                     int* __restrict__ count) {
   __shared__ long long s_a[1024];
   __shared__ long long s_b[1024];
+  __shared__ long long s_off[1024];
+  __shared__ int s_cnt[1024];
+  __shared__ unsigned char s_kind[1024];
   __shared__ long long s_tot[2];
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   // pass 1: totals
   long long pf = 0, dc = 0;
   for (int r = tid; r < num_reqs; r += 1024) {
@@ -1316,7 +1321,9 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
     s_tot[0] = 0;
     s_tot[1] = 0;
   }
-  // pass 2: exclusive scans per chunk of 1024 requests, then emit
+  // pass 2: exclusive scans per chunk of 1024 requests, then emit: the waves
+  // take the chunk's requests in turn and their lanes split each request's
+  // items
   for (int base = 0; base < num_reqs; base += 1024) {
     const int r = base + tid;
     int ql = 0, L = 0;
@@ -1339,22 +1346,32 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
       s_b[tid] += xb;
       __syncthreads();
     }
-    const long long off_pf = s_tot[0] + s_a[tid] - npf;
-    const long long off_dc = s_tot[1] + s_b[tid] - ndc;
-    if (ql > 1) {
-      const int tiles = cdiv(ql * group, rows);
-      for (int g = 0; g < hkv; ++g)
-        for (int k = 0; k < tiles; ++k) {
-          const long long l = merge_pos(off_pf + (long long)g * tiles + k, total_pf, total_dc, true);
-          items[xcd_position(l, total)] = make_int4(kItemPrefill, r, g, tiles - 1 - k);
+    // per request: kind, item count per kv head (tiles) or per chunk row
+    // (chunks), first item index in its list
+    s_kind[tid] = ql > 1 ? 1 : (ql == 1 ? 2 : 0);
+    s_cnt[tid] = ql > 1 ? cdiv(ql * group, rows) : (ql == 1 ? num_splits(L, kstep) : 0);
+    s_off[tid] = ql > 1 ? s_tot[0] + s_a[tid] - npf : s_tot[1] + s_b[tid] - ndc;
+    __syncthreads();
+    const int nr = min(1024, num_reqs - base);
+    for (int rr = wave; rr < nr; rr += 16) {
+      const int kind = s_kind[rr];
+      const int cnt = s_cnt[rr];
+      const long long off = s_off[rr];
+      if (kind == 1) {  // prefill tiles, per kv head last tile first
+        for (int it = lane; it < hkv * cnt; it += 64) {
+          const int g = it / cnt, k = it % cnt;
+          const long long l = merge_pos(off + it, total_pf, total_dc, true);
+          items[xcd_position((unsigned)l, (unsigned)total)] =
+              make_int4(kItemPrefill, base + rr, g, cnt - 1 - k);
         }
-    } else if (ql == 1) {
-      const int S = num_splits(L, kstep);
-      for (int s = 0; s < S; ++s)
-        for (int hg = 0; hg < nhg; ++hg) {
-          const long long l = merge_pos(off_dc + (long long)s * nhg + hg, total_pf, total_dc, false);
-          items[xcd_position(l, total)] = make_int4(kItemDecode, r, hg, s);
+      } else if (kind == 2) {  // decode chunks, per chunk the kv-head groups
+        for (int it = lane; it < cnt * nhg; it += 64) {
+          const int sc = it / nhg, hg = it % nhg;
+          const long long l = merge_pos(off + it, total_pf, total_dc, false);
+          items[xcd_position((unsigned)l, (unsigned)total)] =
+              make_int4(kItemDecode, base + rr, hg, sc);
         }
+      }
     }
     __syncthreads();
     if (tid == 1023) {
