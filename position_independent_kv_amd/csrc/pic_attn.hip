@@ -891,8 +891,10 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
     for (int u = 0; u < P::NVR; ++u) vmeta_blk[u] = vmeta_blk_nx[u];
   };
   auto kload = [&]() {
-    const unsigned blk = (unsigned)clampi(kmeta_blk, 0, nb_max);
-    const unsigned pos = (unsigned)clampi(kmeta_pos, 0, pmax);
+    // an out-of-range id (negative ones wrap to large unsigned values) is
+    // clamped to the last valid one
+    const unsigned blk = min((unsigned)kmeta_blk, (unsigned)nb_max);
+    const unsigned pos = min((unsigned)kmeta_pos, (unsigned)pmax);
     const char* src = kthr + (size_t)blk * blk_bytes;
     klo = *reinterpret_cast<const KV*>(src);
     khi = *reinterpret_cast<const KV*>(src + D);  // + D/2 elements
@@ -902,7 +904,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
   auto vload = [&]() {
 #pragma unroll
     for (int u = 0; u < P::NVR; ++u) {
-      const unsigned vb = (unsigned)clampi(vmeta_blk[u], 0, nb_max);
+      const unsigned vb = min((unsigned)vmeta_blk[u], (unsigned)nb_max);
       vr[u] = *reinterpret_cast<const VRun*>(vthr + (size_t)vb * blk_bytes);
     }
   };
@@ -921,19 +923,19 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
   auto vstore = [&](int step) {  // the loaded V^T runs into V stage `step`
     const int kb = step * P::KSTEP;
     bf16* vdst = lds + P::V_OFF + (step % P::NVB) * P::VBUF + vd * P::VLD + vk0;
-    if (kb + P::KSTEP > L) {  // slots at or beyond L hold no data
+#pragma unroll
+    for (int u = 0; u < P::NVR; ++u) *reinterpret_cast<VRun*>(vdst + u * P::VR) = vr[u];
+    // Slots at or beyond L hold no data: overwrite them with zeros (only the
+    // last step has any).  Done as separate LDS stores after the plain ones
+    // so that the steady-state steps carry no per-element selects.
+    if (kb + P::KSTEP > L) {
 #pragma unroll
       for (int u = 0; u < P::NVR; ++u) {
-        VRun x = vr[u];
         const int key0 = kb + vk0 + u * P::VR;
 #pragma unroll
         for (int e = 0; e < P::VR; ++e)
-          if (key0 + e >= L) x[e] = (bf16)0.0f;
-        *reinterpret_cast<VRun*>(vdst + u * P::VR) = x;
+          if (key0 + e >= L) vdst[u * P::VR + e] = (bf16)0.0f;
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < P::NVR; ++u) *reinterpret_cast<VRun*>(vdst + u * P::VR) = vr[u];
     }
   };
 
