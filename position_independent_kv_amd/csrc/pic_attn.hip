@@ -361,31 +361,42 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   };
   Group grpbuf[NB];
 
-  // issue every load of step j (relative to k0) into a register group
-  auto issue = [&](int j, Group& gb) {
+  // Loads of step j (relative to k0) into a register group, in three parts
+  // so that each part is issued as soon as the previous step has consumed
+  // that part of the group: the table values right after they are copied to
+  // LDS, the K rows after the score MFMAs, the V runs after the PV MFMAs.
+  auto issue_tab = [&](int j, Group& gb) {
+    const size_t row = (size_t)sm.pos[j * C::KSTEP + skey] * (D / 2) + spart;
+    gb.c = RF::load(a.cos_tab + row);
+    gb.sn = RF::load(a.sin_tab + row);
+  };
+  auto issue_k = [&](int j, Group& gb) {
     const int kb = j * C::KSTEP;  // offset in the chunk
-    const int b0 = sm.blk[kb >> 4];
-    const int b1 = sm.blk[min((kb >> 4) + 1, nsteps * C::KSTEP / kBlockSize - 1)];
+    const int blk = sm.blk[min((kb >> 4) + kblk_sel, nsteps * C::KSTEP / kBlockSize - 1)];
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
       const int kk = key_of<C::NT>(t, row16);
-      const int blk = (kblk_sel ? b1 : b0);
       const T* krow = kpool + (size_t)blk * blk_stride + head_k +
                       (size_t)((kb + kk) & 15) * D + grp * C::KPL;
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) gb.k[t][c] = M::load(krow + c * C::KCH);
     }
+  };
+  auto issue_v = [&](int j, Group& gb) {
+    const int kb = j * C::KSTEP;
+    const int blk = sm.blk[min((kb >> 4) + vblk_sel, nsteps * C::KSTEP / kBlockSize - 1)];
 #pragma unroll
     for (int mi = 0; mi < C::NPV; ++mi) {
-      const int blk = (vblk_sel ? b1 : b0);
       const T* vrow = vpool + (size_t)blk * blk_stride + head_v + (size_t)row16 * kBlockSize +
                       ((vkey_off + mi * C::KPL) & 15);
 #pragma unroll
       for (int dt = 0; dt < C::ND; ++dt) gb.v[mi][dt] = M::load(vrow + (size_t)dt * 16 * kBlockSize);
     }
-    const size_t row = (size_t)sm.pos[kb + skey] * (D / 2) + spart;
-    gb.c = RF::load(a.cos_tab + row);
-    gb.sn = RF::load(a.sin_tab + row);
+  };
+  auto issue = [&](int j, Group& gb) {
+    issue_k(j, gb);
+    issue_v(j, gb);
+    issue_tab(j, gb);
   };
 
   f32x4 acc[C::ND];
@@ -403,6 +414,7 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     const int kb = k0 + j * C::KSTEP;  // absolute key index
     RF::store(&sm.cs[buf][skey][spart], gb.c);
     RF::store(&sm.sn[buf][skey][spart], gb.sn);
+    if (j + NB < nsteps) issue_tab(j + NB, gb);
     __syncthreads();
     f32x4 sc[C::NT];
 #pragma unroll
@@ -414,6 +426,7 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) sc[t] = M::run(gb.k[t][c], qop[c], sc[t]);
     }
+    if (j + NB < nsteps) issue_k(j + NB, gb);
 #pragma unroll
     for (int t = 0; t < C::NT; ++t)
 #pragma unroll
@@ -442,7 +455,7 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
 #pragma unroll
       for (int dt = 0; dt < C::ND; ++dt) acc[dt] = M::run(gb.v[mi][dt], p, acc[dt]);
     }
-    if (j + NB < nsteps) issue(j + NB, gb);
+    if (j + NB < nsteps) issue_v(j + NB, gb);
   };
 
   for (int j0 = 0; j0 < nsteps; j0 += NB) {
