@@ -117,6 +117,50 @@ def time_config(name, steps, warmup, with_rows=False):
     return res
 
 
+def rope_ablation(name, reps=20):
+    """In-kernel rotation cost: position-free attention vs the same kernels over a
+    conventional cache of pre-rotated keys (key rotation compiled out).
+
+    Both calls read the same logical bytes and do the same matrix products; the
+    rotated cache holds one private copy of every block per request (a shared span
+    cannot be pre-rotated for two offsets).  Calls alternate, timed with HIP events
+    on the launch stream.
+    """
+    import torch
+
+    from tests.gpu_harness import DeviceWorkload
+    from workloads import make_workload
+
+    w = make_workload(name)
+    dw = DeviceWorkload(w)
+    dw.write_new_tokens()
+    dw.build_rotated_cache()
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dw.attention()
+        dw.attention_rotated()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for k in range(reps):
+        ev[k][0].record(stream)
+        dw.attention()
+        ev[k][1].record(stream)
+        dw.attention_rotated()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    pf = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    rot = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    res = {"workload": WORKLOAD_TEXT[name], "position_free_ms": pf, "rotated_cache_ms": rot,
+           "rotation_overhead_frac": pf / rot - 1.0,
+           "position_free_pool_blocks": int(w.num_blocks),
+           "rotated_cache_pool_blocks": int(dw.rot_k_pool.shape[0])}
+    log(f"[bench] rope ablation {name}: position-free {pf * 1e3:.1f} us, rotated cache "
+        f"{rot * 1e3:.1f} us ({res['rotation_overhead_frac'] * 100:+.1f} %)")
+    del dw
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, counts, budget_s=12.0):
     """The fp64 oracle on the host: a bounded sample of the same step."""
     import oracle
@@ -179,6 +223,8 @@ def main():
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--others", default="c2p,c3,c4,c5",
                     help="comma list of further configs reported under 'configs' ('' for none)")
+    ap.add_argument("--ablation", default="c2p,c3,c4",
+                    help="configs on which to time the in-kernel rotation ablation ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a plain copy of this many bytes (PMC scaling run)")
@@ -243,6 +289,10 @@ def main():
         log(f"[bench] {name}: kernel {r['kernel_ms'] * 1e3:.1f} us, "
             f"{others[name]['kernel_GBps']:.0f} GB/s, {others[name]['kernel_TFLOPs']:.1f} TFLOP/s")
 
+    ablation = {}
+    for name in [x for x in args.ablation.split(",") if x]:
+        ablation[name] = rope_ablation(name)
+
     cpu = None
     if not args.no_cpu_baseline:
         t = time.time()
@@ -273,6 +323,7 @@ def main():
                  "cache_write_ms": main_res["cache_write_ms"],
                  "attention_kernel_ms": main_res["kernel_ms"]},
         "configs": others,
+        "rope_ablation": ablation,
         "source_hash": source_hash(),
     }
     print(json.dumps(out), flush=True)

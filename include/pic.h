@@ -111,10 +111,11 @@ int pic_cache_write(const void* k, const void* v, const int32_t* slot_mapping, i
 /*
  * pic_attn_workspace_size -- bytes of device workspace that pic_attn_decode /
  * pic_attn_prefill need for these bounds (total_q = number of query rows,
- * max_seq_len >= every seq_len).  The workspace must be zero-filled once
- * after allocation; every call leaves its split-combine counters at zero
- * again, so the same workspace can be reused by later calls on the same
- * stream.  Calls that overlap in time must use different workspaces.
+ * max_seq_len >= every seq_len).  It holds the work list of the mixed
+ * launch and the per-chunk partial results of split requests; every call
+ * writes what it reads, so it needs no initialisation and can be reused by
+ * later calls on the same stream.  Calls that overlap in time must use
+ * different workspaces.
  * Returns 0 for unsupported arguments.
  */
 size_t pic_attn_workspace_size(int num_reqs, int total_q, int max_seq_len, int num_q_heads,
@@ -129,8 +130,8 @@ size_t pic_attn_workspace_size(int num_reqs, int total_q, int max_seq_len, int n
  * block_table[r * block_table_stride + j / block_size] at offset
  * j % block_size.  Long contexts are split into chunks whose count depends
  * only on seq_len (so a request's result does not depend on the rest of the
- * batch); the last chunk of a request to finish merges the partial results
- * inside the same kernel.
+ * batch); a second small kernel on the same stream merges the chunks'
+ * partial results.
  *   q        [num_reqs][Hq][head_dim] unrotated, dtype
  *   q_pos    int32 [num_reqs]
  *   out      [num_reqs][Hq][head_dim], dtype (written)
@@ -166,6 +167,57 @@ int pic_attn_prefill(const void* q, const int32_t* cu_seqlens_q, const int32_t* 
                      int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                      int block_size, int num_blocks, int max_seq_len, int dtype, void* out,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * In-kernel-rotation ablation: the conventional RoPE cache that the
+ * position-free design replaces, and the same attention kernels with the key
+ * rotation compiled out.  MiniPIC §2.1 (Implementation) moves the rotation of
+ * keys from the cache write into the attention kernel at the price of a
+ * table lookup and a few fused multiply-adds per key element; the page puts
+ * that price at 5.7 % of end-to-end time (§4).  These entry points measure
+ * it at kernel level on MI355X: same shapes, same kernels, keys pre-rotated.
+ *
+ * pic_cache_write_rotated -- like pic_cache_write, but each key is rotated
+ * to positions[t] (int32 [num_tokens], device) before it is stored:
+ *   k_pool slot = round(R_p k~)  (rotate-half, fp32 arithmetic with the
+ *   table's float32 cos/sin, rounded to dtype);  V is copied unchanged.
+ * A block written this way is valid at that one offset only (it cannot be
+ * shared at another offset, which is the point of the comparison).
+ * cos_tab/sin_tab: float32 [max_pos][head_dim/2] from pic_rope_table;
+ * positions are clamped into [0, max_pos).  Errors as pic_cache_write, plus
+ * PIC_EINVAL for null positions/tables or max_pos <= 0.
+ */
+int pic_cache_write_rotated(const void* k, const void* v, const int32_t* slot_mapping,
+                            const int32_t* positions, const float* cos_tab,
+                            const float* sin_tab, int max_pos, int num_tokens,
+                            int num_kv_heads, int head_dim, int dtype, void* k_pool,
+                            void* v_pool, int num_blocks, int block_size, void* stream);
+
+/*
+ * pic_attn_decode_rotated / pic_attn_prefill_rotated -- pic_attn_decode /
+ * pic_attn_prefill for a k_pool that already holds every key rotated to the
+ * position at which this request uses it (for instance written by
+ * pic_cache_write_rotated).  The kernels are the position-free ones with the
+ * key-side table lookup and rotation removed; there is no cu_seqlens_k /
+ * k_pos argument.  The query is still rotated in the kernel by q_pos, with
+ * cos_tab/sin_tab.  All other arguments, layouts and the workspace are as in
+ * the position-free calls.  dtype must be PIC_BF16 (else PIC_EUNSUPPORTED).
+ */
+int pic_attn_decode_rotated(const void* q, const int32_t* q_pos, const void* k_pool,
+                            const void* v_pool, const int32_t* block_table,
+                            int block_table_stride, const int32_t* seq_lens,
+                            const float* cos_tab, const float* sin_tab, int max_pos,
+                            int num_reqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int block_size, int num_blocks, int max_seq_len, int dtype,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream);
+int pic_attn_prefill_rotated(const void* q, const int32_t* cu_seqlens_q, const int32_t* q_pos,
+                             const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, int block_table_stride,
+                             const int32_t* seq_lens, const float* cos_tab,
+                             const float* sin_tab, int max_pos, int num_reqs, int total_q,
+                             int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                             int block_size, int num_blocks, int max_seq_len, int dtype,
+                             void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pic_validate_metadata -- check the device-value preconditions above on

@@ -30,7 +30,8 @@ BLOCK_SIZE = 16
 EXPORTS = [
     "pic_status_string", "pic_version", "pic_rope_table", "pic_cache_write",
     "pic_attn_workspace_size", "pic_attn_decode", "pic_attn_prefill", "pic_validate_metadata",
-    "pic_decode_num_splits", "pic_decode_split_len",
+    "pic_decode_num_splits", "pic_decode_split_len", "pic_cache_write_rotated",
+    "pic_attn_decode_rotated", "pic_attn_prefill_rotated",
 ]
 
 
@@ -71,6 +72,12 @@ def _load():
                                      + [c_void, c_void, c_size, c_void])
     lib.pic_validate_metadata.argtypes = ([c_void] * 3 + [c_int] + [c_void] * 3 + [c_int] * 6
                                           + [ctypes.c_char_p, c_int])
+    lib.pic_cache_write_rotated.argtypes = ([c_void] * 6 + [c_int] * 5 + [c_void, c_void]
+                                            + [c_int, c_int, c_void])
+    lib.pic_attn_decode_rotated.argtypes = ([c_void] * 5 + [c_int] + [c_void] * 3 + [c_int] * 9
+                                            + [c_void, c_void, c_size, c_void])
+    lib.pic_attn_prefill_rotated.argtypes = ([c_void] * 6 + [c_int] + [c_void] * 3
+                                             + [c_int] * 11 + [c_void, c_void, c_size, c_void])
     lib.pic_decode_num_splits.argtypes = [c_int, c_int]
     lib.pic_decode_split_len.argtypes = [c_int, c_int]
     for name in EXPORTS:
@@ -178,6 +185,30 @@ def pic_cache_write(k, v, slot_mapping, k_pool, v_pool, stream=None):
                                    nb, bs, _stream(stream)), "pic_cache_write")
 
 
+def pic_cache_write_rotated(k, v, slot_mapping, positions, cos_tab, sin_tab, k_pool, v_pool,
+                            stream=None):
+    """Conventional RoPE-cache write (ablation baseline): store R_pos k and v at slot_mapping."""
+    torch = _torch()
+    if k.shape != v.shape or k.dim() != 3:
+        raise ValueError("k and v must both be [num_tokens][Hkv][head_dim]")
+    T, hkv, d = k.shape
+    nb, phkv, bs, pd = k_pool.shape
+    if (phkv, pd) != (hkv, d) or tuple(v_pool.shape) != (nb, hkv, d, bs):
+        raise ValueError("pool shapes must be k [nb][Hkv][B][d] and v [nb][Hkv][d][B]")
+    if k.dtype != k_pool.dtype or v.dtype != k.dtype or v_pool.dtype != k.dtype:
+        raise TypeError("k, v and the pools must share one dtype")
+    if slot_mapping.shape != (T,) or positions.shape != (T,):
+        raise ValueError("slot_mapping and positions must be [num_tokens]")
+    if cos_tab.shape != sin_tab.shape or cos_tab.dim() != 2 or 2 * cos_tab.shape[1] != d:
+        raise ValueError("cos_tab and sin_tab must both be [max_pos][head_dim/2]")
+    _check(_load().pic_cache_write_rotated(
+        _ptr(k, "k"), _ptr(v, "v"), _ptr(slot_mapping, "slot_mapping", torch.int32),
+        _ptr(positions, "positions", torch.int32), _ptr(cos_tab, "cos_tab", torch.float32),
+        _ptr(sin_tab, "sin_tab", torch.float32), cos_tab.shape[0], T, hkv, d, _dtype_code(k),
+        _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"), nb, bs, _stream(stream)),
+        "pic_cache_write_rotated")
+
+
 def pic_attn_workspace_size(num_reqs, total_q, max_seq_len, num_q_heads, num_kv_heads, head_dim,
                             dtype) -> int:
     code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
@@ -237,6 +268,51 @@ def pic_attn_prefill(q, cu_seqlens_q, q_pos, k_pool, v_pool, block_table, seq_le
         hq, hkv, d, bs, nb, int(max_seq_len), _dtype_code(q), _ptr(out, "out"),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)), "pic_attn_prefill")
+
+
+def pic_attn_decode_rotated(q, q_pos, k_pool, v_pool, block_table, seq_lens, cos_tab, sin_tab,
+                            max_seq_len, out, workspace, stream=None):
+    """pic_attn_decode over a cache of already rotated keys (no key positions)."""
+    torch = _torch()
+    i32 = torch.int32
+    R, hq, d = q.shape
+    nb, hkv, bs, pd = _pool_dims(k_pool, v_pool)
+    if pd != d or tuple(out.shape) != (R, hq, d) or out.dtype != q.dtype:
+        raise ValueError("q / out / pool head sizes disagree")
+    if block_table.dim() != 2 or block_table.shape[0] < R:
+        raise ValueError("block_table must be [R][stride]")
+    _check(_load().pic_attn_decode_rotated(
+        _ptr(q, "q"), _ptr(q_pos, "q_pos", i32), _ptr(k_pool, "k_pool", q.dtype),
+        _ptr(v_pool, "v_pool", q.dtype), _ptr(block_table, "block_table", i32),
+        block_table.shape[1], _ptr(seq_lens, "seq_lens", i32),
+        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
+        cos_tab.shape[0], R, hq, hkv, d, bs, nb, int(max_seq_len), _dtype_code(q),
+        _ptr(out, "out"), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "pic_attn_decode_rotated")
+
+
+def pic_attn_prefill_rotated(q, cu_seqlens_q, q_pos, k_pool, v_pool, block_table, seq_lens,
+                             cos_tab, sin_tab, max_q_len, max_seq_len, out, workspace,
+                             stream=None):
+    """pic_attn_prefill over a cache of already rotated keys (no key positions)."""
+    torch = _torch()
+    i32 = torch.int32
+    total_q, hq, d = q.shape
+    R = seq_lens.shape[0]
+    nb, hkv, bs, pd = _pool_dims(k_pool, v_pool)
+    if pd != d or tuple(out.shape) != (total_q, hq, d) or out.dtype != q.dtype:
+        raise ValueError("q / out / pool head sizes disagree")
+    if cu_seqlens_q.shape != (R + 1,) or block_table.dim() != 2:
+        raise ValueError("cu_seqlens_q must be [R+1] and block_table [R][stride]")
+    _check(_load().pic_attn_prefill_rotated(
+        _ptr(q, "q"), _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(q_pos, "q_pos", i32),
+        _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype),
+        _ptr(block_table, "block_table", i32), block_table.shape[1],
+        _ptr(seq_lens, "seq_lens", i32), _ptr(cos_tab, "cos_tab", torch.float32),
+        _ptr(sin_tab, "sin_tab", torch.float32), cos_tab.shape[0], R, total_q, int(max_q_len),
+        hq, hkv, d, bs, nb, int(max_seq_len), _dtype_code(q), _ptr(out, "out"),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "pic_attn_prefill_rotated")
 
 
 def pic_validate_metadata(cu_seqlens_q, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos,

@@ -286,7 +286,10 @@ struct DecodeSmem {
 // address lookup ever waits behind the data loads.  With one chunk the wave
 // writes the output row; otherwise it writes a normalised partial and
 // (max, sum) that combine_kernel merges.  Uniform across the workgroup.
-template <typename T, int D, int NB, int NW>
+// ROT = false compiles the key rotation out (the pool then holds keys
+// already rotated to this request's positions): no positions, no table rows,
+// no per-step barrier.
+template <typename T, int D, int NB, int NW, bool ROT>
 __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long qrow,
                             unsigned char* smem_raw) {
   using C = Cfg<T, D>;
@@ -321,10 +324,12 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   // chunk metadata -> LDS: positions of keys k0.., block ids of blocks k0/16..
   {
     const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
-    const int32_t* kp = a.k_pos + a.cu_k[r];
     const int nk = nsteps * C::KSTEP;
-    for (int j = tid; j < nk; j += NTH)
-      sm.pos[j] = clampi(kp[min(k0 + j, L - 1)], 0, a.max_pos - 1);
+    if constexpr (ROT) {
+      const int32_t* kp = a.k_pos + a.cu_k[r];
+      for (int j = tid; j < nk; j += NTH)
+        sm.pos[j] = clampi(kp[min(k0 + j, L - 1)], 0, a.max_pos - 1);
+    }
     const int nbk = nk / kBlockSize;
     for (int j = tid; j < nbk; j += NTH)
       sm.blk[j] = clampi(bt[min((k0 >> 4) + j, (L - 1) >> 4)], 0, a.num_blocks - 1);
@@ -396,7 +401,7 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   auto issue = [&](int j, Group& gb) {
     issue_k(j, gb);
     issue_v(j, gb);
-    issue_tab(j, gb);
+    if constexpr (ROT) issue_tab(j, gb);
   };
 
   f32x4 acc[C::ND];
@@ -412,16 +417,19 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   auto step = [&](int j, Group& gb) {
     const int buf = j & 1;
     const int kb = k0 + j * C::KSTEP;  // absolute key index
-    RF::store(&sm.cs[buf][skey][spart], gb.c);
-    RF::store(&sm.sn[buf][skey][spart], gb.sn);
-    if (j + NB < nsteps) issue_tab(j + NB, gb);
-    __syncthreads();
+    if constexpr (ROT) {
+      RF::store(&sm.cs[buf][skey][spart], gb.c);
+      RF::store(&sm.sn[buf][skey][spart], gb.sn);
+      if (j + NB < nsteps) issue_tab(j + NB, gb);
+      __syncthreads();
+    }
     f32x4 sc[C::NT];
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
       const int krow = key_of<C::NT>(t, row16);
-      rotate_from_lds<T, D>(gb.k[t], &sm.cs[buf][krow][grp * C::KPL],
-                            &sm.sn[buf][krow][grp * C::KPL]);
+      if constexpr (ROT)
+        rotate_from_lds<T, D>(gb.k[t], &sm.cs[buf][krow][grp * C::KPL],
+                              &sm.sn[buf][krow][grp * C::KPL]);
       sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) sc[t] = M::run(gb.k[t][c], qop[c], sc[t]);
@@ -792,7 +800,7 @@ struct Pf {
 // One barrier per step.  The rotated query rows (the B operand, pre-scaled
 // by log2(e)/sqrt(d) so scores come out in base-2 units) sit in a per-wave
 // LDS slice.  Steps that lie wholly below the causal diagonal skip the mask.
-template <int D, int NW>
+template <int D, int NW, bool ROT>
 __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
                                   unsigned char* smem) {
   using P = Pf<D, NW>;
@@ -851,7 +859,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
   }
 
   const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
-  const int32_t* kp = a.k_pos + a.cu_k[r];
+  const int32_t* kp = ROT ? a.k_pos + a.cu_k[r] : nullptr;
   const int nb_max = a.num_blocks - 1;
   const int pmax = a.max_pos - 1;
   const size_t blk_bytes = (size_t)a.hkv * kBlockSize * D * sizeof(bf16);
@@ -885,11 +893,11 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
   // data loads of a step, so waiting for a lookup never waits for data (the
   // load counter completes in issue order).
   int kmeta_blk, kmeta_pos, vmeta_blk[P::NVR];
-  int kmeta_blk_nx, kmeta_pos_nx, vmeta_blk_nx[P::NVR];
+  int kmeta_blk_nx, kmeta_pos_nx = 0, vmeta_blk_nx[P::NVR];
   auto kmeta = [&](int kb) {
     const int kc = min(kb + skey, L - 1);
     kmeta_blk_nx = bt[kc >> 4];
-    kmeta_pos_nx = kp[kc];
+    if constexpr (ROT) kmeta_pos_nx = kp[kc];
   };
   auto vmeta = [&](int kb) {
 #pragma unroll
@@ -911,8 +919,10 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
     const char* src = kthr + (size_t)blk * blk_bytes;
     klo = *reinterpret_cast<const KV*>(src);
     khi = *reinterpret_cast<const KV*>(src + D);  // + D/2 elements
-    tc = *reinterpret_cast<const TV*>(cthr + (size_t)pos * (D * 2));  // D/2 floats per row
-    ts = *reinterpret_cast<const TV*>(sthr + (size_t)pos * (D * 2));
+    if constexpr (ROT) {
+      tc = *reinterpret_cast<const TV*>(cthr + (size_t)pos * (D * 2));  // D/2 floats per row
+      ts = *reinterpret_cast<const TV*>(sthr + (size_t)pos * (D * 2));
+    }
   };
   auto vload = [&]() {
 #pragma unroll
@@ -922,12 +932,14 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
     }
   };
   auto kstore = [&](int step) {  // rotate the loaded K piece into K stage `step`
-    KV lo, hi;
+    KV lo = klo, hi = khi;
+    if constexpr (ROT) {
 #pragma unroll
-    for (int e = 0; e < P::KPT; ++e) {
-      const float x = (float)klo[e], y = (float)khi[e];
-      lo[e] = (bf16)(x * tc[e] - y * ts[e]);
-      hi[e] = (bf16)(y * tc[e] + x * ts[e]);
+      for (int e = 0; e < P::KPT; ++e) {
+        const float x = (float)klo[e], y = (float)khi[e];
+        lo[e] = (bf16)(x * tc[e] - y * ts[e]);
+        hi[e] = (bf16)(y * tc[e] + x * ts[e]);
+      }
     }
     bf16* kd = lds + (step % P::NKB) * P::KBUF + skey * P::KLD + si0;
     *reinterpret_cast<KV*>(kd) = lo;
@@ -1214,7 +1226,7 @@ constexpr int kDecodeDepth = 1;
 // Decode-only launch: logical item = (chunk s, request r, head group hg),
 // head group fastest, then request: the workgroups that read the same table
 // rows (the same key positions) run on one XCD and share its L2.
-template <typename T, int D>
+template <typename T, int D, bool ROT>
 __global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(DecodeSmem<T, D>)];
   const long long n = (long long)gridDim.x;
@@ -1223,7 +1235,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
   const long long rs = l / a.nhg;
   const int r = (int)(rs % a.num_reqs);
   const int s = (int)(rs / a.num_reqs);
-  decode_item<T, D, kDecodeDepth, kWaves>(a, r, hg, s, r, smem);
+  decode_item<T, D, kDecodeDepth, kWaves, ROT>(a, r, hg, s, r, smem);
 }
 
 // Waves per workgroup of the mixed launch.  bf16: eight, so a prefill tile
@@ -1248,7 +1260,7 @@ struct MixedSmem {
 };
 
 // Mixed launch over the planner's work list.
-template <typename T, int D>
+template <typename T, int D, bool ROT>
 __global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
     mixed_kernel(AttnArgs a) {
   constexpr int NW = mixed_waves<T>();
@@ -1257,12 +1269,13 @@ __global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
   const int4 it = a.items[blockIdx.x];
   if (it.x == kItemPrefill) {
     if constexpr (sizeof(T) == 2) {
-      prefill_tile_bf16<D, NW>(a, it.y, it.z, it.w, smem);
+      prefill_tile_bf16<D, NW, ROT>(a, it.y, it.z, it.w, smem);
     } else {
+      static_assert(ROT, "fp32 prefill tiles always rotate");
       prefill_tile<T, D>(a, it.y, it.z, it.w, smem);
     }
   } else {
-    decode_item<T, D, 1, NW>(a, it.y, it.z, it.w, (long long)a.cu_q[it.y], smem);
+    decode_item<T, D, 1, NW, ROT>(a, it.y, it.z, it.w, (long long)a.cu_q[it.y], smem);
   }
 }
 
@@ -1441,16 +1454,16 @@ static void launch_combine(const AttnArgs& a, hipStream_t s) {
                        dim3(kThreads), 0, s, a);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool ROT>
 static int launch_decode(const AttnArgs& a, hipStream_t s) {
   const long long n = (long long)a.num_reqs * a.s_max * a.nhg;
   if (n > 0x7fffffffLL || (long long)a.num_reqs * a.hkv > 0x7fffffffLL) return PIC_EUNSUPPORTED;
-  hipLaunchKernelGGL((decode_kernel<T, D>), dim3((unsigned)n), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<T, D, ROT>), dim3((unsigned)n), dim3(kThreads), 0, s, a);
   launch_combine<T, D>(a, s);
   return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool ROT>
 static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnHostArgs& h,
                         hipStream_t s) {
   if (w.max_items > 0x7fffffffLL) return PIC_EUNSUPPORTED;
@@ -1461,10 +1474,48 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
                      h.num_reqs, h.hkv, h.hq / h.hkv, cdiv(h.hkv, mixed_waves<T>()),
                      Cfg<T, D>::KSTEP, prefill_rows<T, D>(), len_cap,
                      w.max_items, (int4*)(ws + w.items_off), (int*)(ws + w.count_off));
-  hipLaunchKernelGGL((mixed_kernel<T, D>), dim3((unsigned)w.max_items),
+  hipLaunchKernelGGL((mixed_kernel<T, D, ROT>), dim3((unsigned)w.max_items),
                      dim3(64 * mixed_waves<T>()), 0, s, a);
   launch_combine<T, D>(a, s);
   return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
+}
+
+// One decode call: position-free (ROT) or over an already rotated cache.
+template <bool ROT>
+static int attn_decode(const AttnHostArgs& h, hipStream_t s) {
+  int st = check_attn_common(h, ROT);
+  if (st || h.num_reqs == 0) return st;
+  if (!ROT && h.dtype != PIC_BF16) return PIC_EUNSUPPORTED;
+  const WorkspaceLayout w = workspace_layout(h.num_reqs, h.num_reqs, h.max_seq_len, h.hq,
+                                             h.hkv, h.head_dim);
+  const AttnArgs a = make_args(h, w);
+  if (h.dtype == PIC_BF16)
+    return h.head_dim == 128 ? launch_decode<bf16, 128, ROT>(a, s)
+                             : launch_decode<bf16, 64, ROT>(a, s);
+  if constexpr (ROT) {
+    return h.head_dim == 128 ? launch_decode<float, 128, true>(a, s)
+                             : launch_decode<float, 64, true>(a, s);
+  }
+  return PIC_EUNSUPPORTED;
+}
+
+template <bool ROT>
+static int attn_prefill(const AttnHostArgs& h, hipStream_t s) {
+  int st = check_attn_common(h, ROT);
+  if (st || h.num_reqs == 0 || h.total_q == 0) return st;
+  if (!h.cu_seqlens_q || h.max_q_len < 0) return PIC_EINVAL;
+  if (!ROT && h.dtype != PIC_BF16) return PIC_EUNSUPPORTED;
+  const WorkspaceLayout w = workspace_layout(h.num_reqs, h.total_q, h.max_seq_len, h.hq, h.hkv,
+                                             h.head_dim);
+  const AttnArgs a = make_args(h, w);
+  if (h.dtype == PIC_BF16)
+    return h.head_dim == 128 ? launch_mixed<bf16, 128, ROT>(a, w, h, s)
+                             : launch_mixed<bf16, 64, ROT>(a, w, h, s);
+  if constexpr (ROT) {
+    return h.head_dim == 128 ? launch_mixed<float, 128, true>(a, w, h, s)
+                             : launch_mixed<float, 64, true>(a, w, h, s);
+  }
+  return PIC_EUNSUPPORTED;
 }
 
 }  // namespace pic
@@ -1480,21 +1531,11 @@ extern "C" int pic_attn_decode(const void* q, const int32_t* q_pos, const void* 
                                int block_size, int num_blocks, int max_seq_len, int dtype,
                                void* out, void* workspace, size_t workspace_bytes,
                                void* stream) {
-  AttnHostArgs h{q, nullptr, q_pos, k_pool, v_pool, block_table, block_table_stride, seq_lens,
-                 cu_seqlens_k, k_pos, cos_tab, sin_tab, max_pos, num_reqs, num_reqs, 1,
-                 num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_seq_len,
-                 dtype, out, workspace, workspace_bytes};
-  int st = pic::check_attn_common(h);
-  if (st || num_reqs == 0) return st;
-  const pic::WorkspaceLayout w = pic::workspace_layout(num_reqs, num_reqs, max_seq_len,
-                                                       num_q_heads, num_kv_heads, head_dim);
-  const pic::AttnArgs a = pic::make_args(h, w);
-  hipStream_t s = (hipStream_t)stream;
-  if (dtype == PIC_BF16)
-    return head_dim == 128 ? pic::launch_decode<pic::bf16, 128>(a, s)
-                           : pic::launch_decode<pic::bf16, 64>(a, s);
-  return head_dim == 128 ? pic::launch_decode<float, 128>(a, s)
-                         : pic::launch_decode<float, 64>(a, s);
+  const AttnHostArgs h{q, nullptr, q_pos, k_pool, v_pool, block_table, block_table_stride,
+                       seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab, max_pos, num_reqs,
+                       num_reqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, max_seq_len, dtype, out, workspace, workspace_bytes};
+  return pic::attn_decode<true>(h, (hipStream_t)stream);
 }
 
 extern "C" int pic_attn_prefill(const void* q, const int32_t* cu_seqlens_q, const int32_t* q_pos,
@@ -1506,20 +1547,41 @@ extern "C" int pic_attn_prefill(const void* q, const int32_t* cu_seqlens_q, cons
                                 int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                                 int num_blocks, int max_seq_len, int dtype, void* out,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-  AttnHostArgs h{q, cu_seqlens_q, q_pos, k_pool, v_pool, block_table, block_table_stride,
-                 seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab, max_pos, num_reqs, total_q,
-                 max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                 max_seq_len, dtype, out, workspace, workspace_bytes};
-  int st = pic::check_attn_common(h);
-  if (st || num_reqs == 0 || total_q == 0) return st;
-  if (!cu_seqlens_q || max_q_len < 0) return PIC_EINVAL;
-  const pic::WorkspaceLayout w = pic::workspace_layout(num_reqs, total_q, max_seq_len,
-                                                       num_q_heads, num_kv_heads, head_dim);
-  const pic::AttnArgs a = pic::make_args(h, w);
-  hipStream_t s = (hipStream_t)stream;
-  if (dtype == PIC_BF16)
-    return head_dim == 128 ? pic::launch_mixed<pic::bf16, 128>(a, w, h, s)
-                           : pic::launch_mixed<pic::bf16, 64>(a, w, h, s);
-  return head_dim == 128 ? pic::launch_mixed<float, 128>(a, w, h, s)
-                         : pic::launch_mixed<float, 64>(a, w, h, s);
+  const AttnHostArgs h{q, cu_seqlens_q, q_pos, k_pool, v_pool, block_table, block_table_stride,
+                       seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab, max_pos, num_reqs,
+                       total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, max_seq_len, dtype, out, workspace, workspace_bytes};
+  return pic::attn_prefill<true>(h, (hipStream_t)stream);
+}
+
+extern "C" int pic_attn_decode_rotated(const void* q, const int32_t* q_pos, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_table,
+                                       int block_table_stride, const int32_t* seq_lens,
+                                       const float* cos_tab, const float* sin_tab, int max_pos,
+                                       int num_reqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int num_blocks,
+                                       int max_seq_len, int dtype, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const AttnHostArgs h{q, nullptr, q_pos, k_pool, v_pool, block_table, block_table_stride,
+                       seq_lens, nullptr, nullptr, cos_tab, sin_tab, max_pos, num_reqs,
+                       num_reqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, max_seq_len, dtype, out, workspace, workspace_bytes};
+  return pic::attn_decode<false>(h, (hipStream_t)stream);
+}
+
+extern "C" int pic_attn_prefill_rotated(const void* q, const int32_t* cu_seqlens_q,
+                                        const int32_t* q_pos, const void* k_pool,
+                                        const void* v_pool, const int32_t* block_table,
+                                        int block_table_stride, const int32_t* seq_lens,
+                                        const float* cos_tab, const float* sin_tab,
+                                        int max_pos, int num_reqs, int total_q, int max_q_len,
+                                        int num_q_heads, int num_kv_heads, int head_dim,
+                                        int block_size, int num_blocks, int max_seq_len,
+                                        int dtype, void* out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  const AttnHostArgs h{q, cu_seqlens_q, q_pos, k_pool, v_pool, block_table, block_table_stride,
+                       seq_lens, nullptr, nullptr, cos_tab, sin_tab, max_pos, num_reqs,
+                       total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, max_seq_len, dtype, out, workspace, workspace_bytes};
+  return pic::attn_prefill<false>(h, (hipStream_t)stream);
 }

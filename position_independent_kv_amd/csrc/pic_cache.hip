@@ -65,6 +65,68 @@ static int launch_cache_write(const void* k, const void* v, const int32_t* slots
   return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }
 
+// The conventional write of a RoPE cache, kept for the in-kernel-rotation
+// ablation: the key is rotated to its position before it is stored (rotate-
+// half pairs (i, i + d/2), angle table from pic_rope_table), so the block is
+// only valid at that one offset.  One thread per (token, head, VEC pairs):
+// it reads the two halves of the pairs, writes both rotated halves, and
+// copies the same elements of V unchanged.  The rotation is computed in fp32
+// with the same expression the attention kernels use, then rounded to T.
+template <typename T>
+__global__ void __launch_bounds__(256) cache_write_rotated_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ slots,
+    const int32_t* __restrict__ positions, const float* __restrict__ cos_tab,
+    const float* __restrict__ sin_tab, int max_pos, long long num_tokens, int hkv, int head_dim,
+    T* __restrict__ k_pool, T* __restrict__ v_pool, long long num_slots) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int half = head_dim / 2;
+  const int chunks = half / VEC;  // chunks of the first half of d
+  const long long n = num_tokens * hkv * chunks;
+  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < n;
+       idx += (long long)gridDim.x * 256) {
+    const int c = (int)(idx % chunks);
+    const long long th = idx / chunks;  // token * hkv + head
+    const int h = (int)(th % hkv);
+    const long long t = th / hkv;
+    const long long slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int p = min(max(positions[t], 0), max_pos - 1);
+    const long long blk = slot / kBlockSize;
+    const int off = (int)(slot % kBlockSize);
+    const int i0 = c * VEC;
+    T* kdst = k_pool + ((blk * hkv + h) * kBlockSize + off) * head_dim;
+    T* vdst = v_pool + (blk * hkv + h) * (long long)head_dim * kBlockSize + off;
+    const T* ks = k + th * head_dim;
+    const T* vs = v + th * head_dim;
+    const float* cr = cos_tab + (long long)p * half + i0;
+    const float* sr = sin_tab + (long long)p * half + i0;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float x = (float)ks[i0 + e], y = (float)ks[half + i0 + e];
+      const float co = cr[e], si = sr[e];
+      kdst[i0 + e] = (T)(x * co - y * si);
+      kdst[half + i0 + e] = (T)(y * co + x * si);
+      vdst[(long long)(i0 + e) * kBlockSize] = vs[i0 + e];
+      vdst[(long long)(half + i0 + e) * kBlockSize] = vs[half + i0 + e];
+    }
+  }
+}
+
+template <typename T>
+static int launch_cache_write_rotated(const void* k, const void* v, const int32_t* slots,
+                                      const int32_t* positions, const float* cos_tab,
+                                      const float* sin_tab, int max_pos, int n, int hkv, int d,
+                                      void* kp, void* vp, long long num_slots, hipStream_t s) {
+  constexpr int VEC = 16 / sizeof(T);
+  const long long nt = (long long)n * hkv * (d / 2 / VEC);
+  long long blocks = (nt + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(cache_write_rotated_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const T*)k, (const T*)v, slots, positions, cos_tab, sin_tab, max_pos,
+                     (long long)n, hkv, d, (T*)kp, (T*)vp, num_slots);
+  return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
+}
+
 }  // namespace pic
 
 extern "C" int pic_cache_write(const void* k, const void* v, const int32_t* slot_mapping,
@@ -85,4 +147,28 @@ extern "C" int pic_cache_write(const void* k, const void* v, const int32_t* slot
                                               num_slots, s);
   return pic::launch_cache_write<float>(k, v, slot_mapping, num_tokens, num_kv_heads, head_dim,
                                         k_pool, v_pool, num_slots, s);
+}
+
+extern "C" int pic_cache_write_rotated(const void* k, const void* v, const int32_t* slot_mapping,
+                                       const int32_t* positions, const float* cos_tab,
+                                       const float* sin_tab, int max_pos, int num_tokens,
+                                       int num_kv_heads, int head_dim, int dtype, void* k_pool,
+                                       void* v_pool, int num_blocks, int block_size,
+                                       void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0 || max_pos <= 0) return PIC_EINVAL;
+  if (dtype != PIC_F32 && dtype != PIC_BF16) return PIC_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PIC_EUNSUPPORTED;
+  if (block_size != pic::kBlockSize) return PIC_EUNSUPPORTED;
+  if (num_tokens == 0) return PIC_OK;
+  if (!k || !v || !slot_mapping || !positions || !cos_tab || !sin_tab || !k_pool || !v_pool)
+    return PIC_EINVAL;
+  const long long num_slots = (long long)num_blocks * block_size;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == PIC_BF16)
+    return pic::launch_cache_write_rotated<__bf16>(k, v, slot_mapping, positions, cos_tab,
+                                                   sin_tab, max_pos, num_tokens, num_kv_heads,
+                                                   head_dim, k_pool, v_pool, num_slots, s);
+  return pic::launch_cache_write_rotated<float>(k, v, slot_mapping, positions, cos_tab, sin_tab,
+                                                max_pos, num_tokens, num_kv_heads, head_dim,
+                                                k_pool, v_pool, num_slots, s);
 }

@@ -47,7 +47,7 @@ int check_heads(int hq, int hkv) {
   return PIC_OK;
 }
 
-int check_attn_common(const AttnHostArgs& a) {
+int check_attn_common(const AttnHostArgs& a, bool key_positions) {
   if (a.num_reqs < 0 || a.total_q < 0 || a.max_seq_len < 0 || a.num_blocks < 0 ||
       a.block_table_stride < 0 || a.max_pos <= 0)
     return PIC_EINVAL;
@@ -57,8 +57,9 @@ int check_attn_common(const AttnHostArgs& a) {
   if (st) return st;
   if (a.num_reqs == 0 || a.total_q == 0) return PIC_OK;
   if (!a.q || !a.q_pos || !a.k_pool || !a.v_pool || !a.block_table || !a.seq_lens ||
-      !a.cu_seqlens_k || !a.k_pos || !a.cos_tab || !a.sin_tab || !a.out)
+      !a.cos_tab || !a.sin_tab || !a.out)
     return PIC_EINVAL;
+  if (key_positions && (!a.cu_seqlens_k || !a.k_pos)) return PIC_EINVAL;
   if (a.num_blocks == 0 || a.block_table_stride == 0) return PIC_EINVAL;
   if ((long long)a.block_table_stride * a.block_size < a.max_seq_len) return PIC_EINVAL;
   if (!a.workspace) return PIC_EWORKSPACE;

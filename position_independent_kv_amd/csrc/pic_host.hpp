@@ -37,6 +37,8 @@ struct AttnHostArgs {
 
 int check_dtype_dims(int dtype, int head_dim, int block_size);
 int check_heads(int hq, int hkv);
-int check_attn_common(const AttnHostArgs& a);
+// Host-visible argument checks of an attention call; key_positions: the call
+// reads cu_seqlens_k and k_pos (the position-free kernels do).
+int check_attn_common(const AttnHostArgs& a, bool key_positions);
 
 }  // namespace pic

@@ -92,6 +92,66 @@ class DeviceWorkload:
                                  self.sin, w.max_q_len, w.max_seq_len, out, self.workspace)
         return out
 
+    def build_rotated_cache(self):
+        """The conventional RoPE cache of this batch, for the in-kernel-rotation ablation.
+
+        Every request gets private blocks holding its own slots' keys rotated to
+        its own positions (pic_cache_write_rotated); a shared span is therefore
+        stored once per request that uses it.  Reads the pools as they are now
+        (call after the step's cache write).  Sets rot_k_pool, rot_v_pool and
+        rot_block_table.
+        """
+        torch = _torch()
+        w = self.w
+        B = w.block_size
+        L = w.seq_lens.astype(np.int64)
+        nblk = (L + B - 1) // B
+        base = np.concatenate([[0], np.cumsum(nblk)[:-1]]).astype(np.int64)
+        total = int(nblk.sum())
+        stride = max(int(nblk.max()) if len(nblk) else 1, 1)
+        bt = np.zeros((w.num_reqs, stride), np.int32)
+        src, dst, pos = [], [], []
+        for r in range(w.num_reqs):
+            j = np.arange(int(L[r]), dtype=np.int64)
+            bt[r, :nblk[r]] = base[r] + np.arange(nblk[r])
+            src.append(w.block_table[r, j // B].astype(np.int64) * B + j % B)
+            dst.append((base[r] + j // B) * B + j % B)
+            pos.append(w.k_pos[int(w.cu_seqlens_k[r]):int(w.cu_seqlens_k[r]) + int(L[r])])
+        src = np.concatenate(src) if src else np.zeros(0, np.int64)
+        dst = np.concatenate(dst) if dst else np.zeros(0, np.int64)
+        pos = np.concatenate(pos) if pos else np.zeros(0, np.int32)
+        dev = self.k_pool.device
+        s_t = torch.from_numpy(src).to(dev)
+        blk, off = s_t // B, s_t % B
+        k_tok = self.k_pool[blk, :, off, :].contiguous()      # [T][Hkv][d]
+        v_tok = self.v_pool[blk, :, :, off].contiguous()      # [T][Hkv][d]
+        self.rot_k_pool = torch.full((max(total, 1), w.hkv, B, w.d), float("nan"),
+                                     dtype=self.dtype, device=dev)
+        self.rot_v_pool = torch.full((max(total, 1), w.hkv, w.d, B), float("nan"),
+                                     dtype=self.dtype, device=dev)
+        self.rot_block_table = i32(bt, dev)
+        if src.shape[0]:
+            pic.pic_cache_write_rotated(k_tok, v_tok, i32(dst, dev), i32(pos, dev), self.cos,
+                                        self.sin, self.rot_k_pool, self.rot_v_pool)
+        return self
+
+    def attention_rotated(self, decode=None, out=None):
+        """The same attention over the rotated cache (key rotation compiled out)."""
+        w = self.w
+        out = self.out if out is None else out
+        if decode is None:
+            decode = w.kind == "decode"
+        if decode:
+            pic.pic_attn_decode_rotated(self.q, self.q_pos, self.rot_k_pool, self.rot_v_pool,
+                                        self.rot_block_table, self.seq_lens, self.cos, self.sin,
+                                        w.max_seq_len, out, self.workspace)
+        else:
+            pic.pic_attn_prefill_rotated(self.q, self.cu_q, self.q_pos, self.rot_k_pool,
+                                         self.rot_v_pool, self.rot_block_table, self.seq_lens,
+                                         self.cos, self.sin, w.max_q_len, w.max_seq_len, out,
+                                         self.workspace)
+        return out
+
     def step(self, decode=None):
         """One serving step: write the new tokens, then attention."""
         self.write_new_tokens()

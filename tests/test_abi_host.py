@@ -28,7 +28,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = pic.library()
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(pic.EXPORTS)
@@ -114,6 +114,44 @@ def test_entry_points_reject_bad_arguments_before_launch():
     pargs[24] = buf
     pargs[25] = 1 << 40
     assert lib.pic_attn_prefill(*pargs) == pic.PIC_EINVAL
+
+
+def test_rotated_cache_entry_points_reject_bad_arguments_before_launch():
+    """The ablation entry points (rotated cache): same host checks, bf16 attention only."""
+    lib = pic.library()
+    buf = ctypes.c_void_p(1)  # never dereferenced: rejected before launch
+    w = lib.pic_cache_write_rotated
+    assert w(None, None, None, None, None, None, 10, 0, 8, 128, 1, None, None, 4, 16, None) == 0
+    assert w(buf, buf, buf, None, buf, buf, 10, 5, 8, 128, 1, buf, buf, 4, 16, None) == -1
+    assert w(buf, buf, buf, buf, None, buf, 10, 5, 8, 128, 1, buf, buf, 4, 16, None) == -1
+    assert w(buf, buf, buf, buf, buf, buf, 0, 5, 8, 128, 1, buf, buf, 4, 16, None) == -1
+    assert w(buf, buf, buf, buf, buf, buf, 10, 5, 8, 96, 1, buf, buf, 4, 16, None) == -2
+    assert w(buf, buf, buf, buf, buf, buf, 10, 5, 8, 128, 1, buf, buf, 4, 8, None) == -2
+    # decode over a rotated cache: 3 pointers fewer than pic_attn_decode (no k positions)
+    args = [buf] * 5 + [300] + [buf] * 3 + [4097, 4, 32, 8, 128, 16, 100, 4097, 1] + [buf, None,
+                                                                                   0, None]
+    assert lib.pic_attn_decode_rotated(*args) == pic.PIC_EWORKSPACE
+    a2 = list(args)
+    a2[17] = pic.PIC_F32
+    a2[19], a2[20] = buf, 1 << 40
+    assert lib.pic_attn_decode_rotated(*a2) == pic.PIC_EUNSUPPORTED
+    a3 = list(args)
+    a3[7] = None  # cos_tab
+    assert lib.pic_attn_decode_rotated(*a3) == pic.PIC_EINVAL
+    a4 = list(args)
+    a4[10] = 0  # empty batch
+    assert lib.pic_attn_decode_rotated(*a4) == pic.PIC_OK
+    pargs = [buf] * 6 + [300] + [buf] * 3 + [4097, 4, 40, 16, 32, 8, 128, 16, 100, 4097, 1] + [
+        buf, None, 0, None]
+    assert lib.pic_attn_prefill_rotated(*pargs) == pic.PIC_EWORKSPACE
+    p2 = list(pargs)
+    p2[20] = pic.PIC_F32
+    p2[22], p2[23] = buf, 1 << 40
+    assert lib.pic_attn_prefill_rotated(*p2) == pic.PIC_EUNSUPPORTED
+    p3 = list(pargs)
+    p3[1] = None
+    p3[22], p3[23] = buf, 1 << 40
+    assert lib.pic_attn_prefill_rotated(*p3) == pic.PIC_EINVAL
 
 
 def test_validate_metadata_accepts_configs():
