@@ -161,6 +161,38 @@ def rope_ablation(name, reps=20):
     return res
 
 
+def block_table_build(reps=5):
+    """Host cost of the span-aware block tables (pic_build_block_tables) for a batch
+    composed like the default decode workload: 64 prompts of 4 x 1024 tokens, two of
+    them SSEP spans drawn from a pool of 32 (so shared), two private, each prompt
+    closed by a 16-token PDEP block.  Median of `reps` builds."""
+    import position_independent_kv_amd as pic
+    rng = np.random.default_rng(7)
+    ssep, pdep = 128001, 128002
+    spans = [np.concatenate([[ssep], rng.integers(0, 120000, 1023)]).astype(np.int32)
+             for _ in range(32)]
+    prompts = []
+    for _ in range(64):
+        k = rng.choice(32, size=2, replace=False)
+        own = [rng.integers(0, 120000, 1024).astype(np.int32) for _ in range(2)]
+        suffix = np.concatenate([[pdep], rng.integers(0, 120000, 15)]).astype(np.int32)
+        prompts.append(np.concatenate([own[0], spans[k[0]], own[1], spans[k[1]], suffix]))
+    toks = np.concatenate(prompts)
+    cu = np.concatenate([[0], np.cumsum([len(p) for p in prompts])]).astype(np.int32)
+    times = []
+    for _ in range(reps):
+        t = time.perf_counter()
+        res = pic.pic_build_block_tables(toks, cu, 16, ssep, pdep, seed=1)
+        times.append(time.perf_counter() - t)
+    ms = float(np.median(times)) * 1e3
+    logical = int(sum(-(-len(p) // 16) for p in prompts))
+    log(f"[bench] block tables: {toks.shape[0]} tokens in {ms:.2f} ms on the host; "
+        f"{res['num_new_blocks']} physical blocks for {logical} logical")
+    return {"tokens": int(toks.shape[0]), "host_ms": ms,
+            "tokens_per_s": toks.shape[0] / (ms * 1e-3),
+            "physical_blocks": res["num_new_blocks"], "logical_blocks": logical}
+
+
 def cpu_baseline(w, counts, budget_s=12.0):
     """The fp64 oracle on the host: a bounded sample of the same step."""
     import oracle
@@ -295,6 +327,7 @@ def main():
     ablation = {}
     for name in [x for x in args.ablation.split(",") if x]:
         ablation[name] = rope_ablation(name)
+    tables = block_table_build()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -327,6 +360,7 @@ def main():
                  "attention_kernel_ms": main_res["kernel_ms"]},
         "configs": others,
         "rope_ablation": ablation,
+        "block_tables": tables,
         "source_hash": source_hash(),
     }
     print(json.dumps(out), flush=True)

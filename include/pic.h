@@ -220,6 +220,61 @@ int pic_attn_prefill_rotated(const void* q, const int32_t* cu_seqlens_q, const i
                              void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Span-aware block hashing (host code, no device work).  MiniPIC §2.2
+ * ("user-controlled cache reuse primitives"): spans are padded to KV-block
+ * boundaries, and two special tokens at the START of a block change how that
+ * block's prefix-cache hash is chained, which decides which blocks requests
+ * share:
+ *   default            h_i = H(h_{i-1}, x_i)
+ *   SSEP at block start h_i = H(h_0, x_i)       chain restarts: the span is
+ *                                               cacheable whatever precedes it
+ *   PDEP at block start h_i = H(h_0, x_{<=i})   depends on the whole prompt up
+ *                                               to block i (no false hits)
+ * x_i = token ids of block i, h_0 = seed, h_{-1} = h_0.  H is FNV-1a 64 over
+ * the little-endian bytes of the 8-byte parent hash followed by each token as
+ * 4 bytes (for PDEP: h_0 followed by every token of blocks 0..i).  A special
+ * token anywhere else is an ordinary token.  Pass -1 to disable a primitive.
+ * Only full blocks are hashed; a trailing partial block is never shared.
+ *
+ * pic_block_hashes -- hashes of the full blocks of one token sequence.
+ *   tokens  int32 [num_tokens], HOST;  hashes  uint64 [num_tokens / block_size], HOST
+ * Returns the number of hashes written (>= 0), or PIC_EINVAL (num_tokens < 0,
+ * block_size <= 0, null pointers with at least one full block).
+ */
+int pic_block_hashes(const int32_t* tokens, int num_tokens, int block_size, int32_t ssep_token,
+                     int32_t pdep_token, uint64_t seed, uint64_t* hashes);
+
+/*
+ * pic_build_block_tables -- the attention metadata of a batch of prompts with
+ * block sharing decided by the hashes above (all arrays HOST memory).
+ *   tokens      int32 [cu_seqlens[num_reqs]]: the prompts, concatenated
+ *   cu_seqlens  int32 [num_reqs + 1], cu_seqlens[0] == 0
+ *   block_size  must be 16 (the attention kernels' block size)
+ *   first_block, num_blocks: new physical blocks are numbered first_block,
+ *               first_block + 1, ... and must stay below num_blocks
+ * Outputs:
+ *   block_table  int32 [num_reqs][block_table_stride] (unused entries 0):
+ *                full blocks with equal hashes (across and within requests)
+ *                map to one physical block, numbered in order of first use;
+ *                a partial last block always gets its own block
+ *   k_pos        int32 [total tokens]: pi(j) = j, the token's index in its
+ *                request (positions run over the composed prompt)
+ *   slot_mapping int32 [total tokens]: the cache slot to write each token's
+ *                K/V to (pic_cache_write), or -1 where an earlier occurrence of
+ *                the same block in the batch writes it
+ *   block_hashes uint64 [sum of full blocks], may be NULL
+ *   num_new_blocks  physical blocks used
+ * Returns PIC_OK, or PIC_EINVAL for bad sizes, a table too narrow for a
+ * request, or a pool too small (num_blocks reached).
+ */
+int pic_build_block_tables(const int32_t* tokens, const int32_t* cu_seqlens, int num_reqs,
+                           int block_size, int32_t ssep_token, int32_t pdep_token,
+                           uint64_t seed, int first_block, int num_blocks,
+                           int32_t* block_table, int block_table_stride, int32_t* k_pos,
+                           int32_t* slot_mapping, uint64_t* block_hashes,
+                           int* num_new_blocks);
+
+/*
  * pic_validate_metadata -- check the device-value preconditions above on
  * HOST copies of the metadata (test and debug helper; no device work).
  * cu_seqlens_q may be NULL for a decode batch (one query per request).

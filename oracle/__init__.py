@@ -17,7 +17,11 @@ hit.  Every step the page leaves open is a documented reading (rotate-half
 pairing, standard RoPE frequencies, bottom-right causal mask over slot index,
 GQA head mapping h -> h // G, unrotated V); see the module docstrings.
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+The span-hashing reference (``pic_spans``) follows §2.2 (the SSEP / PDEP
+block-hash primitives) and is pinned by ``tests/test_spans_oracle.py``
+(published FNV-1a test vectors, closed-form hash chains, mutation checks).
+
+Parity status: every attention function here is pinned by ``tests/test_oracle_pins.py``
 (brute force with explicit rotation matrices, pre-rotated equality with a
 library attention routine, shift invariance, closed forms and special cases).
 """
@@ -31,4 +35,9 @@ from .pic_oracle import (  # noqa: F401
     attention_request,
     attention,
     bf16_bits_to_f64,
+)
+from .pic_spans import (  # noqa: F401
+    fnv1a64,
+    block_hashes,
+    build_block_tables,
 )

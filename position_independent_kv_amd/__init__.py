@@ -31,7 +31,8 @@ EXPORTS = [
     "pic_status_string", "pic_version", "pic_rope_table", "pic_cache_write",
     "pic_attn_workspace_size", "pic_attn_decode", "pic_attn_prefill", "pic_validate_metadata",
     "pic_decode_num_splits", "pic_decode_split_len", "pic_cache_write_rotated",
-    "pic_attn_decode_rotated", "pic_attn_prefill_rotated",
+    "pic_attn_decode_rotated", "pic_attn_prefill_rotated", "pic_block_hashes",
+    "pic_build_block_tables",
 ]
 
 
@@ -78,6 +79,11 @@ def _load():
                                             + [c_void, c_void, c_size, c_void])
     lib.pic_attn_prefill_rotated.argtypes = ([c_void] * 6 + [c_int] + [c_void] * 3
                                              + [c_int] * 11 + [c_void, c_void, c_size, c_void])
+    c_i32, c_u64 = ctypes.c_int32, ctypes.c_uint64
+    lib.pic_block_hashes.argtypes = [c_void, c_int, c_int, c_i32, c_i32, c_u64, c_void]
+    lib.pic_build_block_tables.argtypes = ([c_void, c_void, c_int, c_int, c_i32, c_i32, c_u64,
+                                            c_int, c_int, c_void, c_int, c_void, c_void, c_void,
+                                            c_void])
     lib.pic_decode_num_splits.argtypes = [c_int, c_int]
     lib.pic_decode_split_len.argtypes = [c_int, c_int]
     for name in EXPORTS:
@@ -339,6 +345,50 @@ def pic_validate_metadata(cu_seqlens_q, q_pos, block_table, seq_lens, cu_seqlens
                                        p(arrs["k_pos"]), R, total_q, int(max_seq_len),
                                        int(max_pos), int(num_blocks), int(block_size), buf, 256)
     return st, buf.value.decode()
+
+
+def _host_i32(a, name):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.int32:
+        raise TypeError(f"{name} must be int32")
+    return a
+
+
+def pic_block_hashes(tokens, block_size: int, ssep_token: int = -1, pdep_token: int = -1,
+                     seed: int = 0) -> np.ndarray:
+    """Span-aware hashes of the full blocks of one host int32 token sequence (uint64)."""
+    tok = _host_i32(tokens, "tokens")
+    out = np.zeros(max(tok.shape[0] // max(block_size, 1), 1), np.uint64)
+    n = _load().pic_block_hashes(tok.ctypes.data, tok.shape[0], block_size, ssep_token,
+                                 pdep_token, seed, out.ctypes.data)
+    if n < 0:
+        _check(n, "pic_block_hashes")
+    return out[:n]
+
+
+def pic_build_block_tables(tokens, cu_seqlens, block_size: int = BLOCK_SIZE,
+                           ssep_token: int = -1, pdep_token: int = -1, seed: int = 0,
+                           first_block: int = 0, num_blocks: int = 1 << 30, stride=None):
+    """Block tables, positions and slot mapping of a batch of host prompts (see pic.h)."""
+    tok = _host_i32(tokens, "tokens")
+    cu = _host_i32(cu_seqlens, "cu_seqlens")
+    R = cu.shape[0] - 1
+    lens = np.diff(cu)
+    if stride is None:
+        stride = max(int(((lens + block_size - 1) // block_size).max()) if R else 1, 1)
+    bt = np.zeros((max(R, 1), stride), np.int32)
+    total = int(cu[-1]) if R else 0
+    k_pos = np.zeros(max(total, 1), np.int32)
+    slots = np.zeros(max(total, 1), np.int32)
+    hashes = np.zeros(max(int((lens // block_size).sum()) if R else 0, 1), np.uint64)
+    nnew = ctypes.c_int(0)
+    _check(_load().pic_build_block_tables(
+        tok.ctypes.data, cu.ctypes.data, R, block_size, ssep_token, pdep_token, seed,
+        first_block, num_blocks, bt.ctypes.data, stride, k_pos.ctypes.data, slots.ctypes.data,
+        hashes.ctypes.data, ctypes.byref(nnew)), "pic_build_block_tables")
+    nh = int((lens // block_size).sum()) if R else 0
+    return dict(block_table=bt[:R], k_pos=k_pos[:total], slot_mapping=slots[:total],
+                block_hashes=hashes[:nh], num_new_blocks=int(nnew.value))
 
 
 def pic_decode_num_splits(seq_len: int, dtype: int = PIC_BF16) -> int:

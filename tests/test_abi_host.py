@@ -28,7 +28,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = pic.library()
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(pic.EXPORTS)
@@ -218,14 +218,29 @@ int main() {
   bt[4] = 9;
   if (pic_validate_metadata(cu_q, q_pos, bt, 3, sl, cu_k, k_pos, 2, 3, 10, 20, 4, 4, msg, 8) == 0) ++fails;
   if (strlen(msg) > 7) ++fails;
+  // span hashing and block tables: a batch with a shared SSEP span, a PDEP suffix, partial blocks
+  int tok[100];
+  for (int i = 0; i < 100; ++i) tok[i] = (i * 7919) % 1000;
+  tok[0] = 5001; tok[50] = 5001; tok[66] = 5002;
+  for (int i = 1; i < 16; ++i) tok[50 + i] = tok[i];
+  unsigned long long hs[8];
+  if (pic_block_hashes(tok, 100, 16, 5001, 5002, 7, (uint64_t*)hs) != 6) ++fails;
+  int cu2[4] = {0, 40, 90, 100}, bt2[3 * 4], kp2[100], sm2[100], nnew = -1;
+  unsigned long long bh[8];
+  if (pic_build_block_tables(tok, cu2, 3, 16, 5001, 5002, 7, 0, 64, bt2, 4, kp2, sm2,
+                             (uint64_t*)bh, &nnew) != 0) ++fails;
+  if (nnew <= 0 || nnew > 9) ++fails;
+  if (pic_build_block_tables(tok, cu2, 3, 16, 5001, 5002, 7, 0, 2, bt2, 4, kp2, sm2, NULL,
+                             &nnew) == 0) ++fails;  // pool too small
   printf("fails=%d\n", fails);
   return fails;
 }
 ''')
     exe = tmp_path / "host_test"
-    src = os.path.join(ROOT, "position_independent_kv_amd", "csrc", "pic_host.cpp")
+    csrc = os.path.join(ROOT, "position_independent_kv_amd", "csrc")
+    srcs = [os.path.join(csrc, "pic_host.cpp"), os.path.join(csrc, "pic_spans.cpp")]
     cmd = [gxx, "-std=c++17", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
-           "-I", os.path.join(ROOT, "include"), src, str(main), "-o", str(exe)]
+           "-I", os.path.join(ROOT, "include"), *srcs, str(main), "-o", str(exe)]
     subprocess.run(cmd, check=True)
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
