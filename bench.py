@@ -47,10 +47,11 @@ def log(*a):
 
 
 def source_hash() -> str:
-    """Hash of the kernel sources: traffic counters are only valid for this exact code."""
+    """Hash of the GPU kernel sources (.hip, .hpp): traffic counters are only valid for
+    this exact device code.  Host-only C++ (.cpp) does not enter."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "position_independent_kv_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".hpp"))):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -157,6 +158,46 @@ def rope_ablation(name, reps=20):
     log(f"[bench] rope ablation {name}: position-free {pf * 1e3:.1f} us, rotated cache "
         f"{rot * 1e3:.1f} us ({res['rotation_overhead_frac'] * 100:+.1f} %)")
     del dw
+    torch.cuda.empty_cache()
+    return res
+
+
+def offload_bandwidth(n_blocks=4096, reps=5):
+    """pic_blocks_copy between the device pools and a pinned host pool (CPU offload of
+    position-free blocks): n_blocks whole blocks of the default layer shape (K+V = 64 KiB
+    each in bf16), scattered ids, each direction timed with HIP events."""
+    import torch
+
+    import position_independent_kv_amd as pic
+    shape_k, shape_v = (n_blocks, 8, 16, 128), (n_blocks, 8, 128, 16)
+    dk = torch.randn(shape_k, device="cuda").to(torch.bfloat16)
+    dv = torch.randn(shape_v, device="cuda").to(torch.bfloat16)
+    hk = torch.empty(shape_k, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty(shape_v, dtype=torch.bfloat16, pin_memory=True)
+    rng = np.random.default_rng(3)
+    src = torch.from_numpy(rng.permutation(n_blocks).astype(np.int32)).cuda()
+    dst = torch.from_numpy(rng.permutation(n_blocks).astype(np.int32)).cuda()
+    nbytes = 2 * dk.numel() * dk.element_size()
+    stream = torch.cuda.current_stream()
+    res = {}
+    for label, args in [("device_to_host", (dk, dv, src, hk, hv, dst)),
+                        ("host_to_device", (hk, hv, dst, dk, dv, src))]:
+        pic.pic_blocks_copy(*args)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            pic.pic_blocks_copy(*args)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[label] = {"ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9}
+    ok = torch.equal(dk[src.long()].cpu(), hk[dst.long().cpu()])
+    log(f"[bench] offload {n_blocks} blocks ({nbytes / 2**20:.0f} MiB): "
+        f"d2h {res['device_to_host']['GBps']:.1f} GB/s, h2d {res['host_to_device']['GBps']:.1f} GB/s, "
+        f"round trip exact: {ok}")
+    res.update(blocks=n_blocks, bytes=nbytes, round_trip_exact=bool(ok))
+    del dk, dv, hk, hv
     torch.cuda.empty_cache()
     return res
 
@@ -328,6 +369,7 @@ def main():
     for name in [x for x in args.ablation.split(",") if x]:
         ablation[name] = rope_ablation(name)
     tables = block_table_build()
+    offload = offload_bandwidth()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -361,6 +403,7 @@ def main():
         "configs": others,
         "rope_ablation": ablation,
         "block_tables": tables,
+        "offload": offload,
         "source_hash": source_hash(),
     }
     print(json.dumps(out), flush=True)

@@ -220,6 +220,28 @@ int pic_attn_prefill_rotated(const void* q, const int32_t* cu_seqlens_q, const i
                              void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pic_blocks_copy -- copy whole KV blocks between two pools: block
+ * src_blocks[i] of (src_k_pool, src_v_pool) goes to block dst_blocks[i] of
+ * (dst_k_pool, dst_v_pool), K and V, bytes unchanged.  For CPU offload of
+ * position-free blocks (MiniPIC §3, "native compatibility": unrotated
+ * blocks move between GPU and host without tracking or adjusting positions):
+ * either pool may be device memory or PINNED host memory allocated with
+ * hipHostMalloc (torch: pin_memory=True), which the kernel reads or writes
+ * over the host link.  Both pools use the layouts above with the same
+ * num_kv_heads, head_dim and dtype; src_blocks/dst_blocks are int32
+ * [num_pairs] in device-accessible memory (device or pinned host).  A pair
+ * with an id outside [0, num_src_blocks) or [0, num_dst_blocks) is skipped.
+ * Pairs writing the same destination block race.  Stream-ordered like
+ * every other call: synchronise the stream before the host reads a host
+ * pool.  Errors: PIC_EINVAL (negative sizes, null pointers with
+ * num_pairs > 0), PIC_EUNSUPPORTED (dtype, head_dim, block_size).
+ */
+int pic_blocks_copy(const void* src_k_pool, const void* src_v_pool, const int32_t* src_blocks,
+                    int num_src_blocks, void* dst_k_pool, void* dst_v_pool,
+                    const int32_t* dst_blocks, int num_dst_blocks, int num_pairs,
+                    int num_kv_heads, int head_dim, int dtype, int block_size, void* stream);
+
+/*
  * Span-aware block hashing (host code, no device work).  MiniPIC §2.2
  * ("user-controlled cache reuse primitives"): spans are padded to KV-block
  * boundaries, and two special tokens at the START of a block change how that

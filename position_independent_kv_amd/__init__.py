@@ -32,7 +32,7 @@ EXPORTS = [
     "pic_attn_workspace_size", "pic_attn_decode", "pic_attn_prefill", "pic_validate_metadata",
     "pic_decode_num_splits", "pic_decode_split_len", "pic_cache_write_rotated",
     "pic_attn_decode_rotated", "pic_attn_prefill_rotated", "pic_block_hashes",
-    "pic_build_block_tables",
+    "pic_build_block_tables", "pic_blocks_copy",
 ]
 
 
@@ -84,6 +84,8 @@ def _load():
     lib.pic_build_block_tables.argtypes = ([c_void, c_void, c_int, c_int, c_i32, c_i32, c_u64,
                                             c_int, c_int, c_void, c_int, c_void, c_void, c_void,
                                             c_void])
+    lib.pic_blocks_copy.argtypes = ([c_void] * 3 + [c_int] + [c_void] * 3 + [c_int] * 6
+                                    + [c_void])
     lib.pic_decode_num_splits.argtypes = [c_int, c_int]
     lib.pic_decode_split_len.argtypes = [c_int, c_int]
     for name in EXPORTS:
@@ -345,6 +347,33 @@ def pic_validate_metadata(cu_seqlens_q, q_pos, block_table, seq_lens, cu_seqlens
                                        p(arrs["k_pos"]), R, total_q, int(max_seq_len),
                                        int(max_pos), int(num_blocks), int(block_size), buf, 256)
     return st, buf.value.decode()
+
+
+def pic_blocks_copy(src_k_pool, src_v_pool, src_blocks, dst_k_pool, dst_v_pool, dst_blocks,
+                    stream=None):
+    """Copy whole blocks src_blocks[i] -> dst_blocks[i] between two pools (device or pinned
+    host tensors); the id arrays are int32 tensors the device can read."""
+    torch = _torch()
+    nsb, hkv, bs, d = _pool_dims(src_k_pool, src_v_pool)
+    ndb, dhkv, dbs, dd = _pool_dims(dst_k_pool, dst_v_pool)
+    if (hkv, bs, d) != (dhkv, dbs, dd) or src_k_pool.dtype != dst_k_pool.dtype:
+        raise ValueError("source and destination pools must have the same block shape and dtype")
+    if src_blocks.shape != dst_blocks.shape or src_blocks.dim() != 1:
+        raise ValueError("src_blocks and dst_blocks must both be [num_pairs]")
+    for t, name in [(src_k_pool, "src_k_pool"), (src_v_pool, "src_v_pool"),
+                    (dst_k_pool, "dst_k_pool"), (dst_v_pool, "dst_v_pool"),
+                    (src_blocks, "src_blocks"), (dst_blocks, "dst_blocks")]:
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be device memory or pinned host memory")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if src_blocks.dtype != torch.int32 or dst_blocks.dtype != torch.int32:
+        raise TypeError("block id arrays must be int32")
+    _check(_load().pic_blocks_copy(
+        src_k_pool.data_ptr(), src_v_pool.data_ptr(), src_blocks.data_ptr(), nsb,
+        dst_k_pool.data_ptr(), dst_v_pool.data_ptr(), dst_blocks.data_ptr(), ndb,
+        src_blocks.shape[0], hkv, d, _dtype_code(src_k_pool), bs, _stream(stream)),
+        "pic_blocks_copy")
 
 
 def _host_i32(a, name):

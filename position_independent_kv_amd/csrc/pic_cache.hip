@@ -127,6 +127,32 @@ static int launch_cache_write_rotated(const void* k, const void* v, const int32_
   return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }
 
+// Whole-block copies between two pools, for moving position-free blocks
+// between GPU memory and pinned host memory (MiniPIC §3, contribution 5:
+// unrotated blocks move between GPU and host with no position bookkeeping).
+// Either pool may live in device memory or in pinned host memory that the
+// device can address.  One thread per 16 bytes of a block: the (K, V) bytes of
+// block src_ids[i] of the source go to block dst_ids[i] of the destination;
+// K and V of one block are each hkv * B * d contiguous elements, so the copy
+// is a contiguous 16-byte stream per block pair.  Pairs with an id out of
+// range are skipped.
+__global__ void __launch_bounds__(256) blocks_copy_kernel(
+    const uint4* __restrict__ src_k, const uint4* __restrict__ src_v,
+    const int32_t* __restrict__ src_ids, uint4* __restrict__ dst_k, uint4* __restrict__ dst_v,
+    const int32_t* __restrict__ dst_ids, long long n_pairs, long long chunks_per_block,
+    int num_src, int num_dst) {
+  const long long n = n_pairs * chunks_per_block;
+  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < n;
+       idx += (long long)gridDim.x * 256) {
+    const long long i = idx / chunks_per_block;
+    const long long c = idx % chunks_per_block;
+    const int sb = src_ids[i], db = dst_ids[i];
+    if (sb < 0 || sb >= num_src || db < 0 || db >= num_dst) continue;
+    dst_k[(long long)db * chunks_per_block + c] = src_k[(long long)sb * chunks_per_block + c];
+    dst_v[(long long)db * chunks_per_block + c] = src_v[(long long)sb * chunks_per_block + c];
+  }
+}
+
 }  // namespace pic
 
 extern "C" int pic_cache_write(const void* k, const void* v, const int32_t* slot_mapping,
@@ -171,4 +197,29 @@ extern "C" int pic_cache_write_rotated(const void* k, const void* v, const int32
   return pic::launch_cache_write_rotated<float>(k, v, slot_mapping, positions, cos_tab, sin_tab,
                                                 max_pos, num_tokens, num_kv_heads, head_dim,
                                                 k_pool, v_pool, num_slots, s);
+}
+
+extern "C" int pic_blocks_copy(const void* src_k_pool, const void* src_v_pool,
+                               const int32_t* src_blocks, int num_src_blocks, void* dst_k_pool,
+                               void* dst_v_pool, const int32_t* dst_blocks, int num_dst_blocks,
+                               int num_pairs, int num_kv_heads, int head_dim, int dtype,
+                               int block_size, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || num_src_blocks < 0 || num_dst_blocks < 0)
+    return PIC_EINVAL;
+  if (dtype != PIC_F32 && dtype != PIC_BF16) return PIC_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PIC_EUNSUPPORTED;
+  if (block_size != pic::kBlockSize) return PIC_EUNSUPPORTED;
+  if (num_pairs == 0) return PIC_OK;
+  if (!src_k_pool || !src_v_pool || !src_blocks || !dst_k_pool || !dst_v_pool || !dst_blocks)
+    return PIC_EINVAL;
+  const long long elem = dtype == PIC_BF16 ? 2 : 4;
+  const long long chunks = (long long)num_kv_heads * block_size * head_dim * elem / 16;
+  const long long n = (long long)num_pairs * chunks;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pic::blocks_copy_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     (hipStream_t)stream, (const uint4*)src_k_pool, (const uint4*)src_v_pool,
+                     src_blocks, (uint4*)dst_k_pool, (uint4*)dst_v_pool, dst_blocks,
+                     (long long)num_pairs, chunks, num_src_blocks, num_dst_blocks);
+  return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }

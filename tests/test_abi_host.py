@@ -28,7 +28,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = pic.library()
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(pic.EXPORTS)
@@ -114,6 +114,19 @@ def test_entry_points_reject_bad_arguments_before_launch():
     pargs[24] = buf
     pargs[25] = 1 << 40
     assert lib.pic_attn_prefill(*pargs) == pic.PIC_EINVAL
+
+
+def test_blocks_copy_rejects_bad_arguments_before_launch():
+    lib = pic.library()
+    buf = ctypes.c_void_p(1)  # never dereferenced: rejected before launch
+    f = lib.pic_blocks_copy
+    assert f(None, None, None, 4, None, None, None, 4, 0, 8, 128, 1, 16, None) == pic.PIC_OK
+    assert f(buf, buf, None, 4, buf, buf, buf, 4, 3, 8, 128, 1, 16, None) == pic.PIC_EINVAL
+    assert f(buf, buf, buf, 4, buf, buf, buf, 4, -1, 8, 128, 1, 16, None) == pic.PIC_EINVAL
+    assert f(buf, buf, buf, -4, buf, buf, buf, 4, 3, 8, 128, 1, 16, None) == pic.PIC_EINVAL
+    assert f(buf, buf, buf, 4, buf, buf, buf, 4, 3, 8, 96, 1, 16, None) == pic.PIC_EUNSUPPORTED
+    assert f(buf, buf, buf, 4, buf, buf, buf, 4, 3, 8, 128, 5, 16, None) == pic.PIC_EUNSUPPORTED
+    assert f(buf, buf, buf, 4, buf, buf, buf, 4, 3, 8, 128, 1, 32, None) == pic.PIC_EUNSUPPORTED
 
 
 def test_rotated_cache_entry_points_reject_bad_arguments_before_launch():
