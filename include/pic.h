@@ -154,7 +154,8 @@ int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool, con
  * ongoing decodes in the same batch).  Request r owns query rows
  * cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1 of q; query row i of the request
  * (0-based) sits at position q_pos[cu_seqlens_q[r] + i] and sees key slots
- * j <= seq_lens[r] - q_len + i.  Other arguments as in pic_attn_decode.
+ * j <= seq_lens[r] - q_len + i.  max_q_len must be >= every q_len (a
+ * precondition, like the others).  Other arguments as in pic_attn_decode.
  * A small planner kernel builds the work list in the workspace first.
  *   q, out   [total_q][Hq][head_dim]
  *   workspace >= pic_attn_workspace_size(num_reqs, total_q, max_seq_len, ...)

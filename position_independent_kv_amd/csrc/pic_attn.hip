@@ -1500,7 +1500,11 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
                      w.max_items, (int4*)(ws + w.items_off), (int*)(ws + w.count_off));
   hipLaunchKernelGGL((mixed_kernel<T, D, ROT>), dim3((unsigned)w.max_items),
                      dim3(64 * mixed_waves<T>()), 0, s, a);
-  launch_combine<T, D>(a, s);
+  // Every request has q_len >= total_q - (num_reqs - 1) * max_q_len; when that
+  // bound is at least 2 the batch has no decode rows and nothing to merge.
+  const long long min_q_len =
+      (long long)h.total_q - (long long)(h.num_reqs - 1) * h.max_q_len;
+  if (min_q_len < 2) launch_combine<T, D>(a, s);
   return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }
 

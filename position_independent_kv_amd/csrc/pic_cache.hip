@@ -15,12 +15,13 @@
 
 namespace pic {
 
-// One thread per (token, head, 16-byte chunk of the row): the K chunk is one
-// 16-byte store into the token's row; the V chunk's elements go to
-// consecutive d rows of the block, each at the token's offset.  Consecutive
-// threads take consecutive chunks, so a K row is written by neighbouring
-// lanes, and tokens that fill one block write neighbouring bytes of each V
-// row.
+// One workgroup per (group of 16 consecutive input tokens, head).  K: each
+// token's row is one contiguous run in the pool; thread t copies 16 bytes of
+// it.  V: when the group's 16 slots are offsets 0..15 of one block (a block
+// filled in order, the usual prefill case), the group is transposed on the
+// way: thread t gathers 8 consecutive keys of d row t/2 and writes them as
+// one contiguous run of the block's V^T row; otherwise every element goes to
+// its own place.  Tokens whose slot is negative or past the pool are skipped.
 template <typename T>
 __global__ void __launch_bounds__(256) cache_write_kernel(const T* __restrict__ k,
                                                           const T* __restrict__ v,
@@ -30,35 +31,72 @@ __global__ void __launch_bounds__(256) cache_write_kernel(const T* __restrict__ 
                                                           T* __restrict__ v_pool,
                                                           long long num_slots) {
   constexpr int VEC = 16 / sizeof(T);
-  const int chunks = head_dim / VEC;
-  const long long n = num_tokens * hkv * chunks;
-  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < n;
-       idx += (long long)gridDim.x * 256) {
-    const int c = (int)(idx % chunks);
-    const long long th = idx / chunks;  // token * hkv + head
-    const int h = (int)(th % hkv);
-    const long long t = th / hkv;
-    const long long slot = slots[t];
-    if (slot < 0 || slot >= num_slots) continue;
-    const long long blk = slot / kBlockSize;
-    const int off = (int)(slot % kBlockSize);
-    const uint4 xk = *reinterpret_cast<const uint4*>(k + th * head_dim + c * VEC);
-    const uint4 xv = *reinterpret_cast<const uint4*>(v + th * head_dim + c * VEC);
-    *reinterpret_cast<uint4*>(k_pool + ((blk * hkv + h) * kBlockSize + off) * head_dim +
-                              c * VEC) = xk;
-    T* dst = v_pool + ((blk * hkv + h) * head_dim + c * VEC) * kBlockSize + off;
-    const T* xs = reinterpret_cast<const T*>(&xv);
+  constexpr int HALF = kBlockSize / 2;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const long long groups = (num_tokens + kBlockSize - 1) / kBlockSize;
+  const long long nwork = groups * hkv;
+  for (long long wk = blockIdx.x; wk < nwork; wk += gridDim.x) {
+    const int h = (int)(wk % hkv);
+    const long long t0 = (wk / hkv) * kBlockSize;
+    const int nt = (int)min((long long)kBlockSize, num_tokens - t0);
+    // every wave reads the group's slots (lane % 16) and decides the path itself
+    const int j = lane & 15;
+    const long long my_slot = j < nt ? (long long)slots[t0 + j] : -1;
+    const long long slot0 = __shfl(my_slot, 0);
+    const bool in_order = nt == kBlockSize && slot0 >= 0 && slot0 % kBlockSize == 0 &&
+                          slot0 + kBlockSize <= num_slots && my_slot == slot0 + j;
+    const bool aligned = __all(in_order);
+    // K: chunk c of token jj; every lane runs the same trip count so that the
+    // shuffle always finds its source lane active
+    const int chunks = head_dim / VEC;
+    for (int e0 = 0; e0 < nt * chunks; e0 += 256) {
+      const int e = e0 + tid;
+      const int jj = min(e / chunks, kBlockSize - 1), c = e % chunks;
+      const long long sl = __shfl(my_slot, jj);
+      if (e >= nt * chunks || sl < 0 || sl >= num_slots) continue;
+      const long long blk = sl / kBlockSize;
+      const int off = (int)(sl % kBlockSize);
+      const uint4 x = *reinterpret_cast<const uint4*>(k + ((t0 + jj) * hkv + h) * head_dim +
+                                                      c * VEC);
+      *reinterpret_cast<uint4*>(k_pool + ((blk * hkv + h) * kBlockSize + off) * head_dim +
+                                c * VEC) = x;
+    }
+    if (aligned) {
+      const int d = tid >> 1, k0 = (tid & 1) * HALF;
+      if (d < head_dim) {
+        T run[HALF];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) dst[j * kBlockSize] = xs[j];
+        for (int q = 0; q < HALF; ++q) run[q] = v[((t0 + k0 + q) * hkv + h) * head_dim + d];
+        T* dst = v_pool + (((slot0 / kBlockSize) * hkv + h) * (long long)head_dim + d) *
+                              kBlockSize + k0;
+#pragma unroll
+        for (int q = 0; q < HALF; q += VEC)
+          *reinterpret_cast<uint4*>(dst + q) = *reinterpret_cast<const uint4*>(&run[q]);
+      }
+    } else {  // chunk c of token jj: one 16-byte load, VEC scattered element stores
+      for (int e0 = 0; e0 < nt * chunks; e0 += 256) {
+        const int e = e0 + tid;
+        const int jj = min(e / chunks, kBlockSize - 1), c = e % chunks;
+        const long long sl = __shfl(my_slot, jj);
+        if (e >= nt * chunks || sl < 0 || sl >= num_slots) continue;
+        const long long blk = sl / kBlockSize;
+        const int off = (int)(sl % kBlockSize);
+        const uint4 x = *reinterpret_cast<const uint4*>(v + ((t0 + jj) * hkv + h) * head_dim +
+                                                        c * VEC);
+        const T* xs = reinterpret_cast<const T*>(&x);
+        T* dst = v_pool + ((blk * hkv + h) * head_dim + c * VEC) * kBlockSize + off;
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) dst[q * kBlockSize] = xs[q];
+      }
+    }
   }
 }
 
 template <typename T>
 static int launch_cache_write(const void* k, const void* v, const int32_t* slots, int n, int hkv,
                               int d, void* kp, void* vp, long long num_slots, hipStream_t s) {
-  constexpr int VEC = 16 / sizeof(T);
-  const long long nt = (long long)n * hkv * (d / VEC);
-  long long blocks = (nt + 255) / 256;
+  long long blocks = ((long long)n + kBlockSize - 1) / kBlockSize * hkv;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(cache_write_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, s, (const T*)k,
                      (const T*)v, slots, (long long)n, hkv, d, (T*)kp, (T*)vp, num_slots);

@@ -85,6 +85,58 @@ def test_cache_write_readback_bit_exact(name):
                 assert np.all(np.isnan(dw.v_pool[b, :, :, o].float().cpu().numpy()))
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_cache_write_slot_patterns(dtype, d):
+    """Whole blocks filled in order (the transposing fast path), a run of 16 that is not
+    block aligned, a reversed block, skipped and out-of-range slots and a ragged tail:
+    the pools hold exactly the oracle placement, everything else keeps its NaN fill."""
+    torch = _torch()
+    hkv, nb, B = 3, 12, 16
+    slots = np.concatenate([
+        np.arange(2 * B, 4 * B),                 # blocks 2, 3 in order
+        np.arange(5 * B + 3, 6 * B + 3),         # 16 consecutive slots across blocks 5/6
+        np.arange(8 * B, 9 * B)[::-1],           # block 8 reversed
+        [-1, 4 * B + 2, nb * B + 7, 4 * B + 9],  # skip, scattered, out of range, scattered
+        np.arange(10 * B, 10 * B + 5),           # ragged tail
+    ]).astype(np.int32)
+    T = slots.shape[0]
+    rng = np.random.default_rng(2)
+    kx = rng.standard_normal((T, hkv, d), dtype=np.float32)
+    vx = rng.standard_normal((T, hkv, d), dtype=np.float32)
+    if dtype == "bf16":
+        from workloads import f32_to_bf16_bits
+        kx, vx = f32_to_bf16_bits(kx), f32_to_bf16_bits(vx)
+        tdt = torch.bfloat16
+        to_t = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        tdt = torch.float32
+        to_t = lambda a: torch.from_numpy(a).cuda()
+        bits = lambda t: t.cpu().numpy().view(np.uint32)
+    kp = torch.full((nb, hkv, B, d), float("nan"), dtype=tdt, device="cuda")
+    vp = torch.full((nb, hkv, d, B), float("nan"), dtype=tdt, device="cuda")
+    pic.pic_cache_write(to_t(kx), to_t(vx), torch.from_numpy(slots).cuda(), kp, vp)
+    torch.cuda.synchronize()
+    sdt = np.uint16 if dtype == "bf16" else np.float32
+    ok_k = np.zeros((nb, hkv, B, d), sdt)
+    ok_v = np.zeros((nb, hkv, d, B), sdt)
+    inside = np.where(slots < nb * B, slots, -1)
+    oracle.place_tokens(kx, vx, inside, ok_k, ok_v, B)
+    written = np.zeros(nb * B, bool)
+    written[inside[inside >= 0]] = True
+    gk, gv = bits(kp), bits(vp)
+    wk_ = ok_k.view(np.uint16 if dtype == "bf16" else np.uint32)
+    wv_ = ok_v.view(np.uint16 if dtype == "bf16" else np.uint32)
+    for b in range(nb):
+        for o in range(B):
+            if written[b * B + o]:
+                assert np.array_equal(gk[b, :, o, :], wk_[b, :, o, :]), (b, o)
+                assert np.array_equal(gv[b, :, :, o], wv_[b, :, :, o]), (b, o)
+            else:
+                assert np.all(np.isnan(kp[b, :, o, :].float().cpu().numpy())), (b, o)
+                assert np.all(np.isnan(vp[b, :, :, o].float().cpu().numpy())), (b, o)
+
+
 # ---------------------------------------------------------------------------
 # the tiny fp32 config: one span shared at logical offsets 0 and 2048
 # ---------------------------------------------------------------------------
