@@ -750,19 +750,22 @@ __device__ __forceinline__ void sched_phase() {
   }
 }
 
-// Order of one prefill step: score MFMAs with softmax work, PV MFMAs with
-// staging work.
+// Order of one prefill step of NBLK 32-key blocks: score MFMAs with softmax
+// work, PV MFMAs with staging work.
+template <int NBLK>
 __device__ __forceinline__ void sched_interleave() {
-  sched_phase<2, 6>();
-  sched_phase<1, 5>();
-  sched_phase<2, 6>();
-  sched_phase<1, 5>();
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) {
+    sched_phase<2, 6>();
+    sched_phase<1, 5>();
+  }
 }
 
-template <int D, int NW>
+template <int D, int NW, int KS>
 struct Pf {
   static constexpr int NTH = NW * 64;              // threads
-  static constexpr int KSTEP = 64;                 // keys per step (two 32-key blocks)
+  static constexpr int KSTEP = KS;                 // keys per step
+  static constexpr int NBLK = KS / 32;             // 32-key blocks per step
   static constexpr int ROWS = NW * 32;             // query rows per tile
   static constexpr int NCH = D / 16;               // 16-wide d chunks (MFMA K)
   static constexpr int NHC = NCH / 2;              // chunks of the first half of d
@@ -800,10 +803,10 @@ struct Pf {
 // One barrier per step.  The rotated query rows (the B operand, pre-scaled
 // by log2(e)/sqrt(d) so scores come out in base-2 units) sit in a per-wave
 // LDS slice.  Steps that lie wholly below the causal diagonal skip the mask.
-template <int D, int NW, bool ROT>
+template <int D, int NW, int KS, bool ROT>
 __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
                                   unsigned char* smem) {
-  using P = Pf<D, NW>;
+  using P = Pf<D, NW, KS>;
   typedef Mma32::Op Op;
   typedef Mma32::Acc Acc;
   const int tid = threadIdx.x;
@@ -1036,7 +1039,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
       kmeta((j + 3) * P::KSTEP);
       kload();
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < P::NBLK; ++h) {
         Acc sc = qk_block(j, h, zero);
         if (j >= jfull) mask_block(sc, j * P::KSTEP + h * 32);
         mx = fmaxf(mx, col_max(sc));
@@ -1124,9 +1127,9 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
       }
     }
 
-    // step j: blocks (j, 0) and (j, 1); the score MFMAs of the next block run
-    // while a block is exponentiated, the PV MFMAs of a block while the next
-    // data is staged.  Stages K j+2 and V j+1.
+    // step j: blocks (j, 0) .. (j, NBLK-1); the score MFMAs of the next block
+    // run while a block is exponentiated, the PV MFMAs of a block while the
+    // next data is staged.  Stages K j+2 and V j+1.
     auto step = [&](int j, auto mask_tag) {
       constexpr bool MASKED = decltype(mask_tag)::value;
       const int kb = j * P::KSTEP;
@@ -1139,17 +1142,14 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
       // keep the loads at the top of the step: they have the whole step to land
       __builtin_amdgcn_sched_barrier(0);
 
-      Acc s_cur = s_next;
-      if constexpr (MASKED) mask_block(s_cur, kb);
-      s_next = qk_block(j, 1, negm);
-      softmax_block(s_cur);
-      pv_block(j, 0);
-
-      s_cur = s_next;
-      if constexpr (MASKED) mask_block(s_cur, kb + 32);
-      s_next = qk_block(j + 1, 0, negm);
-      softmax_block(s_cur);
-      pv_block(j, 1);
+#pragma unroll
+      for (int h = 0; h < P::NBLK; ++h) {
+        Acc s_cur = s_next;
+        if constexpr (MASKED) mask_block(s_cur, kb + 32 * h);
+        s_next = h + 1 < P::NBLK ? qk_block(j, h + 1, negm) : qk_block(j + 1, 0, negm);
+        softmax_block(s_cur);
+        pv_block(j, h);
+      }
 
       kstore(j + 2);
       vstore(j + 1);
@@ -1158,7 +1158,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
       // behind it): each score MFMA of the next block is followed by a slice
       // of the current block's softmax, each PV MFMA by a slice of the
       // staging work.
-      sched_interleave();
+      sched_interleave<P::NBLK>();
       __syncthreads();
     };
     for (int j = 0; j < jfull; ++j) step(j, std::false_type{});
@@ -1242,20 +1242,28 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
 // holds 256 query rows and each staged (rotated) K step feeds twice the MFMA
 // work of a four-wave tile; a decode item then covers eight kv heads.  fp32
 // keeps four-wave workgroups.
+constexpr int kMixedWavesBf16 = 8;
+// Keys per staged step of the bf16 prefill tile.  (Measured alternative:
+// four-wave workgroups with 32-key steps fit two workgroups per CU in 80 KB of
+// LDS each, so prefill tiles and decode chunks can share a CU; it was slower
+// on both the chunked prefill (454 vs 385 us) and the mixed batch (1395 vs
+// 1316 us).)
+constexpr int kPrefillStep = 64;
+
 template <typename T>
 constexpr int mixed_waves() {
-  return sizeof(T) == 2 ? 8 : kWaves;
+  return sizeof(T) == 2 ? kMixedWavesBf16 : kWaves;
 }
 
 template <typename T, int D>
 constexpr int prefill_rows() {
-  return sizeof(T) == 2 ? Pf<D, mixed_waves<T>()>::ROWS : kPrefillRows;
+  return sizeof(T) == 2 ? Pf<D, mixed_waves<T>(), kPrefillStep>::ROWS : kPrefillRows;
 }
 
 template <typename T, int D>
 struct MixedSmem {
   static constexpr int PB =
-      sizeof(T) == 2 ? Pf<D, mixed_waves<T>()>::BYTES : PrefillSmem<T, D>::BYTES;
+      sizeof(T) == 2 ? Pf<D, mixed_waves<T>(), kPrefillStep>::BYTES : PrefillSmem<T, D>::BYTES;
   static constexpr int BYTES = PB > (int)sizeof(DecodeSmem<T, D>) ? PB : (int)sizeof(DecodeSmem<T, D>);
 };
 
@@ -1269,7 +1277,7 @@ __global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
   const int4 it = a.items[blockIdx.x];
   if (it.x == kItemPrefill) {
     if constexpr (sizeof(T) == 2) {
-      prefill_tile_bf16<D, NW, ROT>(a, it.y, it.z, it.w, smem);
+      prefill_tile_bf16<D, NW, kPrefillStep, ROT>(a, it.y, it.z, it.w, smem);
     } else {
       static_assert(ROT, "fp32 prefill tiles always rotate");
       prefill_tile<T, D>(a, it.y, it.z, it.w, smem);
