@@ -307,9 +307,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the per-GPU path is what one GPU can show; sharding is described in DESIGN.md)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path "
+              "shards by request and kv head with no exchange, so one GPU's share is what is "
+              "measured)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -15,7 +15,7 @@ Follows "MiniPIC: Flexible Position-Independent Caching in <100LOC", §2.1
   which is exactly what this module computes, densely and without any online
   softmax, blocking or fusion.
 
-Readings where the page is silent (each one is listed in the design doc):
+Readings where the page is silent:
 
 * R_p is the rotate-half RoPE rotation: element i is paired with element
   i + d/2 and the pair is rotated by angle p * theta_i, with the standard

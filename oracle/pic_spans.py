@@ -11,7 +11,7 @@ Follows "MiniPIC: Flexible Position-Independent Caching in <100LOC", §2.2
   prompt, h_i = H(h_0, x_<=i), so a suffix block that depends on its context
   never matches a block computed under another context.
 
-Readings (listed in the design doc): a block without a special token chains on
+Readings where the page is silent: a block without a special token chains on
 its predecessor, h_i = H(h_{i-1}, x_i) with h_{-1} = h_0 (the usual prefix
 cache; the page's two formulas only make sense against it); x_<=i means
 every token of blocks 0..i of the prompt; only full blocks are hashed.
