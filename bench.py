@@ -95,8 +95,23 @@ def time_config(name, steps, warmup, with_rows=False):
     t1 = time.perf_counter()
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     step_ms = (t1 - t0) * 1e3 / steps
+    # cold: before each timed call the 256 MB Infinity Cache is refilled by
+    # reading a 512 MiB buffer, so nothing of the previous call is cached and
+    # no dirty line has to be written back during the call
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(max(3, steps // 5))]
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    for k, (a_, b_) in enumerate(cold):
+        sink += flush.sum()
+        a_.record(stream)
+        dw.attention()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    cold_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in cold]))
+    del flush, sink
     res = dict(name=name, w=w, counts=counts, step_ms=step_ms, kernel_ms=kern_ms,
-               step_bytes=step_counts(w, counts))
+               cold_kernel_ms=cold_ms, step_bytes=step_counts(w, counts))
     if with_rows:
         # the other rows of the path, timed on their own (same stream, events)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -200,6 +215,40 @@ def offload_bandwidth(n_blocks=4096, reps=5):
     del dk, dv, hk, hv
     torch.cuda.empty_cache()
     return res
+
+
+def ceilings():
+    """What this machine delivers to plain library code: a 2 GiB device copy (bytes read +
+    written per second) and a large bf16 matrix product (torch.matmul, 8192^3)."""
+    import torch
+    x = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * x.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    c = a @ b
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    mm_tflops = 2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    log(f"[bench] ceilings: device copy {copy_gbps:.0f} GB/s, bf16 matmul {mm_tflops:.0f} TFLOP/s")
+    return {"device_copy_GBps": copy_gbps, "bf16_matmul_TFLOPs": mm_tflops,
+            "note": "2 GiB torch copy (read + write bytes), torch.matmul bf16 8192^3"}
 
 
 def block_table_build(reps=5):
@@ -343,6 +392,8 @@ def main():
     roof["traffic"] = tb
     roof["kernel"] = kernel
     roof["kernel_ms"] = main_res["kernel_ms"]
+    roof["cold_kernel_ms"] = main_res["cold_kernel_ms"]
+    roof["cold_frac"] = roof["frac"] * main_res["kernel_ms"] / main_res["cold_kernel_ms"]
     roof["algorithmic_bytes"] = counts["bytes"]
     roof["algorithmic_flops"] = counts["flops"]
 
@@ -354,7 +405,8 @@ def main():
         c = r["counts"]
         others[name] = {
             "workload": WORKLOAD_TEXT[name],
-            "kernel_ms": r["kernel_ms"], "step_ms": r["step_ms"],
+            "kernel_ms": r["kernel_ms"], "cold_kernel_ms": r["cold_kernel_ms"],
+            "step_ms": r["step_ms"],
             "kernel_GBps": c["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9,
             "kernel_hbm_frac": c["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "kernel_TFLOPs": c["flops"] / (r["kernel_ms"] * 1e-3) / 1e12,
@@ -369,6 +421,7 @@ def main():
     for name in [x for x in args.ablation.split(",") if x]:
         ablation[name] = rope_ablation(name)
     tables = block_table_build()
+    ceil = ceilings()
     offload = offload_bandwidth()
 
     cpu = None
@@ -403,6 +456,7 @@ def main():
         "configs": others,
         "rope_ablation": ablation,
         "block_tables": tables,
+        "ceilings": ceil,
         "offload": offload,
         "source_hash": source_hash(),
     }
