@@ -318,6 +318,89 @@ int pic_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* q_pos,
 int pic_decode_num_splits(int seq_len, int dtype);
 int pic_decode_split_len(int seq_len, int dtype);
 
+/*
+ * Interleaved span-prefill scheduling (host)
+ * ------------------------------------------
+ * MiniPIC §2 (the scheduling paragraph after §2.2, ISPS) and §3,
+ * contribution 4.  A scheduler object turns a trace of requests into engine
+ * steps; each step is ONE mixed batch for pic_cache_write + pic_attn_prefill.
+ *   PIC_SCHED_ISPS     every step mixes, under the token budget: one decode
+ *                      token of every decoding request, then final-prompt
+ *                      chunks, then span-prefill chunks;
+ *   PIC_SCHED_BARRIER  one kind per step: span prefills while any running
+ *                      request still waits for a span, else final prompts,
+ *                      else decodes (the barrier-separated baseline).
+ * Work model (tokens): a span is shared by id, a whole number of blocks, and
+ * prefilled once on its own (causal, positions 0..len-1, blocks reserved
+ * while any running request lists it); a request attends to its spans in
+ * the listed order, then its final prompt (causal), then output_len decode
+ * tokens, one per step.  Slot j of a request's composed sequence (spans'
+ * blocks, then private blocks) has logical position j.  Admission: first come
+ * first served by (arrival step, id), at most max_running at once, all of a
+ * request's blocks reserved on admission; resident spans no running request
+ * lists are evicted (least recently used first) when an admission needs
+ * their blocks.
+ * The scheduler is plain host memory created by pic_sched_create and freed by
+ * pic_sched_destroy (the one stateful object of the library); spans and
+ * requests are added before the first pic_sched_step.  Not thread-safe.
+ */
+typedef struct pic_sched pic_sched;
+
+enum { PIC_SCHED_ISPS = 0, PIC_SCHED_BARRIER = 1 };
+enum { PIC_SEQ_SPAN = 0, PIC_SEQ_PROMPT = 1, PIC_SEQ_DECODE = 2 };
+
+/*
+ * One step's batch.  The caller sets the capacities and points the arrays at
+ * HOST memory of at least that size; pic_sched_step fills them and the
+ * result fields.  Sequence i of the batch (a span chunk, a final-prompt
+ * chunk or a decode token) owns query rows cu_seqlens_q[i]..cu_seqlens_q[i+1]
+ * and key slots 0..seq_lens[i]-1; its new tokens are the query rows (the
+ * caller writes their K/V to slot_mapping before the attention call).
+ */
+typedef struct {
+  /* capacities (set by the caller) */
+  int max_seqs;             /* sequences per step (>= max_running + spans in flight) */
+  int max_rows;             /* query rows per step (>= token_budget) */
+  long long max_keys;       /* sum of seq_lens per step */
+  int block_table_stride;   /* >= blocks of the longest composed sequence */
+  /* host arrays (caller-allocated) */
+  int32_t* cu_seqlens_q;    /* [max_seqs + 1] */
+  int32_t* q_pos;           /* [max_rows]   logical position of each query row */
+  int32_t* slot_mapping;    /* [max_rows]   cache slot of each query row's token */
+  int32_t* seq_lens;        /* [max_seqs] */
+  int32_t* cu_seqlens_k;    /* [max_seqs + 1] */
+  int32_t* k_pos;           /* [max_keys]   pi(j) = j of every sequence */
+  int32_t* block_table;     /* [max_seqs][block_table_stride], unused entries 0 */
+  int32_t* seq_kind;        /* [max_seqs]   PIC_SEQ_* */
+  int32_t* seq_id;          /* [max_seqs]   span id or request id */
+  int32_t* q_begin;         /* [max_seqs]   slot index of the sequence's first query row */
+  /* results (written by pic_sched_step) */
+  long long step;           /* index of this step (steps with no work count too) */
+  int num_seqs, total_q, max_q_len, max_seq_len;
+  long long total_keys;
+  int num_finished;         /* requests that finished with this step */
+} pic_sched_batch;
+
+/* token_budget: query rows per step; block_size must be 16.  PIC_EINVAL for
+ * an unknown policy or non-positive sizes. */
+int pic_sched_create(int policy, int token_budget, int max_running, int num_blocks,
+                     int block_size, pic_sched** sched);
+void pic_sched_destroy(pic_sched* sched);
+/* Returns the new span's id (0, 1, ...) or PIC_EINVAL (length not a positive
+ * multiple of the block size, or stepping has started). */
+int pic_sched_add_span(pic_sched* sched, int length);
+/* Returns the new request's id (0, 1, ...) or PIC_EINVAL (unknown span id,
+ * negative sizes, no span and no prompt, more blocks than the whole pool,
+ * or stepping has started).  The request may be scheduled from step
+ * arrival_step on. */
+int pic_sched_add_request(pic_sched* sched, long long arrival_step, const int32_t* span_ids,
+                          int num_spans, int prompt_len, int output_len);
+/* Builds the next step into *batch: returns 1 (a step; num_seqs == 0 when no
+ * admitted work exists yet at this step), 0 when every request has
+ * finished, or PIC_EINVAL (null or too small arrays; the scheduler's state is
+ * then unchanged, so the call can be repeated with larger arrays). */
+int pic_sched_step(pic_sched* sched, pic_sched_batch* batch);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,8 +32,11 @@ EXPORTS = [
     "pic_attn_workspace_size", "pic_attn_decode", "pic_attn_prefill", "pic_validate_metadata",
     "pic_decode_num_splits", "pic_decode_split_len", "pic_cache_write_rotated",
     "pic_attn_decode_rotated", "pic_attn_prefill_rotated", "pic_block_hashes",
-    "pic_build_block_tables", "pic_blocks_copy",
+    "pic_build_block_tables", "pic_blocks_copy", "pic_sched_create", "pic_sched_destroy",
+    "pic_sched_add_span", "pic_sched_add_request", "pic_sched_step",
 ]
+PIC_SCHED_ISPS, PIC_SCHED_BARRIER = 0, 1
+PIC_SEQ_SPAN, PIC_SEQ_PROMPT, PIC_SEQ_DECODE = 0, 1, 2
 
 
 class PicError(RuntimeError):
@@ -44,6 +47,20 @@ class PicError(RuntimeError):
 
 class PicLibraryMissing(RuntimeError):
     pass
+
+
+class _SchedBatch(ctypes.Structure):
+    """pic_sched_batch (include/pic.h), field for field."""
+    _fields_ = [
+        ("max_seqs", ctypes.c_int), ("max_rows", ctypes.c_int), ("max_keys", ctypes.c_longlong),
+        ("block_table_stride", ctypes.c_int),
+        *[(n, ctypes.c_void_p) for n in ("cu_seqlens_q", "q_pos", "slot_mapping", "seq_lens",
+                                         "cu_seqlens_k", "k_pos", "block_table", "seq_kind",
+                                         "seq_id", "q_begin")],
+        ("step", ctypes.c_longlong), ("num_seqs", ctypes.c_int), ("total_q", ctypes.c_int),
+        ("max_q_len", ctypes.c_int), ("max_seq_len", ctypes.c_int),
+        ("total_keys", ctypes.c_longlong), ("num_finished", ctypes.c_int),
+    ]
 
 
 _lib = None
@@ -86,6 +103,12 @@ def _load():
                                             c_void])
     lib.pic_blocks_copy.argtypes = ([c_void] * 3 + [c_int] + [c_void] * 3 + [c_int] * 6
                                     + [c_void])
+    lib.pic_sched_create.argtypes = [c_int] * 5 + [ctypes.POINTER(c_void)]
+    lib.pic_sched_destroy.restype = None
+    lib.pic_sched_destroy.argtypes = [c_void]
+    lib.pic_sched_add_span.argtypes = [c_void, c_int]
+    lib.pic_sched_add_request.argtypes = [c_void, ctypes.c_longlong, c_void, c_int, c_int, c_int]
+    lib.pic_sched_step.argtypes = [c_void, ctypes.POINTER(_SchedBatch)]
     lib.pic_decode_num_splits.argtypes = [c_int, c_int]
     lib.pic_decode_split_len.argtypes = [c_int, c_int]
     for name in EXPORTS:
@@ -418,6 +441,89 @@ def pic_build_block_tables(tokens, cu_seqlens, block_size: int = BLOCK_SIZE,
     nh = int((lens // block_size).sum()) if R else 0
     return dict(block_table=bt[:R], k_pos=k_pos[:total], slot_mapping=slots[:total],
                 block_hashes=hashes[:nh], num_new_blocks=int(nnew.value))
+
+
+def pic_sched_create(policy: int, token_budget: int, max_running: int, num_blocks: int,
+                     block_size: int = BLOCK_SIZE) -> int:
+    """A scheduler handle (see pic.h: interleaved span-prefill scheduling)."""
+    h = ctypes.c_void_p()
+    _check(_load().pic_sched_create(policy, token_budget, max_running, num_blocks, block_size,
+                                    ctypes.byref(h)), "pic_sched_create")
+    return h.value
+
+
+def pic_sched_destroy(handle) -> None:
+    if handle:
+        _load().pic_sched_destroy(handle)
+
+
+def pic_sched_add_span(handle, length: int) -> int:
+    sid = _load().pic_sched_add_span(handle, length)
+    if sid < 0:
+        _check(sid, "pic_sched_add_span")
+    return sid
+
+
+def pic_sched_add_request(handle, arrival_step: int, span_ids, prompt_len: int,
+                          output_len: int) -> int:
+    ids = _host_i32(np.asarray(span_ids, dtype=np.int32).reshape(-1), "span_ids")
+    rid = _load().pic_sched_add_request(handle, arrival_step, ids.ctypes.data if ids.size else None,
+                                        ids.shape[0], prompt_len, output_len)
+    if rid < 0:
+        _check(rid, "pic_sched_add_request")
+    return rid
+
+
+def pic_sched_step(handle, max_seqs: int, max_rows: int, max_keys: int, block_table_stride: int):
+    """The next step's batch as a dict of host int32 arrays, or None when every request is done."""
+    a = dict(cu_seqlens_q=np.zeros(max_seqs + 1, np.int32), q_pos=np.zeros(max_rows, np.int32),
+             slot_mapping=np.zeros(max_rows, np.int32), seq_lens=np.zeros(max_seqs, np.int32),
+             cu_seqlens_k=np.zeros(max_seqs + 1, np.int32), k_pos=np.zeros(max_keys, np.int32),
+             block_table=np.zeros((max_seqs, block_table_stride), np.int32),
+             seq_kind=np.zeros(max_seqs, np.int32), seq_id=np.zeros(max_seqs, np.int32),
+             q_begin=np.zeros(max_seqs, np.int32))
+    b = _SchedBatch(max_seqs=max_seqs, max_rows=max_rows, max_keys=max_keys,
+                    block_table_stride=block_table_stride,
+                    **{k: v.ctypes.data for k, v in a.items()})
+    st = _load().pic_sched_step(handle, ctypes.byref(b))
+    if st < 0:
+        _check(st, "pic_sched_step")
+    if st == 0:
+        return None
+    n, tq, tk = b.num_seqs, b.total_q, b.total_keys
+    return dict(step=b.step, num_seqs=n, total_q=tq, max_q_len=b.max_q_len,
+                max_seq_len=b.max_seq_len, total_keys=tk, num_finished=b.num_finished,
+                cu_seqlens_q=a["cu_seqlens_q"][:n + 1], q_pos=a["q_pos"][:tq],
+                slot_mapping=a["slot_mapping"][:tq], seq_lens=a["seq_lens"][:n],
+                cu_seqlens_k=a["cu_seqlens_k"][:n + 1], k_pos=a["k_pos"][:tk],
+                block_table=a["block_table"][:n], seq_kind=a["seq_kind"][:n],
+                seq_id=a["seq_id"][:n], q_begin=a["q_begin"][:n])
+
+
+class Scheduler:
+    """Owns a pic_sched handle: spans and requests are added, then steps drawn until None."""
+
+    def __init__(self, policy: int, token_budget: int, max_running: int, num_blocks: int,
+                 max_seqs: int, max_keys: int, block_table_stride: int):
+        self.handle = pic_sched_create(policy, token_budget, max_running, num_blocks)
+        self.caps = (max_seqs, token_budget, max_keys, block_table_stride)
+
+    def add_span(self, length: int) -> int:
+        return pic_sched_add_span(self.handle, length)
+
+    def add_request(self, arrival_step: int, span_ids, prompt_len: int, output_len: int) -> int:
+        return pic_sched_add_request(self.handle, arrival_step, span_ids, prompt_len, output_len)
+
+    def step(self):
+        return pic_sched_step(self.handle, *self.caps)
+
+    def close(self):
+        pic_sched_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            self.close()
 
 
 def pic_decode_num_splits(seq_len: int, dtype: int = PIC_BF16) -> int:

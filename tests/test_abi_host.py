@@ -22,13 +22,13 @@ HEADER = os.path.join(ROOT, "include", "pic.h")
 
 def _declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(pic_\w+)\(", src, re.M)))
+    return sorted(set(re.findall(r"^(?:int|void|size_t|const char\*)\s+(pic_\w+)\(", src, re.M)))
 
 
 def test_library_exports_every_declared_symbol():
     lib = pic.library()
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(pic.EXPORTS)
@@ -245,13 +245,40 @@ int main() {
   if (nnew <= 0 || nnew > 9) ++fails;
   if (pic_build_block_tables(tok, cu2, 3, 16, 5001, 5002, 7, 0, 2, bt2, 4, kp2, sm2, NULL,
                              &nnew) == 0) ++fails;  // pool too small
+  // scheduler: both policies over a trace with sharing, late arrivals and eviction
+  for (int policy = 0; policy < 2; ++policy) {
+    pic_sched* sc = NULL;
+    if (pic_sched_create(policy, 40, 3, 24, 16, &sc) != 0 || !sc) { ++fails; continue; }
+    for (int i = 0; i < 5; ++i) if (pic_sched_add_span(sc, 16 * (1 + i % 3)) != i) ++fails;
+    if (pic_sched_add_span(sc, 20) >= 0) ++fails;
+    for (int r = 0; r < 12; ++r) {
+      int ids[3] = {r % 5, (r + 2) % 5, (r + 3) % 5};
+      if (pic_sched_add_request(sc, r / 2, ids, 1 + r % 3, 5 + r, r % 4) != r) ++fails;
+    }
+    int cq[33], qp[64], sm[64], sl[32], ck[33], kp[4096], btab[32 * 16], kind[32], sid[32], qb[32];
+    pic_sched_batch b;
+    memset(&b, 0, sizeof b);
+    b.max_seqs = 32; b.max_rows = 64; b.max_keys = 4096; b.block_table_stride = 16;
+    b.cu_seqlens_q = cq; b.q_pos = qp; b.slot_mapping = sm; b.seq_lens = sl; b.cu_seqlens_k = ck;
+    b.k_pos = kp; b.block_table = btab; b.seq_kind = kind; b.seq_id = sid; b.q_begin = qb;
+    int st, steps = 0, done = 0;
+    while ((st = pic_sched_step(sc, &b)) == 1 && steps < 10000) {
+      ++steps;
+      done += b.num_finished;
+      if (b.total_q > 40 || b.cu_seqlens_q[b.num_seqs] != b.total_q) ++fails;
+    }
+    if (st != 0 || done != 12) ++fails;
+    b.max_rows = 0;
+    if (pic_sched_step(sc, &b) != 0) ++fails;  // finished: no arrays needed
+    pic_sched_destroy(sc);
+  }
   printf("fails=%d\n", fails);
   return fails;
 }
 ''')
     exe = tmp_path / "host_test"
     csrc = os.path.join(ROOT, "position_independent_kv_amd", "csrc")
-    srcs = [os.path.join(csrc, "pic_host.cpp"), os.path.join(csrc, "pic_spans.cpp")]
+    srcs = [os.path.join(csrc, n) for n in ("pic_host.cpp", "pic_spans.cpp", "pic_sched.cpp")]
     cmd = [gxx, "-std=c++17", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-I", os.path.join(ROOT, "include"), *srcs, str(main), "-o", str(exe)]
     subprocess.run(cmd, check=True)
