@@ -217,6 +217,50 @@ def offload_bandwidth(n_blocks=4096, reps=5):
     return res
 
 
+def scheduled_trace(budget=8192, max_running=32, num_blocks=8192, reps=3):
+    """Interleaved span-prefill scheduling vs the barrier-separated policy on the RAG trace
+    (64 requests in waves of 8, each 4 of 64 shared 1024-token spans + a 256-token final
+    prompt + 32 output tokens): the library's scheduler builds every step's mixed batch,
+    then each step is one cache write + one mixed attention launch.  Token values are drawn
+    on the device.  Reports the attention-layer time of the whole trace (median of `reps`
+    replays, HIP events around all steps) and the number of engine steps; a model's other
+    layers (weights read once per step) are not part of this path."""
+    import torch
+
+    import position_independent_kv_amd as pic
+    from tests.gpu_harness import TraceRun
+    from workloads import RAG_TRACE, make_trace
+
+    trace = make_trace(**{**RAG_TRACE, "values": False})
+    res = {"trace": trace.description, "token_budget": budget, "max_running": max_running}
+    stream = torch.cuda.current_stream()
+    for label, policy in [("isps", pic.PIC_SCHED_ISPS), ("barrier", pic.PIC_SCHED_BARRIER)]:
+        tr = TraceRun(trace, policy, budget, max_running, num_blocks, device_seed=5)
+        tr.run()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            tr.run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        kinds = [len(set(st["seq_kind"].tolist())) for st in tr.steps if st["num_seqs"]]
+        res[label] = {"attention_ms": ms, "steps": len(tr.steps),
+                      "mixed_steps": int(sum(k > 1 for k in kinds)), "query_rows": tr.rows,
+                      "requests_per_s": len(trace.requests) / (ms * 1e-3),
+                      "query_rows_per_s": tr.rows / (ms * 1e-3)}
+        log(f"[bench] scheduled trace {label}: {ms:.2f} ms over {len(tr.steps)} steps "
+            f"({res[label]['mixed_steps']} mixed)")
+        del tr
+        torch.cuda.empty_cache()
+    res["isps_speedup"] = res["barrier"]["attention_ms"] / res["isps"]["attention_ms"]
+    res["isps_step_ratio"] = res["isps"]["steps"] / res["barrier"]["steps"]
+    return res
+
+
 def ceilings():
     """What this machine delivers to plain library code: a 2 GiB device copy (bytes read +
     written per second) and a large bf16 matrix product (torch.matmul, 8192^3)."""
@@ -351,6 +395,8 @@ def main():
     ap.add_argument("--ablation", default="c2p,c3,c4",
                     help="configs on which to time the in-kernel rotation ablation ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sched", action="store_true",
+                    help="skip the scheduled-trace comparison (ISPS vs barrier)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a plain copy of this many bytes (PMC scaling run)")
     args = ap.parse_args()
@@ -421,6 +467,7 @@ def main():
     for name in [x for x in args.ablation.split(",") if x]:
         ablation[name] = rope_ablation(name)
     tables = block_table_build()
+    sched = None if args.no_sched else scheduled_trace()
     ceil = ceilings()
     offload = offload_bandwidth()
 
@@ -456,6 +503,7 @@ def main():
         "configs": others,
         "rope_ablation": ablation,
         "block_tables": tables,
+        "scheduled_trace": sched,
         "ceilings": ceil,
         "offload": offload,
         "source_hash": source_hash(),

@@ -1219,6 +1219,11 @@ __device__ __forceinline__ unsigned xcd_position(unsigned l, unsigned n) {
   return k * 8 + x;
 }
 
+// Context-length bucket of a prefill request (64-key units, capped): the
+// mixed launch dispatches tiles of longer contexts first, so the longest
+// tiles never start last and leave the rest of the GPU idle at the end.
+__device__ __forceinline__ int len_bucket(int L) { return min(max(L, 0) >> 6, 1023); }
+
 // Steps of K/V loads each decode wave keeps in flight.  Measured on MI355X:
 // one step at two waves per SIMD beats deeper rings at one wave per SIMD.
 constexpr int kDecodeDepth = 1;
@@ -1319,10 +1324,15 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   __shared__ int s_brank[1024];        // ranks handed out so far per S
   __shared__ long long s_bbase[1024];  // first decode-list index of group S
   __shared__ int s_bover;              // some request has 1024 or more chunks
+  __shared__ int s_ptot[1024];         // prefill tiles per context-length bucket
+  __shared__ int s_prank[1024];        // prefill tiles placed so far per bucket
+  __shared__ long long s_pbase[1024];  // first prefill-list index of each bucket
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   s_bcnt[tid] = 0;
   s_brank[tid] = 0;
+  s_ptot[tid] = 0;
+  s_prank[tid] = 0;
   if (tid == 0) s_bover = 0;
   __syncthreads();
   // pass 1: totals, and decode requests per chunk count
@@ -1330,7 +1340,9 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   for (int r = tid; r < num_reqs; r += 1024) {
     const int ql = cu_q[r + 1] - cu_q[r];
     if (ql > 1) {
-      pf += (long long)hkv * cdiv(ql * group, rows);
+      const int n = hkv * cdiv(ql * group, rows);
+      pf += n;
+      atomicAdd(&s_ptot[len_bucket(min(seq_lens[r], len_cap))], n);
     } else if (ql == 1) {
       const int S = num_splits(min(seq_lens[r], len_cap), kstep);
       dc += (long long)nhg * S;
@@ -1365,6 +1377,18 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   const long long mine = s_bbase[tid] - (long long)s_bcnt[tid] * tid * nhg;
   __syncthreads();
   s_bbase[tid] = mine;
+  // prefill bucket bases, longest contexts first: exclusive suffix scan of s_ptot
+  s_pbase[tid] = s_ptot[tid];
+  __syncthreads();
+  for (int st = 1; st < 1024; st <<= 1) {
+    const long long x = tid + st < 1024 ? s_pbase[tid + st] : 0;
+    __syncthreads();
+    s_pbase[tid] += x;
+    __syncthreads();
+  }
+  const long long pmine = s_pbase[tid] - s_ptot[tid];
+  __syncthreads();
+  s_pbase[tid] = pmine;
   const bool chunk_major = s_bover == 0;
   __syncthreads();
   // More items than the workspace was sized for means the metadata broke a
@@ -1392,14 +1416,11 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
       else if (ql == 1) ndc = (long long)nhg * num_splits(L, kstep);
     }
     __syncthreads();
-    s_a[tid] = npf;
     s_b[tid] = ndc;
     __syncthreads();
     for (int st = 1; st < 1024; st <<= 1) {  // inclusive Hillis-Steele scan
-      const long long xa = tid >= st ? s_a[tid - st] : 0;
       const long long xb = tid >= st ? s_b[tid - st] : 0;
       __syncthreads();
-      s_a[tid] += xa;
       s_b[tid] += xb;
       __syncthreads();
     }
@@ -1408,7 +1429,11 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
     // request's rank inside its group)
     s_kind[tid] = ql > 1 ? 1 : (ql == 1 ? 2 : 0);
     s_cnt[tid] = ql > 1 ? cdiv(ql * group, rows) : (ql == 1 ? num_splits(L, kstep) : 0);
-    s_off[tid] = ql > 1 ? s_tot[0] + s_a[tid] - npf : s_tot[1] + s_b[tid] - ndc;
+    s_off[tid] = ql > 1 ? 0 : s_tot[1] + s_b[tid] - ndc;
+    if (ql > 1) {
+      const int b = len_bucket(L);
+      s_off[tid] = s_pbase[b] + atomicAdd(&s_prank[b], (int)npf);
+    }
     if (ql == 1 && chunk_major) s_off[tid] = atomicAdd(&s_brank[s_cnt[tid]], 1);
     __syncthreads();
     const int nr = min(1024, num_reqs - base);
@@ -1416,11 +1441,10 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
       const int kind = s_kind[rr];
       const int cnt = s_cnt[rr];
       const long long off = s_off[rr];
-      if (kind == 1) {  // prefill tiles, per kv head last tile first
+      if (kind == 1) {  // prefill tiles, last (longest) tile first, kv heads inner
         for (int it = lane; it < hkv * cnt; it += 64) {
-          const int g = it / cnt, k = it % cnt;
-          items[xcd_position((unsigned)(off + it), (unsigned)total_pf)] =
-              make_int4(kItemPrefill, base + rr, g, cnt - 1 - k);
+          const int k = it / hkv, g = it % hkv;
+          items[off + it] = make_int4(kItemPrefill, base + rr, g, cnt - 1 - k);
         }
       } else if (kind == 2) {  // decode chunks, per chunk the kv-head groups
         for (int it = lane; it < cnt * nhg; it += 64) {
@@ -1434,10 +1458,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
       }
     }
     __syncthreads();
-    if (tid == 1023) {
-      s_tot[0] += s_a[1023];
-      s_tot[1] += s_b[1023];
-    }
+    if (tid == 1023) s_tot[1] += s_b[1023];
     __syncthreads();
   }
 }

@@ -164,3 +164,116 @@ def run_workload(w: Workload, decode=None) -> np.ndarray:
     out = dw.step(decode)
     torch.cuda.synchronize()
     return to_f64(out)
+
+
+# ---------------------------------------------------------------------------
+# scheduled traces (interleaved span-prefill scheduling)
+# ---------------------------------------------------------------------------
+
+def schedule_trace(trace, policy: int, budget: int, max_running: int, num_blocks: int):
+    """Run the library's scheduler over a trace (host).  Returns the steps, each the
+    pic_sched_step dict plus ``src``: the global token index of every query row."""
+    B = pic.BLOCK_SIZE
+    R = len(trace.requests)
+    max_len = max([trace.composed_len(r) for r in range(R)] + list(trace.span_lens))
+    stride = -(-max_len // B)
+    max_seqs = max_running + len(trace.span_lens)
+    sched = pic.Scheduler(policy, budget, max_running, num_blocks, max_seqs=max_seqs,
+                          max_keys=max_seqs * max_len, block_table_stride=stride)
+    try:
+        for n in trace.span_lens:
+            sched.add_span(n)
+        for (arr, sids, p, o) in trace.requests:
+            sched.add_request(arr, sids, p, o)
+        steps = []
+        while True:
+            st = sched.step()
+            if st is None:
+                break
+            src = []
+            for i in range(st["num_seqs"]):
+                kind, sid, qb = int(st["seq_kind"][i]), int(st["seq_id"][i]), int(st["q_begin"][i])
+                ql = int(st["cu_seqlens_q"][i + 1] - st["cu_seqlens_q"][i])
+                c = np.arange(qb, qb + ql)
+                src.append(trace.span_token_index(sid, c) if kind == pic.PIC_SEQ_SPAN
+                           else trace.request_token_index(sid, c))
+            st["src"] = np.concatenate(src) if src else np.zeros(0, np.int64)
+            steps.append(st)
+    finally:
+        sched.close()
+    return steps
+
+
+class TraceRun:
+    """A scheduled trace staged on the GPU: every step's q/k/v rows and metadata resident,
+    then ``run()`` enqueues the steps (cache write + one mixed attention launch each)."""
+
+    def __init__(self, trace, policy: int, budget: int, max_running: int, num_blocks: int,
+                 dev="cuda", device_seed=None):
+        """device_seed: draw the token values on the device (N(0, 1) from a seeded torch
+        generator, rounded to bf16) instead of uploading the trace's own values."""
+        torch = _torch()
+        self.trace = trace
+        self.steps = schedule_trace(trace, policy, budget, max_running, num_blocks)
+        B = pic.BLOCK_SIZE
+        tdt = torch.bfloat16
+        if device_seed is None:
+            q_all = to_torch(trace.q, "bf16", dev)
+            k_all = to_torch(trace.k, "bf16", dev)
+            v_all = to_torch(trace.v, "bf16", dev)
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(int(device_seed))
+            n = trace.n_tokens
+            k_all, v_all, q_all = [torch.randn((n, h, trace.d), generator=g, device=dev).to(tdt)
+                                   for h in (trace.hkv, trace.hkv, trace.hq)]
+        self.k_pool = torch.full((num_blocks, trace.hkv, B, trace.d), float("nan"), dtype=tdt,
+                                 device=dev)
+        self.v_pool = torch.full((num_blocks, trace.hkv, trace.d, B), float("nan"), dtype=tdt,
+                                 device=dev)
+        max_pos = max(trace.composed_len(r) for r in range(len(trace.requests)))
+        max_pos = max([max_pos] + list(trace.span_lens))
+        self.cos = torch.empty((max_pos, trace.d // 2), dtype=torch.float32, device=dev)
+        self.sin = torch.empty_like(self.cos)
+        pic.pic_rope_table(self.cos, self.sin, trace.base)
+        self.dev_steps = []
+        ws = 16
+        for st in self.steps:
+            if st["num_seqs"] == 0:
+                continue
+            src = torch.from_numpy(st["src"]).to(dev)
+            d = dict(q=q_all[src].contiguous(), k=k_all[src].contiguous(),
+                     v=v_all[src].contiguous(), slots=i32(st["slot_mapping"], dev),
+                     cu_q=i32(st["cu_seqlens_q"], dev), q_pos=i32(st["q_pos"], dev),
+                     bt=i32(st["block_table"], dev), seq_lens=i32(st["seq_lens"], dev),
+                     cu_k=i32(st["cu_seqlens_k"], dev), k_pos=i32(st["k_pos"], dev),
+                     max_q_len=st["max_q_len"], max_seq_len=st["max_seq_len"], src=src)
+            d["out"] = torch.empty_like(d["q"])
+            ws = max(ws, pic.pic_attn_workspace_size(st["num_seqs"], st["total_q"],
+                                                     st["max_seq_len"], trace.hq, trace.hkv,
+                                                     trace.d, tdt))
+            self.dev_steps.append(d)
+        self.workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)
+        self.rows = int(sum(st["total_q"] for st in self.steps))
+
+    def run(self):
+        for d in self.dev_steps:
+            pic.pic_cache_write(d["k"], d["v"], d["slots"], self.k_pool, self.v_pool)
+            pic.pic_attn_prefill(d["q"], d["cu_q"], d["q_pos"], self.k_pool, self.v_pool,
+                                 d["bt"], d["seq_lens"], d["cu_k"], d["k_pos"], self.cos,
+                                 self.sin, d["max_q_len"], d["max_seq_len"], d["out"],
+                                 self.workspace)
+
+    def outputs(self):
+        """[n_tokens][Hq][d] float64: each token's output row from its (last) computation,
+        and a bool mask of the tokens computed as a one-row sequence (split-KV path)."""
+        torch = _torch()
+        t = self.trace
+        out = torch.full((t.n_tokens, t.hq, t.d), float("nan"), dtype=torch.bfloat16,
+                         device=self.k_pool.device)
+        single = np.zeros(t.n_tokens, bool)
+        for st, d in zip([s for s in self.steps if s["num_seqs"]], self.dev_steps):
+            out[d["src"]] = d["out"]
+            ql = np.diff(st["cu_seqlens_q"])
+            single[st["src"]] = np.repeat(ql == 1, ql)
+        return to_f64(out), single

@@ -43,3 +43,33 @@ def select_rows(out: np.ndarray, w: Workload, requests, rows=None) -> np.ndarray
         sel = np.arange(ql) if rows is None or r not in rows else np.asarray(rows[r])
         parts.append(out[q0 + sel])
     return np.concatenate(parts, axis=0)
+
+
+def trace_token_outputs(trace, tokens) -> np.ndarray:
+    """fp64 reference output of each listed token of a scheduled trace, [n][Hq][d].
+
+    A span token i of span s attends to tokens 0..i of that span at positions
+    0..i (a span is prefilled on its own); a request's private token at
+    composed slot c attends to slots 0..c of the request's composed sequence
+    (its spans in order, then its private tokens) at positions 0..c.  The
+    output does not depend on how a schedule batches or chunks the work.
+    """
+    tokens = np.asarray(tokens, np.int64)
+    out = np.zeros((tokens.shape[0], trace.hq, trace.d))
+    n_span_tok = int(sum(trace.span_lens))
+    span_end = np.asarray(trace.span_base) + np.asarray(trace.span_lens)
+    for n, g in enumerate(tokens):
+        if g < n_span_tok:
+            s = int(np.searchsorted(span_end, g, side="right"))
+            c = int(g - trace.span_base[s])
+            idx = trace.span_base[s] + np.arange(c + 1)
+        else:
+            # the last request starting at or before g (requests without private
+            # tokens share their successor's base and are passed over)
+            r = int(np.searchsorted(trace.req_base, g, side="right")) - 1
+            c = int(g - trace.req_base[r]) + trace.span_tokens(r)
+            idx = trace.request_token_index(r, np.arange(c + 1))
+        out[n] = oracle.attention_request(trace.q[g][None], np.array([c]), trace.k[idx],
+                                          trace.v[idx], np.arange(c + 1), 1, trace.base,
+                                          trace.hkv)[0]
+    return out

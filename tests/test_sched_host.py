@@ -277,3 +277,53 @@ def test_too_small_arrays_leave_the_state_unchanged():
         got.append(s.step())
     assert s.step() is None
     assert summary(got) == ref
+
+
+@pytest.mark.parametrize("budget,max_running,num_blocks", [(64, 4, 256), (40, 2, 28)])
+@pytest.mark.parametrize("policy", [pic.PIC_SCHED_ISPS, pic.PIC_SCHED_BARRIER])
+def test_gpu_test_traces_replay(policy, budget, max_running, num_blocks):
+    """The schedules the GPU tests execute: valid metadata, right tokens in every slot, and
+    every token of the trace is a query row at least once (the row sources cover it)."""
+    from tests.gpu_harness import schedule_trace
+    from workloads import make_trace
+    trace = make_trace("small", data_seed=11, n_spans=6, n_req=8, values=False)
+    steps = schedule_trace(trace, policy, budget, max_running, num_blocks)
+    replay(trace.span_lens, trace.requests, steps, policy, budget, num_blocks)
+    src = np.concatenate([st["src"] for st in steps])
+    assert np.array_equal(np.unique(src), np.arange(trace.n_tokens))
+    for st in steps:
+        assert st["src"].shape[0] == st["total_q"]
+
+
+def test_trace_token_index():
+    from workloads import make_trace
+    t = make_trace("small", data_seed=11, n_spans=6, n_req=8, values=False)
+    seen = []
+    for s, n in enumerate(t.span_lens):
+        seen.append(t.span_token_index(s, np.arange(n)))
+    for r, (_, sids, p, o) in enumerate(t.requests):
+        st = t.span_tokens(r)
+        comp = t.request_token_index(r, np.arange(st + p + o))
+        off = 0
+        for s in sids:   # the spans' part maps onto the spans' own tokens
+            assert np.array_equal(comp[off:off + t.span_lens[s]], t.span_token_index(s, np.arange(t.span_lens[s])))
+            off += t.span_lens[s]
+        seen.append(comp[st:])
+    assert np.array_equal(np.sort(np.concatenate(seen)), np.arange(t.n_tokens))
+
+
+def test_trace_oracle_first_tokens_are_their_values():
+    """A span's first token and a span-less request's first private token see one key:
+    the oracle output is that token's V, head group by head group."""
+    import oracle
+    from tests.oracle_harness import trace_token_outputs
+    from workloads import make_trace
+    t = make_trace("tiny", data_seed=3, n_spans=2, n_req=3, spans_per_req=(0, 1), hq=4, hkv=2,
+                   d=16)
+    firsts = [int(t.span_base[0])]
+    firsts += [int(t.req_base[r]) for r, (_, sids, p, o) in enumerate(t.requests)
+               if not sids and p + o > 0]
+    out = trace_token_outputs(t, firsts)
+    for n, g in enumerate(firsts):
+        v = oracle.bf16_bits_to_f64(t.v[g])            # [Hkv][d]
+        assert np.array_equal(out[n], np.repeat(v, t.hq // t.hkv, axis=0))

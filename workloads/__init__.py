@@ -13,3 +13,4 @@ from .synth import (  # noqa: F401
     f32_to_bf16_bits,
     algorithmic_counts,
 )
+from .trace import RAG_TRACE, Trace, make_trace  # noqa: F401
