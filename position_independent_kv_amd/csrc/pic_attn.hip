@@ -1293,13 +1293,19 @@ __global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
 }
 
 // Planner: one workgroup of 1024 threads turns (cu_seqlens_q, seq_lens) into
-// the work list: first the prefill tiles (per request and kv head, last tile
-// first: the later query rows see more keys), then the chunks of q_len == 1
+// the work list: first the prefill tiles, then the chunks of q_len == 1
 // requests, so the long MFMA-bound tiles start early and the short chunks
 // fill the tail.  (A workgroup of either kind fills a compute unit's LDS and
 // registers, so the two kinds cannot share one; interleaving them evenly
-// measured 3% slower on the mixed 16-prefill + 128-decode batch.)  Within
-// each kind, item i is written at its XCD dispatch position.
+// measured 3% slower on the mixed 16-prefill + 128-decode batch.)
+// Prefill tiles are ordered longest first: requests by context-length bucket
+// (longest first; ranks inside a bucket from LDS atomics), inside a request
+// the last tile first (the later query rows see more keys) with the kv heads
+// innermost, and item i is dispatched as workgroup i, so consecutive tiles
+// go to different XCDs.  A tile's time grows with its context, and the
+// workgroups of one XCD run in dispatch order: long tiles bunched on one XCD
+// would end the launch alone.  With 8 kv heads every tile of one (request,
+// head) still lands on the same XCD.
 // Decode chunks are ordered chunk-major inside groups of requests with the
 // same chunk count (longest group first): chunk s of every request of a
 // group, then chunk s + 1, ...  Consecutive items then read the same key
