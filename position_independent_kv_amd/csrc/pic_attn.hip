@@ -1313,6 +1313,45 @@ __global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
 // a few chunk levels' table rows in its L2.  (Ranks inside a group are taken
 // with LDS atomics, so the dispatch order of equal-length requests may vary
 // between calls; no result depends on it.)
+// Inclusive scans of NV values per thread across the 1024-thread planner
+// workgroup: a shuffle scan inside each wave, then one over the 16 wave
+// totals; two barriers.  s_w: [16][NV] scratch.  Returns each thread's
+// inclusive prefix; tot gets the workgroup totals.
+template <int NV>
+__device__ __forceinline__ void plan_scan(long long (&x)[NV], long long (*s_w)[NV],
+                                          long long (&tot)[NV]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long y = __shfl_up(x[v], o);
+      if (lane >= o) x[v] += y;
+    }
+  if (lane == 63)
+#pragma unroll
+    for (int v = 0; v < NV; ++v) s_w[wave][v] = x[v];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      long long w = lane < 16 ? s_w[lane][v] : 0;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const long long y = __shfl_up(w, o);
+        if (lane >= o) w += y;
+      }
+      if (lane < 16) s_w[lane][v] = w;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    if (wave > 0) x[v] += s_w[wave - 1][v];
+    tot[v] = s_w[15][v];
+  }
+}
+
 __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ cu_q,
                                                     const int32_t* __restrict__ seq_lens,
                                                     int num_reqs, int hkv, int group, int nhg,
@@ -1320,12 +1359,11 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
                                                     long long max_items,
                                                     int4* __restrict__ items,
                                                     int* __restrict__ count) {
-  __shared__ long long s_a[1024];
-  __shared__ long long s_b[1024];
+  __shared__ long long s_w4[16][4];
+  __shared__ long long s_w1[2][16][1];
   __shared__ long long s_off[1024];
   __shared__ int s_cnt[1024];
   __shared__ unsigned char s_kind[1024];
-  __shared__ long long s_tot[2];
   __shared__ int s_bcnt[1024];         // decode requests per chunk count S
   __shared__ int s_brank[1024];        // ranks handed out so far per S
   __shared__ long long s_bbase[1024];  // first decode-list index of group S
@@ -1341,7 +1379,8 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   s_prank[tid] = 0;
   if (tid == 0) s_bover = 0;
   __syncthreads();
-  // pass 1: totals, and decode requests per chunk count
+  // pass 1: item totals, decode requests per chunk count, prefill tiles per
+  // context-length bucket
   long long pf = 0, dc = 0;
   for (int r = tid; r < num_reqs; r += 1024) {
     const int ql = cu_q[r + 1] - cu_q[r];
@@ -1356,91 +1395,54 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
       else s_bover = 1;
     }
   }
-  s_a[tid] = pf;
-  s_b[tid] = dc;
   __syncthreads();
-  for (int st = 512; st > 0; st >>= 1) {
-    if (tid < st) {
-      s_a[tid] += s_a[tid + st];
-      s_b[tid] += s_b[tid + st];
-    }
-    __syncthreads();
-  }
-  const long long total_pf = s_a[0];
-  const long long total_dc = s_b[0];
+  // totals, and the group / bucket bases (longest first: exclusive suffix
+  // sums, total minus the inclusive prefix): thread b holds bucket b
+  long long x[4] = {pf, dc, (long long)s_bcnt[tid] * tid * nhg, (long long)s_ptot[tid]};
+  long long tot[4];
+  plan_scan<4>(x, s_w4, tot);
+  const long long total_pf = tot[0];
+  const long long total_dc = tot[1];
   const long long total = total_pf + total_dc;
-  __syncthreads();
-  // group bases, longest group first: exclusive suffix scan over S of
-  // (requests with S chunks) * S * nhg
-  s_bbase[tid] = (long long)s_bcnt[tid] * tid * nhg;
-  __syncthreads();
-  for (int st = 1; st < 1024; st <<= 1) {
-    const long long x = tid + st < 1024 ? s_bbase[tid + st] : 0;
-    __syncthreads();
-    s_bbase[tid] += x;
-    __syncthreads();
-  }
-  const long long mine = s_bbase[tid] - (long long)s_bcnt[tid] * tid * nhg;
-  __syncthreads();
-  s_bbase[tid] = mine;
-  // prefill bucket bases, longest contexts first: exclusive suffix scan of s_ptot
-  s_pbase[tid] = s_ptot[tid];
-  __syncthreads();
-  for (int st = 1; st < 1024; st <<= 1) {
-    const long long x = tid + st < 1024 ? s_pbase[tid + st] : 0;
-    __syncthreads();
-    s_pbase[tid] += x;
-    __syncthreads();
-  }
-  const long long pmine = s_pbase[tid] - s_ptot[tid];
-  __syncthreads();
-  s_pbase[tid] = pmine;
+  s_bbase[tid] = tot[2] - x[2];
+  s_pbase[tid] = tot[3] - x[3];
   const bool chunk_major = s_bover == 0;
-  __syncthreads();
   // More items than the workspace was sized for means the metadata broke a
   // precondition (total_q or max_seq_len too small): run nothing.
   if (total > max_items) {
     if (tid == 0) *count = 0;
     return;
   }
-  if (tid == 0) {
-    *count = (int)total;
-    s_tot[0] = 0;
-    s_tot[1] = 0;
-  }
-  // pass 2: exclusive scans per chunk of 1024 requests, then emit: the waves
-  // take the chunk's requests in turn and their lanes split each request's
-  // items
+  if (tid == 0) *count = (int)total;
+  // pass 2, per chunk of 1024 requests: decode offsets (request order, when
+  // not chunk-major) by a scan, prefill and chunk-major ranks by LDS
+  // atomics; then the waves take the chunk's requests in turn and their
+  // lanes split each request's items
+  long long dc_base = 0;
   for (int base = 0; base < num_reqs; base += 1024) {
     const int r = base + tid;
     int ql = 0, L = 0;
-    long long npf = 0, ndc = 0;
+    long long ndc = 0;
     if (r < num_reqs) {
       ql = cu_q[r + 1] - cu_q[r];
       L = min(seq_lens[r], len_cap);
-      if (ql > 1) npf = (long long)hkv * cdiv(ql * group, rows);
-      else if (ql == 1) ndc = (long long)nhg * num_splits(L, kstep);
+      if (ql == 1) ndc = (long long)nhg * num_splits(L, kstep);
     }
-    __syncthreads();
-    s_b[tid] = ndc;
-    __syncthreads();
-    for (int st = 1; st < 1024; st <<= 1) {  // inclusive Hillis-Steele scan
-      const long long xb = tid >= st ? s_b[tid - st] : 0;
-      __syncthreads();
-      s_b[tid] += xb;
-      __syncthreads();
-    }
-    // per request: kind, item count per kv head (tiles) or per chunk row
-    // (chunks), first item index in its list (decode, chunk-major: the
-    // request's rank inside its group)
+    long long y[1] = {ndc};
+    long long ytot[1];
+    plan_scan<1>(y, s_w1[(base >> 10) & 1], ytot);
     s_kind[tid] = ql > 1 ? 1 : (ql == 1 ? 2 : 0);
     s_cnt[tid] = ql > 1 ? cdiv(ql * group, rows) : (ql == 1 ? num_splits(L, kstep) : 0);
-    s_off[tid] = ql > 1 ? 0 : s_tot[1] + s_b[tid] - ndc;
     if (ql > 1) {
       const int b = len_bucket(L);
-      s_off[tid] = s_pbase[b] + atomicAdd(&s_prank[b], (int)npf);
+      s_off[tid] = s_pbase[b] + atomicAdd(&s_prank[b], hkv * cdiv(ql * group, rows));
+    } else if (ql == 1) {
+      s_off[tid] = chunk_major ? (long long)atomicAdd(&s_brank[s_cnt[tid]], 1)
+                               : dc_base + y[0] - ndc;
+    } else {
+      s_off[tid] = 0;
     }
-    if (ql == 1 && chunk_major) s_off[tid] = atomicAdd(&s_brank[s_cnt[tid]], 1);
+    dc_base += ytot[0];
     __syncthreads();
     const int nr = min(1024, num_reqs - base);
     for (int rr = wave; rr < nr; rr += 16) {
@@ -1463,8 +1465,6 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
         }
       }
     }
-    __syncthreads();
-    if (tid == 1023) s_tot[1] += s_b[1023];
     __syncthreads();
   }
 }

@@ -247,7 +247,8 @@ class TraceRun:
                      cu_q=i32(st["cu_seqlens_q"], dev), q_pos=i32(st["q_pos"], dev),
                      bt=i32(st["block_table"], dev), seq_lens=i32(st["seq_lens"], dev),
                      cu_k=i32(st["cu_seqlens_k"], dev), k_pos=i32(st["k_pos"], dev),
-                     max_q_len=st["max_q_len"], max_seq_len=st["max_seq_len"], src=src)
+                     max_q_len=st["max_q_len"], max_seq_len=st["max_seq_len"], src=src,
+                     decode_only=bool(st["max_q_len"] == 1))
             d["out"] = torch.empty_like(d["q"])
             ws = max(ws, pic.pic_attn_workspace_size(st["num_seqs"], st["total_q"],
                                                      st["max_seq_len"], trace.hq, trace.hkv,
@@ -257,12 +258,19 @@ class TraceRun:
         self.rows = int(sum(st["total_q"] for st in self.steps))
 
     def run(self):
+        """Every step: cache write, then one attention call (the decode launch when every
+        sequence of the step is a single row, else the mixed launch)."""
         for d in self.dev_steps:
             pic.pic_cache_write(d["k"], d["v"], d["slots"], self.k_pool, self.v_pool)
-            pic.pic_attn_prefill(d["q"], d["cu_q"], d["q_pos"], self.k_pool, self.v_pool,
-                                 d["bt"], d["seq_lens"], d["cu_k"], d["k_pos"], self.cos,
-                                 self.sin, d["max_q_len"], d["max_seq_len"], d["out"],
-                                 self.workspace)
+            if d["decode_only"]:
+                pic.pic_attn_decode(d["q"], d["q_pos"], self.k_pool, self.v_pool, d["bt"],
+                                    d["seq_lens"], d["cu_k"], d["k_pos"], self.cos, self.sin,
+                                    d["max_seq_len"], d["out"], self.workspace)
+            else:
+                pic.pic_attn_prefill(d["q"], d["cu_q"], d["q_pos"], self.k_pool, self.v_pool,
+                                     d["bt"], d["seq_lens"], d["cu_k"], d["k_pos"], self.cos,
+                                     self.sin, d["max_q_len"], d["max_seq_len"], d["out"],
+                                     self.workspace)
 
     def outputs(self):
         """[n_tokens][Hq][d] float64: each token's output row from its (last) computation,
