@@ -16,7 +16,9 @@
  * ---------------------------------------
  * - Pointers: every array argument is DEVICE memory owned by the caller,
  *   unless the argument is documented as host memory.  The library never
- *   allocates or frees memory and keeps no state between calls.
+ *   allocates or frees device memory and keeps no state between calls; the
+ *   one exception is the host-side scheduler object of pic_sched_* (plain
+ *   host memory, created and destroyed by the caller's calls).
  * - stream: a hipStream_t (NULL = the legacy default stream).  Every call
  *   only enqueues work on that stream and returns without synchronising the
  *   host.
@@ -112,7 +114,8 @@ int pic_cache_write(const void* k, const void* v, const int32_t* slot_mapping, i
  * pic_attn_workspace_size -- bytes of device workspace that pic_attn_decode /
  * pic_attn_prefill need for these bounds (total_q = number of query rows,
  * max_seq_len >= every seq_len).  It holds the work list of the mixed
- * launch and the per-chunk partial results of split requests; every call
+ * launch and the per-chunk partial results of split requests and split
+ * prefill tiles; every call
  * writes what it reads, so it needs no initialisation and can be reused by
  * later calls on the same stream.  Calls that overlap in time must use
  * different workspaces.
@@ -157,6 +160,13 @@ int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool, con
  * j <= seq_lens[r] - q_len + i.  max_q_len must be >= every q_len (a
  * precondition, like the others).  Other arguments as in pic_attn_decode.
  * A small planner kernel builds the work list in the workspace first.
+ * bf16 launches with fewer prefill tiles (256 query rows of one kv head)
+ * than 256 split each tile over a context of 2048 keys or more into key
+ * chunks that run in parallel; a merge kernel on the same stream combines
+ * them.  The split depends on the whole launch, so a request's prefill rows
+ * are bit-identical between launches that split it the same way (always
+ * when both launches have 256 tiles or more) and otherwise agree within
+ * rounding.
  *   q, out   [total_q][Hq][head_dim]
  *   workspace >= pic_attn_workspace_size(num_reqs, total_q, max_seq_len, ...)
  */

@@ -74,7 +74,23 @@ struct AttnArgs {
   float* ws_o;
   const int4* items;
   const int* nitems;
+  // split prefill tiles (null when the launch cannot split): per split item
+  // (its work-list position) and row, (max, sum) and the normalised output;
+  // the split tiles the merge visits, and their number
+  float2* pf_ml;
+  float* pf_o;
+  int4* pf_tiles;
+  int* pf_count;
 };
+
+// Work item x field: kind in bits 0-3; for a split prefill tile the split
+// index in bits 4-15 and the number of splits in bits 16-27 (0: not split).
+__host__ __device__ constexpr int item_code(int kind, int split, int nsplit) {
+  return kind | (split << 4) | (nsplit << 16);
+}
+__device__ __forceinline__ int item_kind(int x) { return x & 15; }
+__device__ __forceinline__ int item_split(int x) { return (x >> 4) & 0xfff; }
+__device__ __forceinline__ int item_nsplit(int x) { return max(1, (x >> 16) & 0xfff); }
 
 // seq_len of request r, clamped to what the grid, the workspace and the block
 // table were sized for (a violated precondition gives wrong numbers, never an
@@ -492,12 +508,56 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
 // o = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m).  One
 // workgroup per (request, kv head); threads take (column, 8 consecutive d)
 // pairs, and threads beyond those pairs take every SG-th chunk in parallel.
+// Merge of one split prefill tile (kPrefillTileRows threads, one query row
+// each): o = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m), over
+// the tile's chunks that saw a key.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a) {
+__device__ void merge_prefill_tile(const AttnArgs& a, int idx) {
+  static_assert(kThreads == kPrefillTileRows, "one thread per tile row");
+  if (!a.pf_tiles || idx >= *a.pf_count) return;
+  const int4 t = a.pf_tiles[idx];  // request, kv head, tile, first item
+  const int r = t.x, g = t.y, p0 = t.w;
+  if (r < 0 || r >= a.num_reqs || g < 0 || g >= a.hkv || p0 < 0 || p0 >= kSplitCUs) return;
+  const int S = min(item_nsplit(a.items[p0].x), kSplitCUs - p0);
+  const int q0 = a.cu_q[r];
+  const int ql = a.cu_q[r + 1] - q0;
+  const int G = a.group;
+  const int n = t.z * kPrefillTileRows + (int)threadIdx.x;
+  if (n >= ql * G) return;
+  float m = -INFINITY, l = 0.0f;
+  f32x4 o[D / 4];
+#pragma unroll
+  for (int e = 0; e < D / 4; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const size_t prow = (size_t)(p0 + s) * kPrefillTileRows + threadIdx.x;
+    const float2 ml = a.pf_ml[prow];
+    if (!(ml.y > 0.0f)) continue;  // the chunk holds no key of this row
+    const float mn = fmaxf(m, ml.x);
+    const float a0 = fast_exp2(m - mn), a1 = ml.y * fast_exp2(ml.x - mn);
+    l = l * a0 + a1;
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.pf_o + prow * D);
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) o[e] = o[e] * a0 + src[e] * a1;
+    m = mn;
+  }
+  const float inv = 1.0f / l;
+  T* dst = (T*)a.out + (((size_t)q0 + n / G) * a.hq + g * G + n % G) * D;
+#pragma unroll
+  for (int e = 0; e < D / 4; ++e) store4<T>(dst + 4 * e, o[e], inv);
+}
+
+// Blocks [0, dec_blocks): one per (request, kv head), merging the chunks of
+// q_len == 1 requests; blocks beyond: one per split prefill tile.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a, int dec_blocks) {
   constexpr int EPT = 8;
   __shared__ __attribute__((aligned(16))) float gm[kThreads * EPT];
   __shared__ float2 gml[kThreads];
   const int tid = threadIdx.x;
+  if ((int)blockIdx.x >= dec_blocks) {
+    if constexpr (sizeof(T) == 2) merge_prefill_tile<T, D>(a, (int)blockIdx.x - dec_blocks);
+    return;
+  }
   const int r = blockIdx.x / a.hkv;
   const int g = blockIdx.x % a.hkv;
   if (a.cu_q && a.cu_q[r + 1] - a.cu_q[r] != 1) return;
@@ -804,8 +864,8 @@ struct Pf {
 // by log2(e)/sqrt(d) so scores come out in base-2 units) sit in a per-wave
 // LDS slice.  Steps that lie wholly below the causal diagonal skip the mask.
 template <int D, int NW, int KS, bool ROT>
-__device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
-                                  unsigned char* smem) {
+__device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int split,
+                                  int nsplit, int pslot, unsigned char* smem) {
   using P = Pf<D, NW, KS>;
   typedef Mma32::Op Op;
   typedef Mma32::Acc Acc;
@@ -824,7 +884,15 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
   const int last_tok = min((trow0 + P::ROWS - 1) / G, ql - 1);
   const int kend = min(L, L - ql + last_tok + 1);  // slots any row of the tile sees
   const int kfull = max(0, L - ql + first_tok + 1);  // slots every row of the tile sees
-  const int nsteps = cdiv(kend, P::KSTEP);
+  // keys [kofs, kstop) of this item: the whole range, or chunk `split` of
+  // nsplit equal chunks of whole steps
+  int kofs = 0, kstop = kend;
+  if (nsplit > 1) {
+    const int chunk = cdiv(cdiv(kend, nsplit), P::KSTEP) * P::KSTEP;
+    kofs = min(kend, split * chunk);
+    kstop = min(kend, kofs + chunk);
+  }
+  const int nsteps = cdiv(kstop - kofs, P::KSTEP);
   bf16* const lds = reinterpret_cast<bf16*>(smem);
 
   // query row of this lane's column, its causal limit, and its LDS slice
@@ -897,7 +965,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
   // load counter completes in issue order).
   int kmeta_blk, kmeta_pos, vmeta_blk[P::NVR];
   int kmeta_blk_nx, kmeta_pos_nx = 0, vmeta_blk_nx[P::NVR];
-  auto kmeta = [&](int kb) {
+  auto kmeta = [&](int kb) {  // kb: absolute key index of a step's first key
     const int kc = min(kb + skey, L - 1);
     kmeta_blk_nx = bt[kc >> 4];
     if constexpr (ROT) kmeta_pos_nx = kp[kc];
@@ -949,7 +1017,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
     *reinterpret_cast<KV*>(kd + D / 2) = hi;
   };
   auto vstore = [&](int step) {  // the loaded V^T runs into V stage `step`
-    const int kb = step * P::KSTEP;
+    const int kb = kofs + step * P::KSTEP;
     bf16* vdst = lds + P::V_OFF + (step % P::NVB) * P::VBUF + vd * P::VLD + vk0;
 #pragma unroll
     for (int u = 0; u < P::NVR; ++u) *reinterpret_cast<VRun*>(vdst + u * P::VR) = vr[u];
@@ -1008,25 +1076,26 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
   };
   // the first K stages and V stage; the next loads' addresses
   auto prologue = [&](bool with_v) {
-    kmeta(0);
+    kmeta(kofs);
     kmeta_use();
     kload();
     if (with_v) {
-      vmeta(0);
+      vmeta(kofs);
       vmeta_use();
       vload();
     }
     kstore(0);
     if (with_v) vstore(0);
-    kmeta(P::KSTEP);
+    kmeta(kofs + P::KSTEP);
     kmeta_use();
     kload();
     kstore(1);
-    kmeta(2 * P::KSTEP);
-    if (with_v) vmeta(P::KSTEP);
+    kmeta(kofs + 2 * P::KSTEP);
+    if (with_v) vmeta(kofs + P::KSTEP);
     __syncthreads();
   };
-  const int jfull = min(nsteps, kfull / P::KSTEP);  // steps below every row's diagonal
+  // steps below every row's diagonal (kofs is a multiple of the step)
+  const int jfull = min(nsteps, max(0, kfull - kofs) / P::KSTEP);
 
   // Exact column max over all visible keys (only for the rare second pass).
   auto row_max = [&]() {
@@ -1036,12 +1105,12 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
     const Acc zero = Acc{};
     for (int j = 0; j < nsteps; ++j) {
       kmeta_use();
-      kmeta((j + 3) * P::KSTEP);
+      kmeta(kofs + (j + 3) * P::KSTEP);
       kload();
 #pragma unroll
       for (int h = 0; h < P::NBLK; ++h) {
         Acc sc = qk_block(j, h, zero);
-        if (j >= jfull) mask_block(sc, j * P::KSTEP + h * 32);
+        if (j >= jfull) mask_block(sc, kofs + j * P::KSTEP + h * 32);
         mx = fmaxf(mx, col_max(sc));
       }
       kstore(j + 2);
@@ -1103,7 +1172,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
       for (int db = 0; db < P::NDB; ++db) o[db] = Mma32::run(va[db], pb[1], o[db]);
     };
 
-    Acc negm;
+    Acc negm = Acc{};  // stays 0 (m = 0) for an item with no keys
     Acc s_next;
     if (nsteps > 0) {
       prologue(true);
@@ -1116,7 +1185,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
       } else {
         s_next = qk_block(0, 0, Acc{});
         Acc t = s_next;
-        if (jfull == 0) mask_block(t, 0);
+        if (jfull == 0) mask_block(t, kofs);
         const float mx = col_max(t);
         m = mx == -INFINITY ? 0.0f : mx;  // a column with no visible key keeps 0
 #pragma unroll
@@ -1132,7 +1201,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
     // next data is staged.  Stages K j+2 and V j+1.
     auto step = [&](int j, auto mask_tag) {
       constexpr bool MASKED = decltype(mask_tag)::value;
-      const int kb = j * P::KSTEP;
+      const int kb = kofs + j * P::KSTEP;
       kmeta_use();
       vmeta_use();
       kmeta(kb + 3 * P::KSTEP);
@@ -1172,6 +1241,22 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile,
       for (int v = 0; v < 16; ++v) bad |= !(fabsf(o[db][v]) < INFINITY);
     if (!exact && __syncthreads_or(bad && valid)) return false;
     if (!valid) return true;
+    if (nsplit > 1) {  // partial of one key chunk: (m, l), and o / l unless empty
+      const size_t prow = (size_t)pslot * kPrefillTileRows + wave * 32 + col;
+      if (hh == 0) a.pf_ml[prow] = make_float2(-negm[0], l_tot);
+      if (l_tot > 0.0f) {
+        const float inv = 1.0f / l_tot;
+        float* po = a.pf_o + prow * D;
+#pragma unroll
+        for (int db = 0; db < P::NDB; ++db)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4)
+            *reinterpret_cast<f32x4*>(po + db * 32 + 8 * v4 + 4 * hh) =
+                f32x4{o[db][4 * v4] * inv, o[db][4 * v4 + 1] * inv, o[db][4 * v4 + 2] * inv,
+                      o[db][4 * v4 + 3] * inv};
+      }
+      return true;
+    }
     const float inv = 1.0f / l_tot;
     bf16* out = (bf16*)a.out + (((size_t)q0 + tok) * a.hq + g * G + head) * D;
 #pragma unroll
@@ -1280,9 +1365,10 @@ __global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
   __shared__ __attribute__((aligned(16))) unsigned char smem[MixedSmem<T, D>::BYTES];
   if ((int)blockIdx.x >= *a.nitems) return;
   const int4 it = a.items[blockIdx.x];
-  if (it.x == kItemPrefill) {
+  if (item_kind(it.x) == kItemPrefill) {
     if constexpr (sizeof(T) == 2) {
-      prefill_tile_bf16<D, NW, kPrefillStep, ROT>(a, it.y, it.z, it.w, smem);
+      prefill_tile_bf16<D, NW, kPrefillStep, ROT>(a, it.y, it.z, it.w, item_split(it.x),
+                                                  item_nsplit(it.x), (int)blockIdx.x, smem);
     } else {
       static_assert(ROT, "fp32 prefill tiles always rotate");
       prefill_tile<T, D>(a, it.y, it.z, it.w, smem);
@@ -1358,8 +1444,13 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
                                                     int kstep, int rows, int len_cap,
                                                     long long max_items,
                                                     int4* __restrict__ items,
-                                                    int* __restrict__ count) {
+                                                    int* __restrict__ count,
+                                                    int4* __restrict__ pf_tiles,
+                                                    int* __restrict__ pf_count) {
   __shared__ long long s_w4[16][4];
+  __shared__ long long s_wt[16][1];
+  __shared__ int s_nsp[1024];          // key chunks per tile of each request (1: not split)
+  __shared__ int s_pfn;                // split tiles listed so far
   __shared__ long long s_w1[2][16][1];
   __shared__ long long s_off[1024];
   __shared__ int s_cnt[1024];
@@ -1377,17 +1468,34 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   s_brank[tid] = 0;
   s_ptot[tid] = 0;
   s_prank[tid] = 0;
-  if (tid == 0) s_bover = 0;
-  __syncthreads();
-  // pass 1: item totals, decode requests per chunk count, prefill tiles per
+  if (tid == 0) {
+    s_bover = 0;
+    s_pfn = 0;
+  }
+  // pass 1a: prefill tiles before splitting; they decide the split
+  long long tl[1] = {0};
+  for (int r = tid; r < num_reqs; r += 1024) {
+    const int ql = cu_q[r + 1] - cu_q[r];
+    if (ql > 1) tl[0] += (long long)hkv * cdiv(ql * group, rows);
+  }
+  long long ttot[1];
+  plan_scan<1>(tl, s_wt, ttot);
+  const int split_max =
+      pf_tiles && ttot[0] > 0 && ttot[0] < kSplitCUs ? kSplitCUs / (int)ttot[0] : 1;
+  // chunks per tile of a prefill request with L keys
+  auto nsplit_of = [&](int L) {
+    return split_max > 1 ? max(1, min(split_max, L / kPrefillChunkMin)) : 1;
+  };
+  // pass 1b: item totals, decode requests per chunk count, prefill items per
   // context-length bucket
   long long pf = 0, dc = 0;
   for (int r = tid; r < num_reqs; r += 1024) {
     const int ql = cu_q[r + 1] - cu_q[r];
     if (ql > 1) {
-      const int n = hkv * cdiv(ql * group, rows);
+      const int L = min(seq_lens[r], len_cap);
+      const int n = hkv * cdiv(ql * group, rows) * nsplit_of(L);
       pf += n;
-      atomicAdd(&s_ptot[len_bucket(min(seq_lens[r], len_cap))], n);
+      atomicAdd(&s_ptot[len_bucket(L)], n);
     } else if (ql == 1) {
       const int S = num_splits(min(seq_lens[r], len_cap), kstep);
       dc += (long long)nhg * S;
@@ -1410,7 +1518,10 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   // More items than the workspace was sized for means the metadata broke a
   // precondition (total_q or max_seq_len too small): run nothing.
   if (total > max_items) {
-    if (tid == 0) *count = 0;
+    if (tid == 0) {
+      *count = 0;
+      if (pf_count) *pf_count = 0;
+    }
     return;
   }
   if (tid == 0) *count = (int)total;
@@ -1433,9 +1544,10 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
     plan_scan<1>(y, s_w1[(base >> 10) & 1], ytot);
     s_kind[tid] = ql > 1 ? 1 : (ql == 1 ? 2 : 0);
     s_cnt[tid] = ql > 1 ? cdiv(ql * group, rows) : (ql == 1 ? num_splits(L, kstep) : 0);
+    s_nsp[tid] = ql > 1 ? nsplit_of(L) : 1;
     if (ql > 1) {
       const int b = len_bucket(L);
-      s_off[tid] = s_pbase[b] + atomicAdd(&s_prank[b], hkv * cdiv(ql * group, rows));
+      s_off[tid] = s_pbase[b] + atomicAdd(&s_prank[b], hkv * s_cnt[tid] * s_nsp[tid]);
     } else if (ql == 1) {
       s_off[tid] = chunk_major ? (long long)atomicAdd(&s_brank[s_cnt[tid]], 1)
                                : dc_base + y[0] - ndc;
@@ -1449,10 +1561,17 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
       const int kind = s_kind[rr];
       const int cnt = s_cnt[rr];
       const long long off = s_off[rr];
-      if (kind == 1) {  // prefill tiles, last (longest) tile first, kv heads inner
-        for (int it = lane; it < hkv * cnt; it += 64) {
-          const int k = it / hkv, g = it % hkv;
-          items[off + it] = make_int4(kItemPrefill, base + rr, g, cnt - 1 - k);
+      if (kind == 1) {  // prefill tiles, last (longest) tile first, kv heads, then chunks
+        const int S = s_nsp[rr];
+        for (int it = lane; it < hkv * cnt * S; it += 64) {
+          const int sp = it % S, k = (it / S) / hkv, g = (it / S) % hkv;
+          items[off + it] = make_int4(item_code(kItemPrefill, S > 1 ? sp : 0, S > 1 ? S : 0),
+                                      base + rr, g, cnt - 1 - k);
+          if (S > 1 && sp == 0) {
+            const int slot = atomicAdd(&s_pfn, 1);
+            if (slot < kSplitCUs / 2)
+              pf_tiles[slot] = make_int4(base + rr, g, cnt - 1 - k, (int)(off + it));
+          }
         }
       } else if (kind == 2) {  // decode chunks, per chunk the kv-head groups
         for (int it = lane; it < cnt * nhg; it += 64) {
@@ -1467,6 +1586,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
     }
     __syncthreads();
   }
+  if (tid == 0 && pf_count) *pf_count = min(s_pfn, kSplitCUs / 2);
 }
 
 // ---------------------------------------------------------------------------
@@ -1503,14 +1623,21 @@ static AttnArgs make_args(const AttnHostArgs& h, const WorkspaceLayout& w) {
   a.ws_o = (float*)(ws + w.o_off);
   a.items = (const int4*)(ws + w.items_off);
   a.nitems = (const int*)(ws + w.count_off);
+  if (w.pf_split && h.dtype == PIC_BF16) {
+    a.pf_ml = (float2*)(ws + w.pf_ml_off);
+    a.pf_o = (float*)(ws + w.pf_o_off);
+    a.pf_tiles = (int4*)(ws + w.pf_tiles_off);
+    a.pf_count = (int*)(ws + w.pf_count_off);
+  }
   return a;
 }
 
 template <typename T, int D>
-static void launch_combine(const AttnArgs& a, hipStream_t s) {
-  if (a.s_max > 1)
-    hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)(a.num_reqs * a.hkv)),
-                       dim3(kThreads), 0, s, a);
+static void launch_combine(const AttnArgs& a, hipStream_t s, int split_blocks = 0) {
+  const int dec_blocks = a.s_max > 1 ? a.num_reqs * a.hkv : 0;
+  if (dec_blocks + split_blocks > 0)
+    hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)(dec_blocks + split_blocks)),
+                       dim3(kThreads), 0, s, a, dec_blocks);
 }
 
 template <typename T, int D, bool ROT>
@@ -1529,17 +1656,25 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
   unsigned char* ws = (unsigned char*)h.workspace;
   const int len_cap = (int)min((long long)h.max_seq_len,
                               (long long)h.block_table_stride * kBlockSize);
+  const bool split = a.pf_tiles != nullptr;  // bf16, and the launch may split tiles
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, h.cu_seqlens_q, h.seq_lens,
                      h.num_reqs, h.hkv, h.hq / h.hkv, cdiv(h.hkv, mixed_waves<T>()),
                      Cfg<T, D>::KSTEP, prefill_rows<T, D>(), len_cap,
-                     w.max_items, (int4*)(ws + w.items_off), (int*)(ws + w.count_off));
+                     w.max_items, (int4*)(ws + w.items_off), (int*)(ws + w.count_off),
+                     a.pf_tiles, a.pf_count);
   hipLaunchKernelGGL((mixed_kernel<T, D, ROT>), dim3((unsigned)w.max_items),
                      dim3(64 * mixed_waves<T>()), 0, s, a);
   // Every request has q_len >= total_q - (num_reqs - 1) * max_q_len; when that
   // bound is at least 2 the batch has no decode rows and nothing to merge.
   const long long min_q_len =
       (long long)h.total_q - (long long)(h.num_reqs - 1) * h.max_q_len;
-  if (min_q_len < 2) launch_combine<T, D>(a, s);
+  if (min_q_len < 2) {
+    launch_combine<T, D>(a, s, split ? kSplitCUs / 2 : 0);
+  } else if (split) {
+    AttnArgs b = a;
+    b.s_max = 1;  // no decode merges
+    launch_combine<T, D>(b, s, kSplitCUs / 2);
+  }
   return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }
 

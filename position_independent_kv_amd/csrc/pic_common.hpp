@@ -39,12 +39,41 @@ constexpr int max_splits(int max_len) { return max_len <= 0 ? 1 : cdiv(max_len, 
 constexpr int kItemPrefill = 0;
 constexpr int kItemDecode = 1;
 
+// Key splitting of bf16 prefill tiles (the mixed launch).  A launch whose
+// prefill tiles are fewer than kSplitCUs (the compute units to fill) splits
+// the key range of each tile of a request with L keys into
+// min(kSplitCUs / tiles, L / kPrefillChunkMin) chunks, each a work item that
+// writes a partial result; a merge kernel combines them.  The decision
+// depends on the launch's total prefill tiles, so a request's prefill rows
+// are bit-identical between launches that split it the same way (always
+// when the launch has kSplitCUs tiles or more, or the request has fewer than
+// 2 * kPrefillChunkMin keys).  Split items of one launch never exceed
+// kSplitCUs, nor split tiles kSplitCUs / 2.
+constexpr int kSplitCUs = 256;
+constexpr int kPrefillChunkMin = 1024;
+constexpr int kPrefillTileRows = 256;  // query rows of one bf16 prefill tile (8 waves x 32)
+
+// Whether a mixed launch of this size might split prefill tiles: a lower
+// bound of its prefill tiles, from the rows that are not decode rows, is
+// below kSplitCUs, and some context is at least two chunks long.
+constexpr bool prefill_split_possible(long long total_q, long long num_reqs, int hq, int hkv,
+                                      long long max_seq_len) {
+  return hkv > 0 && max_seq_len >= 2LL * kPrefillChunkMin &&
+         (long long)hkv * ((total_q - num_reqs > 0 ? total_q - num_reqs : 0) * (hq / hkv) /
+                           kPrefillTileRows) < kSplitCUs;
+}
+
 // Byte layout of the attention workspace.
 struct WorkspaceLayout {
   size_t count_off;     // int: number of work items written by the planner
   size_t items_off;     // int4[max_items]: work list
   size_t ml_off;        // float2[num_reqs * hkv * s_max * group]: (max, sum) per chunk
   size_t o_off;         // float[num_reqs * hkv * s_max * group * head_dim]: chunk outputs
+  size_t pf_count_off;  // int: split prefill tiles written by the planner
+  size_t pf_tiles_off;  // int4[kSplitCUs / 2]: (request, kv head, tile, first item) per split tile
+  size_t pf_ml_off;     // float2[kSplitCUs][kPrefillTileRows]: (max, sum) per split item row
+  size_t pf_o_off;      // float[kSplitCUs][kPrefillTileRows][head_dim]: split item outputs
+  bool pf_split;        // prefill tiles may be split (the four regions above exist)
   size_t total;
   int s_max;            // chunks per request, upper bound
   int nhg;              // kv-head groups of kWaves heads (an upper bound for wider groups)
@@ -62,7 +91,9 @@ inline WorkspaceLayout workspace_layout(int num_reqs, int total_q, int max_seq_l
   // prefill tiles: sum_r ceil(q_len_r * group / rows) <= total_q*group/rows + num_reqs
   const long long tiles = (long long)hkv * ((long long)total_q * group / kPrefillRows + num_reqs);
   const long long dec = (long long)num_reqs * w.s_max * w.nhg;
-  w.max_items = tiles + dec;
+  // a launch that splits prefill tiles has at most kSplitCUs prefill items
+  w.max_items = tiles + dec +
+                (prefill_split_possible(total_q, num_reqs, hq, hkv, max_seq_len) ? kSplitCUs : 0);
   size_t off = 0;
   w.count_off = off;
   off = align_up(off + 16, 256);
@@ -73,6 +104,18 @@ inline WorkspaceLayout workspace_layout(int num_reqs, int total_q, int max_seq_l
   off = align_up(off + parts * 8, 256);
   w.o_off = off;
   off = align_up(off + parts * head_dim * 4, 256);
+  w.pf_split = prefill_split_possible(total_q, num_reqs, hq, hkv, max_seq_len);
+  w.pf_count_off = w.pf_tiles_off = w.pf_ml_off = w.pf_o_off = off;
+  if (w.pf_split) {
+    w.pf_count_off = off;
+    off = align_up(off + 16, 256);
+    w.pf_tiles_off = off;
+    off = align_up(off + (size_t)(kSplitCUs / 2) * 16, 256);
+    w.pf_ml_off = off;
+    off = align_up(off + (size_t)kSplitCUs * kPrefillTileRows * 8, 256);
+    w.pf_o_off = off;
+    off = align_up(off + (size_t)kSplitCUs * kPrefillTileRows * head_dim * 4, 256);
+  }
   w.total = off;
   return w;
 }

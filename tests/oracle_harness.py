@@ -53,23 +53,33 @@ def trace_token_outputs(trace, tokens) -> np.ndarray:
     composed slot c attends to slots 0..c of the request's composed sequence
     (its spans in order, then its private tokens) at positions 0..c.  The
     output does not depend on how a schedule batches or chunks the work.
+    One oracle call per span or request covers all its listed tokens.
     """
     tokens = np.asarray(tokens, np.int64)
     out = np.zeros((tokens.shape[0], trace.hq, trace.d))
     n_span_tok = int(sum(trace.span_lens))
     span_end = np.asarray(trace.span_base) + np.asarray(trace.span_lens)
+    groups = {}
     for n, g in enumerate(tokens):
         if g < n_span_tok:
             s = int(np.searchsorted(span_end, g, side="right"))
-            c = int(g - trace.span_base[s])
-            idx = trace.span_base[s] + np.arange(c + 1)
+            groups.setdefault(("span", s), []).append((n, int(g - trace.span_base[s])))
         else:
             # the last request starting at or before g (requests without private
             # tokens share their successor's base and are passed over)
             r = int(np.searchsorted(trace.req_base, g, side="right")) - 1
             c = int(g - trace.req_base[r]) + trace.span_tokens(r)
-            idx = trace.request_token_index(r, np.arange(c + 1))
-        out[n] = oracle.attention_request(trace.q[g][None], np.array([c]), trace.k[idx],
-                                          trace.v[idx], np.arange(c + 1), 1, trace.base,
-                                          trace.hkv)[0]
+            groups.setdefault(("req", r), []).append((n, c))
+    for (kind, i), items in groups.items():
+        slots = np.array([c for _, c in items])
+        L = int(slots.max()) + 1
+        first = 0 if kind == "span" else trace.span_tokens(i)  # first query slot
+        idx = (trace.span_token_index(i, np.arange(L)) if kind == "span"
+               else trace.request_token_index(i, np.arange(L)))
+        q_slots = np.arange(first, L)
+        res = oracle.attention_request(trace.q[idx[q_slots]], q_slots, trace.k[idx],
+                                       trace.v[idx], np.arange(L), L - first, trace.base,
+                                       trace.hkv, rows=slots - first)
+        for (n, _), row in zip(items, res):
+            out[n] = row
     return out

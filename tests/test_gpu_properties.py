@@ -103,14 +103,19 @@ def test_needle_every_slot_decode(dtype, d, G):
             assert _same_bits(out[r, h], want), (r, j, h)
 
 
-def test_needle_prefill_rows():
-    """Prefill: rows that can see the needle slot return V[j] exactly."""
+@pytest.mark.parametrize("L,needles", [
+    (200, [0, 17, 130, 131, 150, 199]),
+    # 24 tiles over 4200 keys: each tile's keys are split into 4 chunks and merged
+    (4200, [0, 1100, 2100, 4130, 4131, 4199]),
+], ids=["short", "split-tiles"])
+def test_needle_prefill_rows(L, needles):
+    """Prefill: rows that can see the needle slot return V[j] exactly (also when the
+    tile's keys are split into chunks: the other chunks' weights underflow to zero)."""
     torch = _torch()
     rng = np.random.default_rng(8)
     hkv, G, d, B = 2, 4, 128, 16
     hq = hkv * G
-    L, ql = 200, 70
-    needles = [0, 17, 130, 131, 150, 199]
+    ql = 70
     R = len(needles)
     nb_req = -(-L // B)
     nblocks = R * nb_req
