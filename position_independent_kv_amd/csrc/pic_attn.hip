@@ -902,32 +902,18 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
   const int head = (valid ? n : 0) % G;
   const int lim = valid ? L - ql + tok : -1;  // last visible key slot of this row
   bf16* const qs = lds + P::Q_OFF + (wave * 32 + col) * P::QLD + hh * 8;
+  // The query row and its position are loaded here; the table rows and the
+  // rotation into LDS come in the first prologue, so that the row's loads,
+  // the first steps' block lookups and then their K/V loads are all in
+  // flight together (a tile's start otherwise waits on a chain of dependent
+  // loads, and a workgroup fills its compute unit alone).
+  Op qop[P::NCH];
   {
-    Op qop[P::NCH];
     const bf16* qp = (const bf16*)a.q + (((size_t)q0 + tok) * a.hq + g * G + head) * D + hh * 8;
-    const int pos = clampi(a.q_pos[q0 + tok], 0, a.max_pos - 1);
-    const float* cr = a.cos_tab + (size_t)pos * (D / 2) + hh * 8;
-    const float* sr = a.sin_tab + (size_t)pos * (D / 2) + hh * 8;
 #pragma unroll
     for (int c = 0; c < P::NCH; ++c) qop[c] = *reinterpret_cast<const Op*>(qp + c * 16);
-#pragma unroll
-    for (int c = 0; c < P::NHC; ++c) {
-      const vec<float, 8> cv = *reinterpret_cast<const vec<float, 8>*>(cr + c * 16);
-      const vec<float, 8> sv = *reinterpret_cast<const vec<float, 8>*>(sr + c * 16);
-      float lo[8], hi[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (float)qop[c][e], y = (float)qop[c + P::NHC][e];
-        lo[e] = (x * cv[e] - y * sv[e]) * a.scale_log2;
-        hi[e] = (y * cv[e] + x * sv[e]) * a.scale_log2;
-      }
-      qop[c] = Mma<bf16>::pack(lo);
-      qop[c + P::NHC] = Mma<bf16>::pack(hi);
-    }
-#pragma unroll
-    for (int c = 0; c < P::NCH; ++c)
-      *reinterpret_cast<Op*>(qs + c * 16) = valid ? qop[c] : Mma<bf16>::zero();
   }
+  const int qpos = clampi(a.q_pos[q0 + tok], 0, a.max_pos - 1);
 
   const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
   const int32_t* kp = ROT ? a.k_pos + a.cu_k[r] : nullptr;
@@ -955,8 +941,11 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
   typedef vec<bf16, P::KPT> KV;
   typedef vec<float, P::KPT> TV;
   typedef vec<bf16, P::VR> VRun;
-  KV klo, khi;
-  TV tc, ts;
+  struct KRegs {
+    KV lo, hi;  // unrotated halves of the thread's K piece
+    TV c, s;    // their cos/sin
+  };
+  KRegs kr;
   VRun vr[P::NVR];
   // Addresses (block ids, position) of the next loads, looked up one step
   // before those loads are issued: kmeta_* / vmeta_* hold the ones in use,
@@ -982,19 +971,27 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
 #pragma unroll
     for (int u = 0; u < P::NVR; ++u) vmeta_blk[u] = vmeta_blk_nx[u];
   };
-  auto kload = [&]() {
+  // the (block, position) of key kb + skey, looked up without touching the
+  // pipeline's *_nx registers
+  auto kmeta_now = [&](int kb, int& blk, int& pos) {
+    const int kc = min(kb + skey, L - 1);
+    blk = bt[kc >> 4];
+    pos = ROT ? kp[kc] : 0;
+  };
+  auto kload_to = [&](KRegs& d, int kblk, int kpos) {
     // an out-of-range id (negative ones wrap to large unsigned values) is
     // clamped to the last valid one
-    const unsigned blk = min((unsigned)kmeta_blk, (unsigned)nb_max);
-    const unsigned pos = min((unsigned)kmeta_pos, (unsigned)pmax);
+    const unsigned blk = min((unsigned)kblk, (unsigned)nb_max);
+    const unsigned pos = min((unsigned)kpos, (unsigned)pmax);
     const char* src = kthr + (size_t)blk * blk_bytes;
-    klo = *reinterpret_cast<const KV*>(src);
-    khi = *reinterpret_cast<const KV*>(src + D);  // + D/2 elements
+    d.lo = *reinterpret_cast<const KV*>(src);
+    d.hi = *reinterpret_cast<const KV*>(src + D);  // + D/2 elements
     if constexpr (ROT) {
-      tc = *reinterpret_cast<const TV*>(cthr + (size_t)pos * (D * 2));  // D/2 floats per row
-      ts = *reinterpret_cast<const TV*>(sthr + (size_t)pos * (D * 2));
+      d.c = *reinterpret_cast<const TV*>(cthr + (size_t)pos * (D * 2));  // D/2 floats per row
+      d.s = *reinterpret_cast<const TV*>(sthr + (size_t)pos * (D * 2));
     }
   };
+  auto kload = [&]() { kload_to(kr, kmeta_blk, kmeta_pos); };
   auto vload = [&]() {
 #pragma unroll
     for (int u = 0; u < P::NVR; ++u) {
@@ -1002,20 +999,21 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
       vr[u] = *reinterpret_cast<const VRun*>(vthr + (size_t)vb * blk_bytes);
     }
   };
-  auto kstore = [&](int step) {  // rotate the loaded K piece into K stage `step`
-    KV lo = klo, hi = khi;
+  auto kstore_from = [&](int step, const KRegs& d) {  // rotate a K piece into K stage `step`
+    KV lo = d.lo, hi = d.hi;
     if constexpr (ROT) {
 #pragma unroll
       for (int e = 0; e < P::KPT; ++e) {
-        const float x = (float)klo[e], y = (float)khi[e];
-        lo[e] = (bf16)(x * tc[e] - y * ts[e]);
-        hi[e] = (bf16)(y * tc[e] + x * ts[e]);
+        const float x = (float)d.lo[e], y = (float)d.hi[e];
+        lo[e] = (bf16)(x * d.c[e] - y * d.s[e]);
+        hi[e] = (bf16)(y * d.c[e] + x * d.s[e]);
       }
     }
     bf16* kd = lds + (step % P::NKB) * P::KBUF + skey * P::KLD + si0;
     *reinterpret_cast<KV*>(kd) = lo;
     *reinterpret_cast<KV*>(kd + D / 2) = hi;
   };
+  auto kstore = [&](int step) { kstore_from(step, kr); };
   auto vstore = [&](int step) {  // the loaded V^T runs into V stage `step`
     const int kb = kofs + step * P::KSTEP;
     bf16* vdst = lds + P::V_OFF + (step % P::NVB) * P::VBUF + vd * P::VLD + vk0;
@@ -1074,24 +1072,51 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
     return fmaxf(mx, __shfl_xor(mx, 32));
   };
-  // the first K stages and V stage; the next loads' addresses
-  auto prologue = [&](bool with_v) {
-    kmeta(kofs);
-    kmeta_use();
-    kload();
+  // The first K stages and V stage (and, with_q, the rotated queries), and
+  // the next loads' addresses.  Every lookup is issued first, then every
+  // data load, then the stores: two memory round trips, not a chain of six.
+  auto prologue = [&](bool with_v, bool with_q) {
+    int b0, p0, b1, p1;
+    kmeta_now(kofs, b0, p0);
+    kmeta_now(kofs + P::KSTEP, b1, p1);
+    if (with_v) vmeta(kofs);
+    vec<float, 8> qc[P::NHC], qsn[P::NHC];
+    if (with_q) {
+      const float* cr = a.cos_tab + (size_t)qpos * (D / 2) + hh * 8;
+      const float* sr = a.sin_tab + (size_t)qpos * (D / 2) + hh * 8;
+#pragma unroll
+      for (int c = 0; c < P::NHC; ++c) {
+        qc[c] = *reinterpret_cast<const vec<float, 8>*>(cr + c * 16);
+        qsn[c] = *reinterpret_cast<const vec<float, 8>*>(sr + c * 16);
+      }
+    }
+    KRegs k1;
+    kload_to(kr, b0, p0);
+    kload_to(k1, b1, p1);
     if (with_v) {
-      vmeta(kofs);
       vmeta_use();
       vload();
     }
-    kstore(0);
-    if (with_v) vstore(0);
-    kmeta(kofs + P::KSTEP);
-    kmeta_use();
-    kload();
-    kstore(1);
     kmeta(kofs + 2 * P::KSTEP);
     if (with_v) vmeta(kofs + P::KSTEP);
+    if (with_q) {
+#pragma unroll
+      for (int c = 0; c < P::NHC; ++c) {
+        float lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)qop[c][e], y = (float)qop[c + P::NHC][e];
+          lo[e] = (x * qc[c][e] - y * qsn[c][e]) * a.scale_log2;
+          hi[e] = (y * qc[c][e] + x * qsn[c][e]) * a.scale_log2;
+        }
+        *reinterpret_cast<Op*>(qs + c * 16) = valid ? Mma<bf16>::pack(lo) : Mma<bf16>::zero();
+        *reinterpret_cast<Op*>(qs + (c + P::NHC) * 16) =
+            valid ? Mma<bf16>::pack(hi) : Mma<bf16>::zero();
+      }
+    }
+    kstore_from(0, kr);
+    kstore_from(1, k1);
+    if (with_v) vstore(0);
     __syncthreads();
   };
   // steps below every row's diagonal (kofs is a multiple of the step)
@@ -1101,7 +1126,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
   auto row_max = [&]() {
     float mx = -INFINITY;
     if (nsteps <= 0) return mx;
-    prologue(false);
+    prologue(false, false);
     const Acc zero = Acc{};
     for (int j = 0; j < nsteps; ++j) {
       kmeta_use();
@@ -1127,10 +1152,9 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
   // by so much that some block's probability sum passes kPBig (or o or l
   // stop being finite), and then the tile is redone as pass 2, whose
   // probabilities are all <= 1.  Returns false (nothing written) on failure.
-  auto attend = [&](bool exact, float m_given) {
-    Acc o[P::NDB];
-#pragma unroll
-    for (int db = 0; db < P::NDB; ++db) o[db] = Acc{};
+  auto attend = [&](auto exact_tag, float m_given) {
+    constexpr bool exact = decltype(exact_tag)::value;
+    Acc o[P::NDB];  // zeroed after the prologue, which needs the registers
     float l_run = 0.0f;
     bool bad = false;
     const vec<bf16, 2> ones = {(bf16)1.0f, (bf16)1.0f};
@@ -1175,9 +1199,9 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     Acc negm = Acc{};  // stays 0 (m = 0) for an item with no keys
     Acc s_next;
     if (nsteps > 0) {
-      prologue(true);
+      prologue(true, !exact);
       float m;
-      if (exact) {
+      if constexpr (exact) {
         m = m_given == -INFINITY ? 0.0f : m_given;
 #pragma unroll
         for (int v = 0; v < 16; ++v) negm[v] = -m;
@@ -1195,6 +1219,9 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
         }
       }
     }
+
+#pragma unroll
+    for (int db = 0; db < P::NDB; ++db) o[db] = Acc{};
 
     // step j: blocks (j, 0) .. (j, NBLK-1); the score MFMAs of the next block
     // run while a block is exponentiated, the PV MFMAs of a block while the
@@ -1271,9 +1298,9 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     return true;
   };
 
-  if (!attend(false, 0.0f)) {
+  if (!attend(std::false_type{}, 0.0f)) {
     const float m = row_max();
-    attend(true, m);
+    attend(std::true_type{}, m);
   }
 }
 
