@@ -93,25 +93,46 @@ def time_config(name, steps, warmup, with_rows=False):
         ev[k][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     step_ms = (t1 - t0) * 1e3 / steps
+    # the call's main kernel alone (decode_kernel / mixed_kernel): the library
+    # records a pair of events right around its launch, on the launch stream
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a_, b_ in kev:
+        a_.record(stream)
+        b_.record(stream)
+    for k in range(steps):
+        dw.write_new_tokens()
+        pic.pic_set_kernel_events(*kev[k])
+        dw.attention()
+    pic.pic_set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
     # cold: before each timed call the 256 MB Infinity Cache is refilled by
     # reading a 512 MiB buffer, so nothing of the previous call is cached and
     # no dirty line has to be written back during the call
     flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
-    cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(max(3, steps // 5))]
+    ncold = max(3, steps // 5)
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ncold)]
+    for e in cold:
+        for x in e[2:]:
+            x.record(stream)
     sink = torch.zeros((), dtype=torch.float32, device="cuda")
-    for k, (a_, b_) in enumerate(cold):
+    for e in cold:
         sink += flush.sum()
-        a_.record(stream)
+        pic.pic_set_kernel_events(e[2], e[3])
+        e[0].record(stream)
         dw.attention()
-        b_.record(stream)
+        e[1].record(stream)
+    pic.pic_set_kernel_events(None, None)
     torch.cuda.synchronize()
-    cold_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in cold]))
+    cold_call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in cold]))
+    cold_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in cold]))
     del flush, sink
     res = dict(name=name, w=w, counts=counts, step_ms=step_ms, kernel_ms=kern_ms,
-               cold_kernel_ms=cold_ms, step_bytes=step_counts(w, counts))
+               call_ms=call_ms, cold_kernel_ms=cold_ms, cold_call_ms=cold_call_ms,
+               step_bytes=step_counts(w, counts))
     if with_rows:
         # the other rows of the path, timed on their own (same stream, events)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -360,17 +381,19 @@ def cpu_baseline(w, counts, budget_s=12.0):
                       f"({dt:.1f} s, numpy fp64, {threads} BLAS threads; {cpu})"}
 
 
-def load_traffic(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if still valid."""
+def load_traffic(kernel: str, config: str):
+    """HBM bytes per launch of `kernel` (the call's main kernel) from the committed
+    rocprofv3 --pmc summaries, if still valid for the current kernel sources."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         data = json.load(f)
-    ent = data.get(kernel)
+    ent = data.get(kernel + ":" + config)
     if not ent or ent.get("source_hash") != source_hash():
         return None
-    return ent["bytes_per_launch"]
+    part = ent.get("parts", {}).get(kernel)
+    return part["bytes"] if part else None
 
 
 def copy_calibration(nbytes: int, reps: int):
@@ -434,12 +457,15 @@ def main():
         value = counts["flops"] / (main_res["step_ms"] * 1e-3) / 1e12
         metric = "prefill TFLOP/s"
         unit = "TFLOP/s"
-    tb = load_traffic(kernel + ":" + args.config)
-    roof["traffic"] = tb
+    roof["traffic"] = load_traffic(kernel, args.config)
     roof["kernel"] = kernel
     roof["kernel_ms"] = main_res["kernel_ms"]
     roof["cold_kernel_ms"] = main_res["cold_kernel_ms"]
     roof["cold_frac"] = roof["frac"] * main_res["kernel_ms"] / main_res["cold_kernel_ms"]
+    # the whole attention call (planning / merge launches included)
+    roof["call_ms"] = main_res["call_ms"]
+    roof["call_frac"] = roof["frac"] * main_res["kernel_ms"] / main_res["call_ms"]
+    roof["cold_call_ms"] = main_res["cold_call_ms"]
     roof["algorithmic_bytes"] = counts["bytes"]
     roof["algorithmic_flops"] = counts["flops"]
 
@@ -452,6 +478,9 @@ def main():
         others[name] = {
             "workload": WORKLOAD_TEXT[name],
             "kernel_ms": r["kernel_ms"], "cold_kernel_ms": r["cold_kernel_ms"],
+            "call_ms": r["call_ms"], "cold_call_ms": r["cold_call_ms"],
+            "call_GBps": c["bytes"] / (r["call_ms"] * 1e-3) / 1e9,
+            "call_TFLOPs": c["flops"] / (r["call_ms"] * 1e-3) / 1e12,
             "step_ms": r["step_ms"],
             "kernel_GBps": c["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9,
             "kernel_hbm_frac": c["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -460,7 +489,7 @@ def main():
             "unique_kv_bytes": c["unique_kv_bytes"], "algorithmic_bytes": c["bytes"],
             "flops": c["flops"],
         }
-        log(f"[bench] {name}: kernel {r['kernel_ms'] * 1e3:.1f} us, "
+        log(f"[bench] {name}: call {r['call_ms'] * 1e3:.1f} us, kernel {r['kernel_ms'] * 1e3:.1f} us, "
             f"{others[name]['kernel_GBps']:.0f} GB/s, {others[name]['kernel_TFLOPs']:.1f} TFLOP/s")
 
     ablation = {}
@@ -499,6 +528,7 @@ def main():
         "cpu_baseline": cpu,
         "rows": {"rope_table_ms": main_res["rope_table_ms"],
                  "cache_write_ms": main_res["cache_write_ms"],
+                 "attention_call_ms": main_res["call_ms"],
                  "attention_kernel_ms": main_res["kernel_ms"]},
         "configs": others,
         "rope_ablation": ablation,

@@ -329,6 +329,20 @@ int pic_decode_num_splits(int seq_len, int dtype);
 int pic_decode_split_len(int seq_len, int dtype);
 
 /*
+ * pic_set_kernel_events -- measurement hook.  While set (both non-null
+ * hipEvent_t handles, passed as void*), every attention call made from the
+ * calling host thread records `before` on its stream immediately before it
+ * launches its main kernel (decode_kernel for pic_attn_decode*,
+ * mixed_kernel for pic_attn_prefill*) and `after` immediately after it, so
+ * hipEventElapsedTime(before, after) is that kernel's duration alone,
+ * without the planning and merge launches of the call.  The setting is per
+ * host thread; both null turns it off.  The events stay owned by the
+ * caller.  Errors: PIC_EINVAL when exactly one handle is null; an attention
+ * call returns PIC_EHIP when recording fails.
+ */
+int pic_set_kernel_events(void* before, void* after);
+
+/*
  * Interleaved span-prefill scheduling (host)
  * ------------------------------------------
  * MiniPIC §2 (the scheduling paragraph after §2.2, ISPS) and §3,

@@ -33,7 +33,7 @@ EXPORTS = [
     "pic_decode_num_splits", "pic_decode_split_len", "pic_cache_write_rotated",
     "pic_attn_decode_rotated", "pic_attn_prefill_rotated", "pic_block_hashes",
     "pic_build_block_tables", "pic_blocks_copy", "pic_sched_create", "pic_sched_destroy",
-    "pic_sched_add_span", "pic_sched_add_request", "pic_sched_step",
+    "pic_sched_add_span", "pic_sched_add_request", "pic_sched_step", "pic_set_kernel_events",
 ]
 PIC_SCHED_ISPS, PIC_SCHED_BARRIER = 0, 1
 PIC_SEQ_SPAN, PIC_SEQ_PROMPT, PIC_SEQ_DECODE = 0, 1, 2
@@ -109,6 +109,7 @@ def _load():
     lib.pic_sched_add_span.argtypes = [c_void, c_int]
     lib.pic_sched_add_request.argtypes = [c_void, ctypes.c_longlong, c_void, c_int, c_int, c_int]
     lib.pic_sched_step.argtypes = [c_void, ctypes.POINTER(_SchedBatch)]
+    lib.pic_set_kernel_events.argtypes = [c_void, c_void]
     lib.pic_decode_num_splits.argtypes = [c_int, c_int]
     lib.pic_decode_split_len.argtypes = [c_int, c_int]
     for name in EXPORTS:
@@ -532,3 +533,22 @@ def pic_decode_num_splits(seq_len: int, dtype: int = PIC_BF16) -> int:
 
 def pic_decode_split_len(seq_len: int, dtype: int = PIC_BF16) -> int:
     return int(_load().pic_decode_split_len(seq_len, dtype))
+
+
+def pic_set_kernel_events(before=None, after=None) -> None:
+    """Record two torch.cuda.Event objects around the main kernel of every following
+    attention call on this thread (None, None turns it off); elapsed_time(before, after)
+    is then that kernel's duration alone.  An event whose HIP event does not exist yet
+    (torch creates it on first record) is recorded once here."""
+    lib = _load()
+    if (before is None) != (after is None):
+        raise ValueError("pass both events or neither")
+    if before is None:
+        _check(lib.pic_set_kernel_events(None, None), "pic_set_kernel_events")
+        return
+    for e in (before, after):
+        if not e.cuda_event:
+            e.record()
+    _check(lib.pic_set_kernel_events(ctypes.c_void_p(before.cuda_event),
+                                     ctypes.c_void_p(after.cuda_event)),
+           "pic_set_kernel_events")

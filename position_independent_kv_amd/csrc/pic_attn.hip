@@ -1620,6 +1620,17 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
 // host side
 // ---------------------------------------------------------------------------
 
+// Measurement hook (pic_set_kernel_events): events recorded around the main
+// kernel of each attention call made from this host thread.
+static thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+
+static bool record_before(hipStream_t s) {
+  return !g_ev_before || hipEventRecord(g_ev_before, s) == hipSuccess;
+}
+static bool record_after(hipStream_t s) {
+  return !g_ev_after || hipEventRecord(g_ev_after, s) == hipSuccess;
+}
+
 static AttnArgs make_args(const AttnHostArgs& h, const WorkspaceLayout& w) {
   AttnArgs a{};
   a.q = h.q;
@@ -1671,9 +1682,11 @@ template <typename T, int D, bool ROT>
 static int launch_decode(const AttnArgs& a, hipStream_t s) {
   const long long n = (long long)a.num_reqs * a.s_max * a.nhg;
   if (n > 0x7fffffffLL || (long long)a.num_reqs * a.hkv > 0x7fffffffLL) return PIC_EUNSUPPORTED;
+  bool ok = record_before(s);
   hipLaunchKernelGGL((decode_kernel<T, D, ROT>), dim3((unsigned)n), dim3(kThreads), 0, s, a);
+  ok = record_after(s) && ok;
   launch_combine<T, D>(a, s);
-  return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
+  return hipGetLastError() == hipSuccess && ok ? PIC_OK : PIC_EHIP;
 }
 
 template <typename T, int D, bool ROT>
@@ -1689,8 +1702,10 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
                      Cfg<T, D>::KSTEP, prefill_rows<T, D>(), len_cap,
                      w.max_items, (int4*)(ws + w.items_off), (int*)(ws + w.count_off),
                      a.pf_tiles, a.pf_count);
+  bool ok = record_before(s);
   hipLaunchKernelGGL((mixed_kernel<T, D, ROT>), dim3((unsigned)w.max_items),
                      dim3(64 * mixed_waves<T>()), 0, s, a);
+  ok = record_after(s) && ok;
   // Every request has q_len >= total_q - (num_reqs - 1) * max_q_len; when that
   // bound is at least 2 the batch has no decode rows and nothing to merge.
   const long long min_q_len =
@@ -1702,7 +1717,7 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
     b.s_max = 1;  // no decode merges
     launch_combine<T, D>(b, s, kSplitCUs / 2);
   }
-  return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
+  return hipGetLastError() == hipSuccess && ok ? PIC_OK : PIC_EHIP;
 }
 
 // One decode call: position-free (ROT) or over an already rotated cache.
@@ -1746,6 +1761,13 @@ static int attn_prefill(const AttnHostArgs& h, hipStream_t s) {
 }  // namespace pic
 
 using pic::AttnHostArgs;
+
+extern "C" int pic_set_kernel_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return PIC_EINVAL;
+  pic::g_ev_before = (hipEvent_t)before;
+  pic::g_ev_after = (hipEvent_t)after;
+  return PIC_OK;
+}
 
 extern "C" int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool,
                                const void* v_pool, const int32_t* block_table,

@@ -28,7 +28,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = pic.library()
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(pic.EXPORTS)
@@ -39,6 +39,16 @@ def test_status_strings():
         assert isinstance(pic.pic_status_string(st), str)
     assert pic.pic_status_string(-3).startswith("PIC_EWORKSPACE")
     assert pic.pic_version() >= 100
+
+
+def test_kernel_events_hook_arguments():
+    """pic_set_kernel_events takes both handles or neither (host only, no HIP call)."""
+    lib = pic.library()
+    assert lib.pic_set_kernel_events(None, ctypes.c_void_p(16)) == pic.PIC_EINVAL
+    assert lib.pic_set_kernel_events(ctypes.c_void_p(16), None) == pic.PIC_EINVAL
+    assert lib.pic_set_kernel_events(None, None) == pic.PIC_OK
+    with pytest.raises(ValueError):
+        pic.pic_set_kernel_events(object(), None)
 
 
 def test_workspace_size_rules():

@@ -320,3 +320,30 @@ def test_single_key_context():
         blk = int(w.block_table[r, 0])
         for h in range(w.hq):
             assert _same_bits(got[r, h], dw.v_pool[blk, h // G, :, 0]), (r, h)
+
+
+@pytest.mark.parametrize("kw", [SMALL_DEC, SMALL_MIX], ids=["decode", "mixed"])
+def test_kernel_events_bracket_the_main_kernel(kw):
+    """With the measurement hook set, the call's results are unchanged and the events
+    span the main kernel only: a positive time no longer than the whole call."""
+    torch = _torch()
+    w, dw = _fresh(kw)
+    base = _rerun(dw)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    stream = torch.cuda.current_stream()
+    pic.pic_set_kernel_events(ev[2], ev[3])
+    try:
+        ev[0].record(stream)
+        out = torch.empty_like(dw.out)
+        dw.attention(out=out)
+        ev[1].record(stream)
+    finally:
+        pic.pic_set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    assert _same_bits(out, base)
+    kern, call = ev[2].elapsed_time(ev[3]), ev[0].elapsed_time(ev[1])
+    assert 0.0 < kern <= call
+    # with the hook off the events are left alone
+    before = ev[2].elapsed_time(ev[3])
+    _rerun(dw)
+    assert ev[2].elapsed_time(ev[3]) == before
