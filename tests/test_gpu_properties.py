@@ -347,3 +347,66 @@ def test_kernel_events_bracket_the_main_kernel(kw):
     before = ev[2].elapsed_time(ev[3])
     _rerun(dw)
     assert ev[2].elapsed_time(ev[3]) == before
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_needle_at_maximum_sizes(kind):
+    """Indexing at sizes far past the benchmark configs: 3 requests of 2^20 + 37 keys each
+    (65,539 blocks per request, 196,617 in the pool, ~3.2 GB of K/V), positions drawn from
+    [0, 2^21) with a 2^21 + 1-row table (1 GiB).  One needle per request, at the first slot,
+    in the middle and at the last slot; the query shares the needle's position, so its
+    score dominates and every row that sees it must return that slot's V row bit for bit.
+    Prefill runs 40 query rows per request: 6 tiles, so each tile's keys are split into
+    chunks merged by the combine launch."""
+    torch = _torch()
+    rng = np.random.default_rng(11)
+    hkv, G, d, B = 2, 4, 128, 16
+    hq = hkv * G
+    L = (1 << 20) + 37
+    max_pos = (1 << 21) + 1
+    needles = [0, L // 2 + 5, L - 1]
+    R = len(needles)
+    nb_req = -(-L // B)
+    nblocks = R * nb_req
+    perm = rng.permutation(nblocks).astype(np.int32)
+    block_table = perm.reshape(R, nb_req)
+    k_pool = torch.zeros((nblocks, hkv, B, d), dtype=torch.bfloat16, device="cuda")
+    v_pool = torch.randn((nblocks, hkv, d, B), device="cuda").to(torch.bfloat16)
+    t_pos = max_pos - 1
+    k_pos = rng.integers(0, max_pos - 1, size=(R, L)).astype(np.int32)
+    qv = torch.randn((hkv, d))
+    q1 = qv[:, None, :].expand(hkv, G, d).reshape(hq, d)
+    qf = q1.to(torch.bfloat16).float().view(hkv, G, d)[:, 0, :]
+    c = 200.0 * np.sqrt(d) / float((qf * qf).sum(-1).min())
+    for r, j in enumerate(needles):
+        k_pos[r, j] = t_pos
+        k_pool[int(block_table[r, j // B]), :, j % B, :] = (qf * c).to(torch.bfloat16).cuda()
+    cos = torch.empty((max_pos, d // 2), dtype=torch.float32, device="cuda")
+    sin = torch.empty_like(cos)
+    pic.pic_rope_table(cos, sin, 500000.0)
+    seq = np.full(R, L, np.int32)
+    cu_k = (np.arange(R + 1, dtype=np.int64) * L).astype(np.int32)
+    ql = 1 if kind == "decode" else 40
+    q = q1[None].expand(R * ql, hq, d).contiguous().to(torch.bfloat16).cuda()
+    q_pos = i32(np.full(R * ql, t_pos, np.int32))
+    out = torch.empty_like(q)
+    ws = torch.zeros(pic.pic_attn_workspace_size(R, R * ql, L, hq, hkv, d, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    args = (k_pool, v_pool, i32(block_table), i32(seq), i32(cu_k), i32(k_pos.reshape(-1)),
+            cos, sin)
+    if kind == "decode":
+        pic.pic_attn_decode(q, q_pos, *args, L, out, ws)
+    else:
+        cu_q = i32((np.arange(R + 1) * ql).astype(np.int32))
+        pic.pic_attn_prefill(q, cu_q, q_pos, *args, ql, L, out, ws)
+    torch.cuda.synchronize()
+    checked = 0
+    for r, j in enumerate(needles):
+        want = v_pool[int(block_table[r, j // B]), :, :, j % B]
+        for i in range(ql):
+            if j <= L - ql + i:  # the row sees the needle
+                got = out[r * ql + i].view(hkv, G, d)
+                for h in range(hq):
+                    assert _same_bits(got[h // G, h % G], want[h // G]), (kind, r, j, i, h)
+                checked += 1
+    assert checked >= R
