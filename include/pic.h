@@ -17,8 +17,9 @@
  * - Pointers: every array argument is DEVICE memory owned by the caller,
  *   unless the argument is documented as host memory.  The library never
  *   allocates or frees device memory and keeps no state between calls; the
- *   one exception is the host-side scheduler object of pic_sched_* (plain
- *   host memory, created and destroyed by the caller's calls).
+ *   exceptions are the host-side scheduler object of pic_sched_* (plain
+ *   host memory, created and destroyed by the caller's calls) and the
+ *   per-thread measurement events of pic_set_kernel_events.
  * - stream: a hipStream_t (NULL = the legacy default stream).  Every call
  *   only enqueues work on that stream and returns without synchronising the
  *   host.

@@ -1,4 +1,5 @@
-// Position-free paged attention for gfx950: pic_attn_decode, pic_attn_prefill.
+// Position-free paged attention for gfx950: pic_attn_decode, pic_attn_prefill
+// and their rotated-cache variants (key rotation compiled out).
 //
 // What is computed (MiniPIC §2.1, score equation): for query row t of a
 // request and each of its key slots j,
@@ -12,28 +13,36 @@
 // (MiniPIC §2.1, Implementation bullet).
 //
 // Formulation on the matrix cores (per kv head g and group of q heads):
-//     S^T = K_rot * Q_rot^T      A = rotated keys (16 keys x d), B = queries
+//     S^T = K_rot * Q_rot^T      A = rotated keys (keys x d), B = queries
 //     O^T += V^T * P^T           A = values transposed (d x keys), B = probs
 // Keys are the M dimension of the score tile, so the score accumulator lands
 // in exactly the register layout the PV product wants for its B operand (no
 // shuffles), and V^T is read straight from the pool because the pool stores
 // V transposed inside each block.  The rotation pairs element i with i + d/2;
 // in this operand layout both halves of a pair sit in the same lane, so the
-// rotation is a handful of FMAs on registers right after the load.
+// rotation is a handful of FMAs on registers.
 //
-// Decode (one query row per request, memory bound): one wave per
-// (request, kv head, key chunk), the G query heads of the kv head are the
-// columns of the tile; K, V and the table row are read from global memory.
-// Chunks of one request are merged in the same kernel: each chunk writes its
-// normalised partial output and (max, sum) to the workspace, and the last
-// workgroup of a (request, head group) to arrive merges them.
-//
-// Prefill (q_len > 1, MFMA bound): one workgroup per (request, kv head,
-// 128 query rows); the rows are (token, q head of the group) pairs, 32 per
-// wave.  Each 32-key step is gathered from the paged pool once per
-// workgroup, rotated while it is written to LDS as the MFMA operand, and
-// shared by the four waves; V^T is staged in LDS next to it.  Online softmax
-// keeps one running max/sum per row.
+// Kernels:
+// - decode_kernel (batches of q_len == 1, HBM bound): one workgroup of four
+//   waves per (request, key chunk of about 384 keys, four kv heads), one wave
+//   per kv head, the G query heads of the kv head as the columns of a
+//   16x16x32 tile.  The chunk's block ids and positions, and each 32-key
+//   step's cos/sin rows, are staged in LDS once per workgroup; every wave
+//   loads its own head's K rows and V runs into registers.  A request split
+//   into several chunks writes normalised partials and (max, sum) to the
+//   workspace; combine_kernel merges them.
+// - plan_kernel + mixed_kernel (any mix of q_len): the planner turns
+//   (cu_seqlens_q, seq_lens) into a work list of prefill tiles and decode
+//   chunks, and one mixed_kernel launch runs both kinds.  A bf16 prefill tile
+//   is one workgroup of eight waves per (request, kv head, 256 query rows:
+//   (token, group head) pairs, 32 per wave) on 32x32x16 MFMAs; each 64-key
+//   step is gathered from the pool once per workgroup, rotated on its way
+//   into LDS and shared by the eight waves.  Its softmax exponentiates
+//   against a fixed per-row reference and redoes the tile with the exact row
+//   maximum in the rare case a later score overflows that reference.  A
+//   launch with few tiles splits long tiles into key chunks, merged by
+//   combine_kernel.  fp32 tiles use four waves, 128 rows and an online
+//   softmax.
 #include <hip/hip_runtime.h>
 #include <math.h>
 

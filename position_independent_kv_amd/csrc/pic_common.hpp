@@ -12,7 +12,7 @@ namespace pic {
 constexpr int kBlockSize = 16;      // tokens per KV block
 constexpr int kWaves = 4;           // waves (of 64 lanes) per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPrefillRows = 128;   // query rows (tokens x group heads) per prefill tile
+constexpr int kPrefillRows = 128;   // query rows (tokens x group heads) per fp32 prefill tile
 constexpr int kSplitTarget = 384;   // target keys per decode chunk (one workgroup)
 constexpr int kMaxGroup = 16;       // q heads per kv head held in one MFMA column tile
 
