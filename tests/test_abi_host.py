@@ -295,3 +295,52 @@ int main() {
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "fails=0" in res.stdout
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include <string.h>
+#include "pic.h"
+
+int main(void) {
+    int32_t tokens[40];
+    uint64_t h1[2], h2[2];
+    int i, n;
+    for (i = 0; i < 40; ++i) tokens[i] = 1000 + i;
+    if (pic_version() <= 0) return 1;
+    if (strncmp(pic_status_string(PIC_EWORKSPACE), "PIC_EWORKSPACE", 14) != 0) return 2;
+    if (pic_attn_workspace_size(64, 64, 4097, 32, 8, 128, PIC_BF16) == 0) return 3;
+    if (pic_decode_num_splits(4097, PIC_BF16) < 1) return 4;
+    /* two full blocks of 16 tokens, the 8-token tail is not hashed */
+    n = pic_block_hashes(tokens, 40, 16, -1, -1, 7u, h1);
+    if (n != 2) return 5;
+    if (pic_block_hashes(tokens, 40, 16, -1, -1, 7u, h2) != 2) return 6;
+    if (h1[0] != h2[0] || h1[1] != h2[1] || h1[0] == h1[1]) return 7;
+    /* an attention call with a null workspace is rejected before any launch */
+    if (pic_attn_decode(tokens, tokens, tokens, tokens, tokens, 1, tokens, tokens, tokens,
+                        (const float*)tokens, (const float*)tokens, 8, 1, 4, 4, 64, 16, 1, 16,
+                        PIC_F32, tokens, NULL, 0, NULL) != PIC_EWORKSPACE) return 8;
+    printf("ok %d\n", pic_version());
+    return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not installed")
+def test_header_is_c99_and_the_library_links_from_c(tmp_path):
+    """The boundary is a C ABI: include/pic.h compiles as strict C99 and a C program linked
+    against libpic.so calls its host-side entry points (no GPU work)."""
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    lib_dir = os.path.dirname(pic.LIB_PATH)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+           os.path.join(ROOT, "include"), str(src), "-L", lib_dir, "-lpic",
+           f"-Wl,-rpath,{lib_dir}", "-o", str(exe)]
+    if not os.path.exists(os.path.join(lib_dir, "libpic.so")):
+        pytest.skip("libpic.so is not built")
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
+    assert run.stdout.startswith("ok ")
