@@ -198,6 +198,58 @@ def rope_ablation(name, reps=20):
     return res
 
 
+def shared_decode(name, reps=20):
+    """pic_attn_decode_shared against pic_attn_decode on one decode config: chunks cut
+    where the blocks say and identical chunks side by side on one XCD, so shared spans are
+    read once per XCD.  Calls alternate; main kernel (library-recorded events) and whole
+    call (planning and merge launches included), medians of `reps`."""
+    import torch
+
+    import position_independent_kv_amd as pic
+    from tests.gpu_harness import DeviceWorkload
+    from workloads import algorithmic_counts, make_workload
+
+    w = make_workload(name)
+    counts = algorithmic_counts(w)
+    dw = DeviceWorkload(w)
+    dw.write_new_tokens()
+    stream = torch.cuda.current_stream()
+    calls = {"uniform_chunks": dw.attention, "shared_chunks": dw.attention_shared}
+    for fn in calls.values():
+        for _ in range(3):
+            fn()
+    torch.cuda.synchronize()
+    ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+          for k in calls}
+    for k in calls:
+        for e in ev[k]:
+            for x in e:
+                x.record(stream)
+    for i in range(reps):
+        for k, fn in calls.items():
+            e = ev[k][i]
+            pic.pic_set_kernel_events(e[1], e[2])
+            e[0].record(stream)
+            fn()
+            e[3].record(stream)
+    pic.pic_set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    res = {"workload": WORKLOAD_TEXT[name]}
+    for k in calls:
+        kern = float(np.median([e[1].elapsed_time(e[2]) for e in ev[k]]))
+        call = float(np.median([e[0].elapsed_time(e[3]) for e in ev[k]]))
+        res[k] = {"kernel_ms": kern, "call_ms": call,
+                  "kernel_GBps": counts["bytes"] / (kern * 1e-3) / 1e9}
+    res["kernel_speedup"] = res["uniform_chunks"]["kernel_ms"] / res["shared_chunks"]["kernel_ms"]
+    res["call_speedup"] = res["uniform_chunks"]["call_ms"] / res["shared_chunks"]["call_ms"]
+    log(f"[bench] shared decode {name}: main kernel {res['uniform_chunks']['kernel_ms'] * 1e3:.1f}"
+        f" -> {res['shared_chunks']['kernel_ms'] * 1e3:.1f} us, call "
+        f"{res['uniform_chunks']['call_ms'] * 1e3:.1f} -> {res['shared_chunks']['call_ms'] * 1e3:.1f} us")
+    del dw
+    torch.cuda.empty_cache()
+    return res
+
+
 def offload_bandwidth(n_blocks=4096, reps=5):
     """pic_blocks_copy between the device pools and a pinned host pool (CPU offload of
     position-free blocks): n_blocks whole blocks of the default layer shape (K+V = 64 KiB
@@ -417,6 +469,8 @@ def main():
                     help="comma list of further configs reported under 'configs' ('' for none)")
     ap.add_argument("--ablation", default="c2p,c3,c4",
                     help="configs on which to time the in-kernel rotation ablation ('' for none)")
+    ap.add_argument("--shared", default="c2,c4",
+                    help="decode configs on which to compare pic_attn_decode_shared ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sched", action="store_true",
                     help="skip the scheduled-trace comparison (ISPS vs barrier)")
@@ -495,6 +549,9 @@ def main():
     ablation = {}
     for name in [x for x in args.ablation.split(",") if x]:
         ablation[name] = rope_ablation(name)
+    shared = {}
+    for name in [x for x in args.shared.split(",") if x]:
+        shared[name] = shared_decode(name)
     tables = block_table_build()
     sched = None if args.no_sched else scheduled_trace()
     ceil = ceilings()
@@ -532,6 +589,7 @@ def main():
                  "attention_kernel_ms": main_res["kernel_ms"]},
         "configs": others,
         "rope_ablation": ablation,
+        "shared_decode": shared,
         "block_tables": tables,
         "scheduled_trace": sched,
         "ceilings": ceil,

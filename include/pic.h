@@ -152,6 +152,40 @@ int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool, con
                     size_t workspace_bytes, void* stream);
 
 /*
+ * pic_attn_decode_shared -- pic_attn_decode with the key chunks of each
+ * request cut where its blocks say, so that blocks shared by several requests
+ * are read once per XCD instead of once per request (MiniPIC §2.1: one
+ * physical block serves concurrent requests at different offsets).  A block
+ * whose physical id hashes to a fixed residue (probability 1/16) starts a new
+ * chunk unless another such block lies among the 7 blocks before it; gaps
+ * longer than 36 blocks are cut into equal parts.  Two requests holding the
+ * same span at different offsets therefore cut it at the same blocks, and a
+ * planner groups chunks by their first physical block so that identical
+ * chunks run side by side on one XCD and the later ones find the span in
+ * that XCD's L2.  The chunking depends only on the request's own block table,
+ * so a request's output does not depend on the rest of the batch; it differs
+ * from pic_attn_decode's by floating-point rounding only.  Arguments,
+ * layouts and preconditions as in pic_attn_decode, except the workspace:
+ *   workspace >= pic_attn_decode_shared_workspace_size(num_reqs, max_seq_len,
+ *                                                      Hq, Hkv, head_dim, dtype)
+ * PIC_EUNSUPPORTED when a context spans more than 65536 blocks (1,048,576
+ * keys).  Three small launches (chunking, ordering, merge) surround the
+ * decode kernel.
+ */
+int pic_attn_decode_shared(const void* q, const int32_t* q_pos, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table,
+                           int block_table_stride, const int32_t* seq_lens,
+                           const int32_t* cu_seqlens_k, const int32_t* k_pos,
+                           const float* cos_tab, const float* sin_tab, int max_pos,
+                           int num_reqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int max_seq_len, int dtype,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream);
+/* Bytes of workspace pic_attn_decode_shared needs; 0 for unsupported shapes
+ * or dtypes, or a max_seq_len beyond 65536 blocks. */
+size_t pic_attn_decode_shared_workspace_size(int num_reqs, int max_seq_len, int num_q_heads,
+                                             int num_kv_heads, int head_dim, int dtype);
+
+/*
  * pic_attn_prefill -- any mix of requests in ONE launch (chunked prefill,
  * span prefill, and q_len == 1 decodes side by side: the interleaved
  * span-prefill schedule of MiniPIC §2.2 "Scheduling" puts span prefills and
@@ -333,7 +367,8 @@ int pic_decode_split_len(int seq_len, int dtype);
  * pic_set_kernel_events -- measurement hook.  While set (both non-null
  * hipEvent_t handles, passed as void*), every attention call made from the
  * calling host thread records `before` on its stream immediately before it
- * launches its main kernel (decode_kernel for pic_attn_decode*,
+ * launches its main kernel (decode_kernel for pic_attn_decode and
+ * pic_attn_decode_rotated, decode_shared_kernel for pic_attn_decode_shared,
  * mixed_kernel for pic_attn_prefill*) and `after` immediately after it, so
  * hipEventElapsedTime(before, after) is that kernel's duration alone,
  * without the planning and merge launches of the call.  The setting is per

@@ -34,6 +34,7 @@ EXPORTS = [
     "pic_attn_decode_rotated", "pic_attn_prefill_rotated", "pic_block_hashes",
     "pic_build_block_tables", "pic_blocks_copy", "pic_sched_create", "pic_sched_destroy",
     "pic_sched_add_span", "pic_sched_add_request", "pic_sched_step", "pic_set_kernel_events",
+    "pic_attn_decode_shared", "pic_attn_decode_shared_workspace_size",
 ]
 PIC_SCHED_ISPS, PIC_SCHED_BARRIER = 0, 1
 PIC_SEQ_SPAN, PIC_SEQ_PROMPT, PIC_SEQ_DECODE = 0, 1, 2
@@ -110,6 +111,9 @@ def _load():
     lib.pic_sched_add_request.argtypes = [c_void, ctypes.c_longlong, c_void, c_int, c_int, c_int]
     lib.pic_sched_step.argtypes = [c_void, ctypes.POINTER(_SchedBatch)]
     lib.pic_set_kernel_events.argtypes = [c_void, c_void]
+    lib.pic_attn_decode_shared.argtypes = lib.pic_attn_decode.argtypes
+    lib.pic_attn_decode_shared_workspace_size.restype = c_size
+    lib.pic_attn_decode_shared_workspace_size.argtypes = [c_int] * 6
     lib.pic_decode_num_splits.argtypes = [c_int, c_int]
     lib.pic_decode_split_len.argtypes = [c_int, c_int]
     for name in EXPORTS:
@@ -258,6 +262,27 @@ def _pool_dims(k_pool, v_pool):
 def pic_attn_decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens_k, k_pos,
                     cos_tab, sin_tab, max_seq_len, out, workspace, stream=None):
     """One query row per request: q, out [R][Hq][d]; metadata int32 device tensors."""
+    _decode_call("pic_attn_decode", q, q_pos, k_pool, v_pool, block_table, seq_lens,
+                 cu_seqlens_k, k_pos, cos_tab, sin_tab, max_seq_len, out, workspace, stream)
+
+
+def pic_attn_decode_shared(q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens_k,
+                           k_pos, cos_tab, sin_tab, max_seq_len, out, workspace, stream=None):
+    """pic_attn_decode with block-determined chunks, identical chunks co-scheduled on one XCD;
+    the workspace is sized by pic_attn_decode_shared_workspace_size."""
+    _decode_call("pic_attn_decode_shared", q, q_pos, k_pool, v_pool, block_table, seq_lens,
+                 cu_seqlens_k, k_pos, cos_tab, sin_tab, max_seq_len, out, workspace, stream)
+
+
+def pic_attn_decode_shared_workspace_size(num_reqs, max_seq_len, num_q_heads, num_kv_heads,
+                                          head_dim, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
+    return int(_load().pic_attn_decode_shared_workspace_size(
+        num_reqs, max_seq_len, num_q_heads, num_kv_heads, head_dim, code))
+
+
+def _decode_call(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens_k, k_pos,
+                 cos_tab, sin_tab, max_seq_len, out, workspace, stream):
     torch = _torch()
     i32 = torch.int32
     R, hq, d = q.shape
@@ -266,7 +291,7 @@ def pic_attn_decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens_
         raise ValueError("q / out / pool head sizes disagree")
     if block_table.dim() != 2 or block_table.shape[0] < R:
         raise ValueError("block_table must be [R][stride]")
-    _check(_load().pic_attn_decode(
+    _check(getattr(_load(), fn)(
         _ptr(q, "q"), _ptr(q_pos, "q_pos", i32), _ptr(k_pool, "k_pool", q.dtype),
         _ptr(v_pool, "v_pool", q.dtype), _ptr(block_table, "block_table", i32),
         block_table.shape[1], _ptr(seq_lens, "seq_lens", i32),
@@ -274,7 +299,7 @@ def pic_attn_decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens_
         _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
         cos_tab.shape[0], R, hq, hkv, d, bs, nb, int(max_seq_len), _dtype_code(q),
         _ptr(out, "out"), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _stream(stream)), "pic_attn_decode")
+        _stream(stream)), fn)
 
 
 def pic_attn_prefill(q, cu_seqlens_q, q_pos, k_pool, v_pool, block_table, seq_lens,

@@ -90,6 +90,10 @@ struct AttnArgs {
   float* pf_o;
   int4* pf_tiles;
   int* pf_count;
+  // chunk table of the shared-span decode (null elsewhere): chunks per
+  // request, and per request s_max + 1 chunk start blocks
+  const int* cdc_count;
+  const int* cdc_start;
 };
 
 // Work item x field: kind in bits 0-3; for a split prefill tile the split
@@ -290,6 +294,15 @@ constexpr int kMaxChunk = kSplitTarget + kSplitTarget / 2 + 32;
 // LDS of a decode workgroup: the chunk's key positions and block ids, and
 // the cos/sin rows of two steps (one row per key of the step, padded so the
 // 16 rows one read instruction touches fall in different banks).
+constexpr int kCdcMaxKeys = kCdcMaxGap * kBlockSize;  // keys of the longest shared-span chunk
+static_assert(kCdcMaxKeys <= kMaxChunk, "a shared-span chunk fits the decode's LDS staging");
+
+// chunks of request r (L keys): from the table, or the uniform split
+__device__ __forceinline__ int chunks_of(const AttnArgs& a, int r, int L, int kstep) {
+  if (a.cdc_count) return min(max(a.cdc_count[r], 1), a.s_max);
+  return num_splits(L, kstep);
+}
+
 template <typename T, int D>
 struct DecodeSmem {
   static constexpr int KSTEP = Cfg<T, D>::KSTEP;
@@ -332,7 +345,7 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   const int ga = active ? g : 0;  // a valid head for the loads of an idle wave
   const int G = a.group;
   const int L = seq_len_of(a, r);
-  const int S = num_splits(L, C::KSTEP);
+  const int S = chunks_of(a, r, L, C::KSTEP);
   if (s >= S) return;
   if (L <= 0) {  // empty context: zero output
     if (active) {
@@ -341,9 +354,18 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     }
     return;
   }
-  const int chunk = split_len(L, C::KSTEP);
-  const int k0 = s * chunk;
-  const int k1 = min(L, k0 + chunk);
+  int k0, k1;
+  if (a.cdc_start) {  // block-aligned chunk from the table, at most kCdcMaxKeys keys
+    const int* st = a.cdc_start + (size_t)r * (a.s_max + 1);
+    const int nb = cdiv(L, kBlockSize);
+    k0 = min(max(st[s], 0), nb) * kBlockSize;
+    k1 = min(min(L, min(max(st[s + 1], 0), nb) * kBlockSize), k0 + kCdcMaxKeys);
+    if (k1 <= k0) return;
+  } else {
+    const int chunk = split_len(L, C::KSTEP);
+    k0 = s * chunk;
+    k1 = min(L, k0 + chunk);
+  }
   const int nsteps = cdiv(k1 - k0, C::KSTEP);
 
   // chunk metadata -> LDS: positions of keys k0.., block ids of blocks k0/16..
@@ -572,7 +594,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a, int dec_b
   if (a.cu_q && a.cu_q[r + 1] - a.cu_q[r] != 1) return;
   const long long qrow = a.cu_q ? (long long)a.cu_q[r] : (long long)r;
   const int L = seq_len_of(a, r);
-  const int S = num_splits(L, Cfg<T, D>::KSTEP);
+  const int S = chunks_of(a, r, L, Cfg<T, D>::KSTEP);
   if (L <= 0 || S <= 1) return;
   const int G = a.group;
   const int pairs = G * (D / EPT);
@@ -1364,6 +1386,271 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
   decode_item<T, D, kDecodeDepth, kWaves, ROT>(a, r, hg, s, r, smem);
 }
 
+// ---------------------------------------------------------------------------
+// shared-span decode: planner and launch
+// ---------------------------------------------------------------------------
+
+// 32-bit finaliser of MurmurHash3 (Appleby): spreads a block id's bits so
+// that the low bits decide cut candidates independently of how ids were
+// allocated.
+__device__ __forceinline__ unsigned cdc_mix(unsigned x) {
+  x ^= x >> 16;
+  x *= 0x85ebca6bu;
+  x ^= x >> 13;
+  x *= 0xc2b2ae35u;
+  x ^= x >> 16;
+  return x;
+}
+
+__device__ __forceinline__ bool bit_of(const unsigned* w, int b) { return (w[b >> 5] >> (b & 31)) & 1u; }
+
+// Exclusive scan of one int per thread across a workgroup of NT threads
+// (NT / 64 waves, at most 64); tot gets the total.
+template <int NT>
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* s_w, int& tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_w[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int t = lane < NT / 64 ? s_w[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(t, o);
+      if (lane >= o) t += y;
+    }
+    if (lane < NT / 64) s_w[64 + lane] = t;
+  }
+  __syncthreads();
+  tot = s_w[64 + NT / 64 - 1];
+  const int before = wave > 0 ? s_w[64 + wave - 1] : 0;
+  __syncthreads();
+  return before + x - v;
+}
+
+// One workgroup per request: the request's chunk start blocks.  Block b > 0
+// is a cut when its id is a candidate and none of the kCdcMinGap - 1 blocks
+// before it is one; so the cuts inside a span depend only on the span's own
+// blocks (past its first kCdcMinGap - 1), whatever precedes it.  Gaps longer
+// than kCdcMaxGap blocks are split into equal parts.  Writes cdc_count[r]
+// and cdc_start[r][0 .. count] (the last entry is the block count).
+__global__ void __launch_bounds__(1024) cdc_chunk_kernel(AttnArgs a, int* cdc_count,
+                                                         int* cdc_start) {
+  constexpr int NT = 1024;
+  constexpr int NW = kCdcMaxBlocks / 32;
+  __shared__ unsigned s_cand[NW];
+  __shared__ unsigned s_cut[NW];
+  __shared__ int s_pos[kCdcMaxBlocks / kCdcMinGap + 3];  // start, cuts (at most (nb - 2) / gap + 1), end
+  __shared__ int s_w[128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.x;
+  const int L = seq_len_of(a, r);
+  const int nb = min(cdiv(max(L, 0), kBlockSize), kCdcMaxBlocks);
+  int* start = cdc_start + (size_t)r * (a.s_max + 1);
+  if (nb <= 1) {
+    if (tid == 0) {
+      cdc_count[r] = 1;
+      start[0] = 0;
+      start[1] = nb;
+    }
+    return;
+  }
+  const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
+  const int nw = cdiv(nb, 32);
+  // candidates: each wave takes 4 x 64 consecutive blocks at a time (coalesced
+  // ids, four loads in flight per lane)
+  for (int b0 = wave * 256; b0 < nb; b0 += NT * 4) {
+    int id[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = b0 + u * 64 + lane;
+      id[u] = b < nb ? bt[b] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int bu = b0 + u * 64;
+      const bool c = bu + lane < nb && (cdc_mix((unsigned)id[u]) & kCdcCandMask) == 0;
+      const unsigned long long m = __ballot(c);
+      if (lane == 0 && bu < nb) {
+        s_cand[bu >> 5] = (unsigned)m;
+        if ((bu >> 5) + 1 < NW) s_cand[(bu >> 5) + 1] = (unsigned)(m >> 32);
+      }
+    }
+  }
+  __syncthreads();
+  for (int b0 = wave * 64; b0 < nb; b0 += NT) {
+    const int b = b0 + lane;
+    bool c = b >= 1 && b < nb && bit_of(s_cand, b);
+    for (int k = 1; k < kCdcMinGap; ++k) c = c && (b - k < 0 || !bit_of(s_cand, b - k));
+    const unsigned long long m = __ballot(c);
+    if (lane == 0) {
+      s_cut[b0 >> 5] = (unsigned)m;
+      if ((b0 >> 5) + 1 < NW) s_cut[(b0 >> 5) + 1] = (unsigned)(m >> 32);
+    }
+  }
+  __syncthreads();
+  // cut positions in order: thread t owns words [t*per, (t+1)*per)
+  const int per = cdiv(nw, NT);
+  const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(s_cut[w]);
+  int ncut;
+  int k = 1 + wg_exclusive_scan<NT>(cnt, s_w, ncut);
+  for (int w = w0; w < w1; ++w) {
+    unsigned bits = s_cut[w];
+    while (bits) {
+      s_pos[k++] = w * 32 + (__ffs(bits) - 1);
+      bits &= bits - 1;
+    }
+  }
+  if (tid == 0) {
+    s_pos[0] = 0;
+    s_pos[ncut + 1] = nb;
+  }
+  __syncthreads();
+  // gaps between consecutive boundaries -> chunks (long gaps in equal parts)
+  const int ng = ncut + 1;
+  const int gper = cdiv(ng, NT);
+  const int g0 = min(ng, tid * gper), g1 = min(ng, g0 + gper);
+  int parts = 0;
+  for (int gi = g0; gi < g1; ++gi) {
+    const int gap = s_pos[gi + 1] - s_pos[gi];
+    parts += gap > kCdcMaxGap ? cdiv(gap, kCdcSplitGap) : 1;
+  }
+  int S;
+  int c = wg_exclusive_scan<NT>(parts, s_w, S);
+  for (int gi = g0; gi < g1; ++gi) {
+    const int b0 = s_pos[gi], gap = s_pos[gi + 1] - b0;
+    const int n = gap > kCdcMaxGap ? cdiv(gap, kCdcSplitGap) : 1;
+    for (int p = 0; p < n; ++p, ++c)
+      if (c < a.s_max) start[c] = b0 + (int)((long long)p * gap / n);
+  }
+  if (tid == 0) {
+    cdc_count[r] = min(S, a.s_max);
+    start[min(S, a.s_max)] = nb;
+  }
+}
+
+// One workgroup: the work list of the shared-span decode.  A chunk whose first
+// physical block starts another chunk of the batch too (the same span at the
+// same place in several requests) is grouped with those chunks by a hash of
+// that block; the other chunks follow, ordered by their first key index, as
+// the uniform decode orders its chunks (requests' keys at similar positions
+// share cos/sin table rows).  Position i of the list (kv-head group
+// innermost) is dispatched where the XCD-contiguous mapping puts logical item
+// i, so a group's chunks run side by side on one XCD and the later ones read
+// the span from that XCD's L2.  With more than kCdcSortMax chunks the list
+// stays in request order.  coff: int[num_reqs + 1] scratch.
+__global__ void __launch_bounds__(1024) cdc_order_kernel(AttnArgs a, const int* cdc_count,
+                                                         const int* cdc_start, int* coff,
+                                                         int4* items, int* nitems) {
+  constexpr int NT = 1024;
+  constexpr int NH = kCdcSortMax + kCdcPosBuckets;
+  __shared__ int s_w[128];
+  __shared__ int s_req[kCdcSortMax];  // chunk -> request
+  __shared__ int s_key[kCdcSortMax];  // chunk -> hash bucket, then final bucket
+  __shared__ int s_hist[NH];
+  const int tid = threadIdx.x;
+  const int R = a.num_reqs;
+  int carry = 0;
+  for (int base = 0; base < R; base += NT) {
+    const int r = base + tid;
+    const int v = r < R ? min(max(cdc_count[r], 1), a.s_max) : 0;
+    int tot;
+    const int ex = wg_exclusive_scan<NT>(v, s_w, tot);
+    if (r < R) coff[r] = carry + ex;
+    carry += tot;
+  }
+  const int C = carry;
+  const long long total = (long long)C * a.nhg;
+  if (tid == 0) {
+    coff[R] = C;
+    *nitems = (int)total;
+  }
+  __syncthreads();
+  auto emit = [&](int r, int sc, int pos) {
+    for (int hg = 0; hg < a.nhg; ++hg) {
+      const unsigned l = (unsigned)((long long)pos * a.nhg + hg);
+      items[xcd_position(l, (unsigned)total)] = make_int4(kItemDecode, r, hg, sc);
+    }
+  };
+  // request of chunk x: the last r with coff[r] <= x
+  auto locate = [&](int x) {
+    int lo = 0, hi = R - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (coff[mid] <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  if (C > kCdcSortMax) {  // request order
+    for (int x = tid; x < C; x += NT) {
+      const int r = locate(x);
+      emit(r, x - coff[r], x);
+    }
+    return;
+  }
+  int nbk = 1;
+  while (nbk < C) nbk <<= 1;
+  for (int i = tid; i < NH; i += NT) s_hist[i] = 0;
+  __syncthreads();
+  auto first_block = [&](int r, int sc) { return cdc_start[(size_t)r * (a.s_max + 1) + sc]; };
+  for (int x = tid; x < C; x += NT) {
+    const int r = locate(x);
+    const int blk = a.block_table[(size_t)r * a.bt_stride + first_block(r, x - coff[r])];
+    const int hb = (int)(cdc_mix((unsigned)blk * 0x9e3779b9u) & (unsigned)(nbk - 1));
+    s_req[x] = r;
+    s_key[x] = hb;
+    atomicAdd(&s_hist[hb], 1);
+  }
+  __syncthreads();
+  // final bucket: the hash bucket when it holds two chunks or more, else a
+  // class of the chunk's first block after all hash buckets
+  for (int x = tid; x < C; x += NT) {
+    const int r = s_req[x];
+    const int hb = s_key[x];
+    s_key[x] = s_hist[hb] >= 2
+                   ? hb
+                   : kCdcSortMax + min(first_block(r, x - coff[r]) >> 3, kCdcPosBuckets - 1);
+  }
+  __syncthreads();
+  for (int i = tid; i < NH; i += NT) s_hist[i] = 0;
+  __syncthreads();
+  for (int x = tid; x < C; x += NT) atomicAdd(&s_hist[s_key[x]], 1);
+  __syncthreads();
+  // exclusive scan of the histogram: thread t owns buckets [t*per, (t+1)*per)
+  constexpr int per = NH / NT;
+  int sum = 0;
+  for (int i = tid * per; i < (tid + 1) * per; ++i) sum += s_hist[i];
+  int tot;
+  int run = wg_exclusive_scan<NT>(sum, s_w, tot);
+  for (int i = tid * per; i < (tid + 1) * per; ++i) {
+    const int v = s_hist[i];
+    s_hist[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  for (int x = tid; x < C; x += NT) {
+    const int r = s_req[x];
+    emit(r, x - coff[r], atomicAdd(&s_hist[s_key[x]], 1));
+  }
+}
+
+// The shared-span decode's main kernel: one work-list item per workgroup.
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads, 2) decode_shared_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(DecodeSmem<T, D>)];
+  if ((int)blockIdx.x >= *a.nitems) return;
+  const int4 it = a.items[blockIdx.x];
+  decode_item<T, D, kDecodeDepth, kWaves, true>(a, it.y, it.z, it.w, it.y, smem);
+}
+
 // Waves per workgroup of the mixed launch.  bf16: eight, so a prefill tile
 // holds 256 query rows and each staged (rotated) K step feeds twice the MFMA
 // work of a four-wave tile; a decode item then covers eight kv heads.  fp32
@@ -1748,6 +2035,53 @@ static int attn_decode(const AttnHostArgs& h, hipStream_t s) {
   return PIC_EUNSUPPORTED;
 }
 
+// Shared-span decode: chunking, ordering, decode, merge.
+template <typename T, int D>
+static int launch_decode_shared(const AttnArgs& a, const SharedDecodeLayout& w,
+                                const AttnHostArgs& h, hipStream_t s) {
+  unsigned char* ws = (unsigned char*)h.workspace;
+  int* cnt = (int*)(ws + w.cnt_off);
+  int* start = (int*)(ws + w.start_off);
+  hipLaunchKernelGGL(cdc_chunk_kernel, dim3((unsigned)h.num_reqs), dim3(1024), 0, s, a, cnt,
+                     start);
+  hipLaunchKernelGGL(cdc_order_kernel, dim3(1), dim3(1024), 0, s, a, cnt, start,
+                     (int*)(ws + w.coff_off), (int4*)(ws + w.items_off),
+                     (int*)(ws + w.count_off));
+  bool ok = record_before(s);
+  hipLaunchKernelGGL((decode_shared_kernel<T, D>), dim3((unsigned)w.max_items), dim3(kThreads), 0,
+                     s, a);
+  ok = record_after(s) && ok;
+  launch_combine<T, D>(a, s);
+  return hipGetLastError() == hipSuccess && ok ? PIC_OK : PIC_EHIP;
+}
+
+static int attn_decode_shared(const AttnHostArgs& h, hipStream_t s) {
+  if (h.num_reqs < 0 || h.max_seq_len < 0 || h.hq <= 0 || h.hkv <= 0)
+    return check_attn_args(h, true, 0);
+  const SharedDecodeLayout w = shared_decode_layout(h.num_reqs, h.max_seq_len, h.hq, h.hkv,
+                                                    h.head_dim);
+  int st = check_attn_args(h, true, w.total);
+  if (st || h.num_reqs == 0) return st;
+  if (!w.supported) return PIC_EUNSUPPORTED;
+  WorkspaceLayout dl{};
+  dl.count_off = w.count_off;
+  dl.items_off = w.items_off;
+  dl.ml_off = w.ml_off;
+  dl.o_off = w.o_off;
+  dl.s_max = w.s_max;
+  dl.nhg = w.nhg;
+  dl.max_items = w.max_items;
+  AttnArgs a = make_args(h, dl);
+  unsigned char* ws = (unsigned char*)h.workspace;
+  a.cdc_count = (const int*)(ws + w.cnt_off);
+  a.cdc_start = (const int*)(ws + w.start_off);
+  if (h.dtype == PIC_BF16)
+    return h.head_dim == 128 ? launch_decode_shared<bf16, 128>(a, w, h, s)
+                             : launch_decode_shared<bf16, 64>(a, w, h, s);
+  return h.head_dim == 128 ? launch_decode_shared<float, 128>(a, w, h, s)
+                           : launch_decode_shared<float, 64>(a, w, h, s);
+}
+
 template <bool ROT>
 static int attn_prefill(const AttnHostArgs& h, hipStream_t s) {
   int st = check_attn_common(h, ROT);
@@ -1792,6 +2126,22 @@ extern "C" int pic_attn_decode(const void* q, const int32_t* q_pos, const void* 
                        num_reqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, max_seq_len, dtype, out, workspace, workspace_bytes};
   return pic::attn_decode<true>(h, (hipStream_t)stream);
+}
+
+extern "C" int pic_attn_decode_shared(const void* q, const int32_t* q_pos, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_table,
+                                      int block_table_stride, const int32_t* seq_lens,
+                                      const int32_t* cu_seqlens_k, const int32_t* k_pos,
+                                      const float* cos_tab, const float* sin_tab, int max_pos,
+                                      int num_reqs, int num_q_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int num_blocks,
+                                      int max_seq_len, int dtype, void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const AttnHostArgs h{q, nullptr, q_pos, k_pool, v_pool, block_table, block_table_stride,
+                       seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab, max_pos, num_reqs,
+                       num_reqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, max_seq_len, dtype, out, workspace, workspace_bytes};
+  return pic::attn_decode_shared(h, (hipStream_t)stream);
 }
 
 extern "C" int pic_attn_prefill(const void* q, const int32_t* cu_seqlens_q, const int32_t* q_pos,

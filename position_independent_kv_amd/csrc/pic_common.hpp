@@ -120,4 +120,64 @@ inline WorkspaceLayout workspace_layout(int num_reqs, int total_q, int max_seq_l
   return w;
 }
 
+// Shared-span decode (pic_attn_decode_shared): a request's chunk boundaries
+// are decided by its blocks' physical ids, so two requests that hold the same
+// span at different offsets cut it at the same blocks and compute identical
+// chunks, which the planner then runs side by side on one XCD.
+constexpr int kCdcCandMask = 15;      // a block is a cut candidate with probability 1/16
+constexpr int kCdcMinGap = 12;        // blocks between two cuts, at least
+constexpr int kCdcMaxGap = 38;        // a longer gap between cuts is split ...
+constexpr int kCdcSplitGap = 24;      // ... into cdiv(gap, 24) equal parts
+constexpr int kCdcMaxBlocks = 65536;  // blocks of one request the planner handles
+constexpr int kCdcSortMax = 8192;     // chunks the ordering kernel groups (more: request order)
+constexpr int kCdcPosBuckets = 8192;  // start-block classes of chunks that occur once
+
+// Byte layout of the shared-span decode's workspace.
+struct SharedDecodeLayout {
+  size_t count_off;     // int: work items written by the planner
+  size_t items_off;     // int4[max_items]: work list
+  size_t ml_off;        // float2[num_reqs * hkv * s_max * group]: (max, sum) per chunk
+  size_t o_off;         // float[... * head_dim]: chunk outputs
+  size_t cnt_off;       // int[num_reqs]: chunks per request
+  size_t start_off;     // int[num_reqs][s_max + 1]: chunk start blocks, then the block count
+  size_t coff_off;      // int[num_reqs + 1]: first chunk of each request in the list
+  size_t total;
+  int s_max;            // chunks per request, upper bound
+  int nhg;              // kv-head groups of kWaves heads
+  long long max_items;  // work-list capacity
+  bool supported;       // within the planner's limits
+};
+
+// Chunks are at least kCdcMinGap blocks long except the first and the last,
+// so a request of nb blocks has at most nb / kCdcMinGap + 3 of them.
+inline SharedDecodeLayout shared_decode_layout(int num_reqs, int max_seq_len, int hq, int hkv,
+                                               int head_dim) {
+  SharedDecodeLayout w{};
+  const int group = hq / hkv;
+  const int nb_max = cdiv(max_seq_len > 0 ? max_seq_len : 0, kBlockSize);
+  w.s_max = cdiv(nb_max, kCdcMinGap) + 3;
+  w.nhg = cdiv(hkv, kWaves);
+  w.max_items = (long long)num_reqs * w.s_max * w.nhg;
+  w.supported = nb_max <= kCdcMaxBlocks && w.max_items <= 0x7fffffffLL &&
+                (long long)num_reqs * hkv <= 0x7fffffffLL;
+  const size_t parts = (size_t)num_reqs * hkv * w.s_max * group;
+  size_t off = 0;
+  w.count_off = off;
+  off = align_up(off + 16, 256);
+  w.items_off = off;
+  off = align_up(off + (size_t)w.max_items * 16, 256);
+  w.ml_off = off;
+  off = align_up(off + parts * 8, 256);
+  w.o_off = off;
+  off = align_up(off + parts * head_dim * 4, 256);
+  w.cnt_off = off;
+  off = align_up(off + (size_t)num_reqs * 4, 256);
+  w.start_off = off;
+  off = align_up(off + (size_t)num_reqs * (w.s_max + 1) * 4, 256);
+  w.coff_off = off;
+  off = align_up(off + ((size_t)num_reqs + 1) * 4, 256);
+  w.total = off;
+  return w;
+}
+
 }  // namespace pic

@@ -48,6 +48,14 @@ int check_heads(int hq, int hkv) {
 }
 
 int check_attn_common(const AttnHostArgs& a, bool key_positions) {
+  if (a.num_reqs < 0 || a.total_q < 0 || a.max_seq_len < 0 || a.hq <= 0 || a.hkv <= 0)
+    return check_attn_args(a, key_positions, 0);
+  const WorkspaceLayout w = workspace_layout(a.num_reqs, a.total_q, a.max_seq_len, a.hq, a.hkv,
+                                             a.head_dim);
+  return check_attn_args(a, key_positions, w.total);
+}
+
+int check_attn_args(const AttnHostArgs& a, bool key_positions, size_t need) {
   if (a.num_reqs < 0 || a.total_q < 0 || a.max_seq_len < 0 || a.num_blocks < 0 ||
       a.block_table_stride < 0 || a.max_pos <= 0)
     return PIC_EINVAL;
@@ -63,9 +71,7 @@ int check_attn_common(const AttnHostArgs& a, bool key_positions) {
   if (a.num_blocks == 0 || a.block_table_stride == 0) return PIC_EINVAL;
   if ((long long)a.block_table_stride * a.block_size < a.max_seq_len) return PIC_EINVAL;
   if (!a.workspace) return PIC_EWORKSPACE;
-  const WorkspaceLayout w = workspace_layout(a.num_reqs, a.total_q, a.max_seq_len, a.hq, a.hkv,
-                                             a.head_dim);
-  if (a.workspace_bytes < w.total) return PIC_EWORKSPACE;
+  if (a.workspace_bytes < need) return PIC_EWORKSPACE;
   return PIC_OK;
 }
 
@@ -79,6 +85,17 @@ extern "C" size_t pic_attn_workspace_size(int num_reqs, int total_q, int max_seq
   if (pic::check_heads(num_q_heads, num_kv_heads)) return 0;
   return pic::workspace_layout(num_reqs, total_q, max_seq_len, num_q_heads, num_kv_heads,
                                head_dim).total;
+}
+
+extern "C" size_t pic_attn_decode_shared_workspace_size(int num_reqs, int max_seq_len,
+                                                        int num_q_heads, int num_kv_heads,
+                                                        int head_dim, int dtype) {
+  if (num_reqs < 0 || max_seq_len < 0) return 0;
+  if (pic::check_dtype_dims(dtype, head_dim, pic::kBlockSize)) return 0;
+  if (pic::check_heads(num_q_heads, num_kv_heads)) return 0;
+  const pic::SharedDecodeLayout w =
+      pic::shared_decode_layout(num_reqs, max_seq_len, num_q_heads, num_kv_heads, head_dim);
+  return w.supported ? w.total : 0;
 }
 
 static int fail(char* msg, int msg_len, const char* fmt, long long a, long long b) {

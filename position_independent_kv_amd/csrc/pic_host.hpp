@@ -40,5 +40,7 @@ int check_heads(int hq, int hkv);
 // Host-visible argument checks of an attention call; key_positions: the call
 // reads cu_seqlens_k and k_pos (the position-free kernels do).
 int check_attn_common(const AttnHostArgs& a, bool key_positions);
+// The same checks against a workspace requirement of `need` bytes.
+int check_attn_args(const AttnHostArgs& a, bool key_positions, size_t need);
 
 }  // namespace pic

@@ -92,6 +92,20 @@ class DeviceWorkload:
                                  self.sin, w.max_q_len, w.max_seq_len, out, self.workspace)
         return out
 
+    def attention_shared(self, out=None):
+        """The batch through pic_attn_decode_shared (block-determined chunks, identical
+        chunks side by side on one XCD); its workspace is allocated on first use."""
+        w = self.w
+        out = self.out if out is None else out
+        if getattr(self, "shared_ws", None) is None:
+            n = pic.pic_attn_decode_shared_workspace_size(w.num_reqs, w.max_seq_len, w.hq, w.hkv,
+                                                          w.d, self.dtype)
+            self.shared_ws = _torch().zeros(max(n, 16), dtype=_torch().uint8, device=out.device)
+        pic.pic_attn_decode_shared(self.q, self.q_pos, self.k_pool, self.v_pool,
+                                   self.block_table, self.seq_lens, self.cu_k, self.k_pos,
+                                   self.cos, self.sin, w.max_seq_len, out, self.shared_ws)
+        return out
+
     def build_rotated_cache(self):
         """The conventional RoPE cache of this batch, for the in-kernel-rotation ablation.
 

@@ -28,7 +28,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = pic.library()
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(pic.EXPORTS)
@@ -124,6 +124,39 @@ def test_entry_points_reject_bad_arguments_before_launch():
     pargs[24] = buf
     pargs[25] = 1 << 40
     assert lib.pic_attn_prefill(*pargs) == pic.PIC_EINVAL
+
+
+def test_shared_decode_sizes_and_rejections_before_launch():
+    lib = pic.library()
+    f = pic.pic_attn_decode_shared_workspace_size
+    base = f(64, 4097, 32, 8, 128, pic.PIC_BF16)
+    assert base > 0
+    assert f(64, 4097, 32, 8, 96, pic.PIC_BF16) == 0          # head_dim unsupported
+    assert f(64, 4097, 30, 8, 128, pic.PIC_BF16) == 0         # Hq % Hkv
+    assert f(4, (1 << 20) + 16, 32, 8, 128, pic.PIC_BF16) == 0  # more than 65536 blocks
+    assert f(4, 1 << 20, 32, 8, 128, pic.PIC_BF16) > 0        # exactly 65536 blocks
+    assert f(65, 4097, 32, 8, 128, pic.PIC_BF16) >= base      # monotone
+    assert f(64, 8193, 32, 8, 128, pic.PIC_BF16) >= base
+    buf = ctypes.c_void_p(1)  # never dereferenced: rejected before launch
+    args = [buf] * 5 + [300] + [buf] * 5 + [4097, 4, 32, 8, 128, 16, 100, 4097, 1] + [buf, None, 0,
+                                                                                   None]
+    assert lib.pic_attn_decode_shared(*args) == pic.PIC_EWORKSPACE
+    need = f(4, 4097, 32, 8, 128, pic.PIC_BF16)  # the call's own shape: 4 requests
+    assert 0 < need < base
+    small = list(args)
+    small[21], small[22] = buf, need - 1
+    assert lib.pic_attn_decode_shared(*small) == pic.PIC_EWORKSPACE
+    nulls = list(args)
+    nulls[8] = None  # k_pos: the position-free kernels read it
+    nulls[21], nulls[22] = buf, 1 << 40
+    assert lib.pic_attn_decode_shared(*nulls) == pic.PIC_EINVAL
+    big = list(args)
+    big[5], big[19] = 70000, 70000 * 16  # 70000 blocks per context
+    big[21], big[22] = buf, 1 << 50
+    assert lib.pic_attn_decode_shared(*big) == pic.PIC_EUNSUPPORTED
+    empty = list(args)
+    empty[12] = 0
+    assert lib.pic_attn_decode_shared(*empty) == pic.PIC_OK
 
 
 def test_blocks_copy_rejects_bad_arguments_before_launch():
