@@ -344,3 +344,37 @@ def test_negative_control_prerotated_keys_fail():
     got = run_workload(w2)
     ref = oracle_outputs(w)
     assert _maxerr(got, ref) > 1e-2
+
+
+# ---------------------------------------------------------------------------
+# one block referenced twice by the same request
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case,first,second,n", [
+    ("decode_long", 0, 70, 70),      # the second 1120-token segment re-references the first
+    ("prefill_long_q", 0, 10, 10),   # the second 160-token span re-references the first
+])
+def test_block_repeated_within_a_request(case, first, second, n):
+    """Position-free storage lets a request hold the same physical blocks twice (one
+    document twice in a prompt): each occurrence is rotated by its own positions.  The
+    blocks of request 0's second segment are replaced by those of its first, and the
+    outputs must still match the oracle over the same block table."""
+    w = make_workload(case, **dict(SMALL[case]))
+    bt = w.block_table.copy()
+    assert int(w.seq_lens[0]) >= (second + n) * w.block_size
+    bt[0, second:second + n] = bt[0, first:first + n]
+    w.block_table = bt
+    dw = DeviceWorkload(w)
+    dw.write_new_tokens()
+    got = to_f64_out(dw.attention())
+    ref = oracle_outputs(w)
+    err = _maxerr(got, ref)
+    print(f"{case}: max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+    if w.kind == "decode":
+        shared = to_f64_out(dw.attention_shared())
+        assert _maxerr(shared, ref) <= TOL[w.dtype]
+
+
+def to_f64_out(t):
+    return t.float().cpu().numpy().astype(np.float64)
