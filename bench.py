@@ -428,9 +428,22 @@ def cpu_baseline(w, counts, budget_s=12.0):
     frac = counts["bytes"] * n / w.num_reqs  # every byte count is per request
     cpu = os.popen("lscpu 2>/dev/null | grep 'Model name' | head -1").read()
     cpu = " ".join(cpu.split(":", 1)[-1].split())
-    return {"value": frac * reps / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {w.num_reqs} requests of the {w.name} attention call, {reps} runs "
-                      f"({dt:.1f} s, numpy fp64, {threads} BLAS threads; {cpu})"}
+    res = {"value": frac * reps / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} of {w.num_reqs} requests of the {w.name} attention call, {reps} runs "
+                     f"({dt:.1f} s, numpy fp64, {threads} BLAS threads; {cpu})"}
+    # the same oracle on one core, on a smaller sample (about budget_s / 2 of CPU time)
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            t1 = run([0])
+            n1 = int(max(1, min(w.num_reqs, budget_s / 2 / max(t1, 1e-6))))
+            d1 = run(list(range(n1)))
+        res["single_core"] = {"value": counts["bytes"] * n1 / w.num_reqs / d1 / 1e9,
+                              "unit": "GB/s", "cores": 1,
+                              "sample": f"{n1} of {w.num_reqs} requests, one run ({d1:.1f} s)"}
+    except ImportError:  # pragma: no cover
+        pass
+    return res
 
 
 def load_traffic(kernel: str, config: str):
