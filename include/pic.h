@@ -157,8 +157,9 @@ int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool, con
  * are read once per XCD instead of once per request (MiniPIC §2.1: one
  * physical block serves concurrent requests at different offsets).  A block
  * whose physical id hashes to a fixed residue (probability 1/16) starts a new
- * chunk unless another such block lies among the 7 blocks before it; gaps
- * longer than 36 blocks are cut into equal parts.  Two requests holding the
+ * chunk unless another such block lies among the 11 blocks before it; a gap
+ * of more than 38 blocks between two cuts is cut into equal parts of at most
+ * 24 blocks.  Two requests holding the
  * same span at different offsets therefore cut it at the same blocks, and a
  * planner groups chunks by their first physical block so that identical
  * chunks run side by side on one XCD and the later ones find the span in
@@ -193,8 +194,14 @@ size_t pic_attn_decode_shared_workspace_size(int num_reqs, int max_seq_len, int 
  * cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1 of q; query row i of the request
  * (0-based) sits at position q_pos[cu_seqlens_q[r] + i] and sees key slots
  * j <= seq_lens[r] - q_len + i.  max_q_len must be >= every q_len (a
- * precondition, like the others).  Other arguments as in pic_attn_decode.
- * A small planner kernel builds the work list in the workspace first.
+ * precondition, like the others; no kernel reads it).  Other arguments as in
+ * pic_attn_decode.  A small planner kernel builds the work list in the
+ * workspace first.  If the device metadata break a precondition so that the
+ * work list would not fit the workspace (for instance cu_seqlens_q not
+ * ascending, so that requests' rows overlap), the planner runs nothing and
+ * every output row of the launch (as cu_seqlens_q delimits them, clipped to
+ * [0, total_q)) is filled with NaN; the call still returns PIC_OK, since the
+ * host never reads device data.
  * bf16 launches with fewer prefill tiles (256 query rows of one kv head)
  * than 256 split each tile over a context of 2048 keys or more into key
  * chunks that run in parallel; a merge kernel on the same stream combines

@@ -281,6 +281,52 @@ def pic_attn_decode_shared_workspace_size(num_reqs, max_seq_len, num_q_heads, nu
         num_reqs, max_seq_len, num_q_heads, num_kv_heads, head_dim, code))
 
 
+def _check_meta(fn, R, total_q, d, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos, cos_tab,
+                sin_tab, cu_seqlens_q=None):
+    """Shapes of the metadata and the table (no device reads): every length the kernels
+    index by must be there, and the table must be built for this head size."""
+    if cos_tab.shape != sin_tab.shape or cos_tab.dim() != 2 or 2 * cos_tab.shape[1] != d:
+        raise ValueError(f"{fn}: cos_tab and sin_tab must both be [max_pos][{d // 2}]")
+    if q_pos.dim() != 1 or q_pos.shape[0] != total_q:
+        raise ValueError(f"{fn}: q_pos must be [{total_q}]")
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != R:
+        raise ValueError(f"{fn}: seq_lens must be [{R}]")
+    if block_table.dim() != 2 or block_table.shape[0] < R:
+        raise ValueError(f"{fn}: block_table must be [R][stride]")
+    if cu_seqlens_k is not None and (cu_seqlens_k.dim() != 1 or cu_seqlens_k.shape[0] != R + 1):
+        raise ValueError(f"{fn}: cu_seqlens_k must be [{R + 1}]")
+    if k_pos is not None and k_pos.dim() != 1:
+        raise ValueError(f"{fn}: k_pos must be one-dimensional")
+    if cu_seqlens_q is not None and (cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape[0] != R + 1):
+        raise ValueError(f"{fn}: cu_seqlens_q must be [{R + 1}]")
+
+
+def validation_enabled() -> bool:
+    """PIC_VALIDATE=1: every attention call first checks its metadata on host copies."""
+    return os.environ.get("PIC_VALIDATE", "") == "1"
+
+
+def _validate(fn, cu_seqlens_q, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos, max_q_len,
+              max_seq_len, max_pos, num_blocks):
+    """The device-value preconditions of an attention call, checked on host copies (this
+    synchronises with the device).  Raises ValueError naming the first violation."""
+    host = [None if t is None else t.detach().cpu().numpy()
+            for t in (cu_seqlens_q, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos)]
+    cu_q, qp, bt, sl, cu_k, kp = host
+    R = sl.shape[0]
+    if cu_k is not None and R and kp.shape[0] < int(cu_k[R]):
+        raise ValueError(f"{fn}: k_pos holds {kp.shape[0]} entries, cu_seqlens_k[R] = {cu_k[R]}")
+    if cu_k is None:  # a rotated-cache call: positions are not read, any in-range value will do
+        cu_k = np.concatenate([[0], np.cumsum(sl.astype(np.int64))]).astype(np.int32)
+        kp = np.zeros(int(cu_k[-1]), np.int32)
+    st, msg = pic_validate_metadata(cu_q, qp, bt[:R], sl, cu_k, kp, max_seq_len, max_pos,
+                                    num_blocks)
+    if st != PIC_OK:
+        raise ValueError(f"{fn}: {msg}")
+    if cu_q is not None and R and int(np.diff(cu_q.astype(np.int64)).max()) > max_q_len:
+        raise ValueError(f"{fn}: a request has more than max_q_len = {max_q_len} query rows")
+
+
 def _decode_call(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens_k, k_pos,
                  cos_tab, sin_tab, max_seq_len, out, workspace, stream):
     torch = _torch()
@@ -289,8 +335,10 @@ def _decode_call(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens
     nb, hkv, bs, pd = _pool_dims(k_pool, v_pool)
     if pd != d or tuple(out.shape) != (R, hq, d) or out.dtype != q.dtype:
         raise ValueError("q / out / pool head sizes disagree")
-    if block_table.dim() != 2 or block_table.shape[0] < R:
-        raise ValueError("block_table must be [R][stride]")
+    _check_meta(fn, R, R, d, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab)
+    if validation_enabled():
+        _validate(fn, None, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos, 1, max_seq_len,
+                  cos_tab.shape[0], nb)
     _check(getattr(_load(), fn)(
         _ptr(q, "q"), _ptr(q_pos, "q_pos", i32), _ptr(k_pool, "k_pool", q.dtype),
         _ptr(v_pool, "v_pool", q.dtype), _ptr(block_table, "block_table", i32),
@@ -313,8 +361,11 @@ def pic_attn_prefill(q, cu_seqlens_q, q_pos, k_pool, v_pool, block_table, seq_le
     nb, hkv, bs, pd = _pool_dims(k_pool, v_pool)
     if pd != d or tuple(out.shape) != (total_q, hq, d) or out.dtype != q.dtype:
         raise ValueError("q / out / pool head sizes disagree")
-    if cu_seqlens_q.shape != (R + 1,) or block_table.dim() != 2:
-        raise ValueError("cu_seqlens_q must be [R+1] and block_table [R][stride]")
+    _check_meta("pic_attn_prefill", R, total_q, d, q_pos, block_table, seq_lens, cu_seqlens_k,
+                k_pos, cos_tab, sin_tab, cu_seqlens_q)
+    if validation_enabled():
+        _validate("pic_attn_prefill", cu_seqlens_q, q_pos, block_table, seq_lens, cu_seqlens_k,
+                  k_pos, int(max_q_len), max_seq_len, cos_tab.shape[0], nb)
     _check(_load().pic_attn_prefill(
         _ptr(q, "q"), _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(q_pos, "q_pos", i32),
         _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype),
@@ -336,8 +387,11 @@ def pic_attn_decode_rotated(q, q_pos, k_pool, v_pool, block_table, seq_lens, cos
     nb, hkv, bs, pd = _pool_dims(k_pool, v_pool)
     if pd != d or tuple(out.shape) != (R, hq, d) or out.dtype != q.dtype:
         raise ValueError("q / out / pool head sizes disagree")
-    if block_table.dim() != 2 or block_table.shape[0] < R:
-        raise ValueError("block_table must be [R][stride]")
+    _check_meta("pic_attn_decode_rotated", R, R, d, q_pos, block_table, seq_lens, None, None,
+                cos_tab, sin_tab)
+    if validation_enabled():
+        _validate("pic_attn_decode_rotated", None, q_pos, block_table, seq_lens, None, None, 1,
+                  max_seq_len, cos_tab.shape[0], nb)
     _check(_load().pic_attn_decode_rotated(
         _ptr(q, "q"), _ptr(q_pos, "q_pos", i32), _ptr(k_pool, "k_pool", q.dtype),
         _ptr(v_pool, "v_pool", q.dtype), _ptr(block_table, "block_table", i32),
@@ -359,8 +413,11 @@ def pic_attn_prefill_rotated(q, cu_seqlens_q, q_pos, k_pool, v_pool, block_table
     nb, hkv, bs, pd = _pool_dims(k_pool, v_pool)
     if pd != d or tuple(out.shape) != (total_q, hq, d) or out.dtype != q.dtype:
         raise ValueError("q / out / pool head sizes disagree")
-    if cu_seqlens_q.shape != (R + 1,) or block_table.dim() != 2:
-        raise ValueError("cu_seqlens_q must be [R+1] and block_table [R][stride]")
+    _check_meta("pic_attn_prefill_rotated", R, total_q, d, q_pos, block_table, seq_lens, None,
+                None, cos_tab, sin_tab, cu_seqlens_q)
+    if validation_enabled():
+        _validate("pic_attn_prefill_rotated", cu_seqlens_q, q_pos, block_table, seq_lens, None,
+                  None, int(max_q_len), max_seq_len, cos_tab.shape[0], nb)
     _check(_load().pic_attn_prefill_rotated(
         _ptr(q, "q"), _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(q_pos, "q_pos", i32),
         _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype),

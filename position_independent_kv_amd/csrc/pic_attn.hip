@@ -70,6 +70,7 @@ struct AttnArgs {
   const float* sin_tab;
   int max_pos;
   int num_reqs;
+  int total_q;
   int hq;
   int hkv;
   int group;
@@ -577,8 +578,25 @@ __device__ void merge_prefill_tile(const AttnArgs& a, int idx) {
   for (int e = 0; e < D / 4; ++e) store4<T>(dst + 4 * e, o[e], inv);
 }
 
+// NaN into the output rows of request r for the q heads of kv head g (rows
+// clipped to [0, total_q)): what a mixed launch leaves when its planner
+// refused a work list larger than the workspace.
+template <typename T, int D>
+__device__ void fill_nan_rows(const AttnArgs& a, int r, int g) {
+  const int q0 = max(a.cu_q[r], 0), q1 = min(a.cu_q[r + 1], a.total_q);
+  const int G = a.group;
+  const long long n = (long long)max(q1 - q0, 0) * G * D;
+  T* out = (T*)a.out;
+  for (long long i = threadIdx.x; i < n; i += kThreads) {
+    const long long row = q0 + i / (G * D);
+    const int h = g * G + (int)((i / D) % G);
+    out[(row * a.hq + h) * D + i % D] = (T)__builtin_nanf("");
+  }
+}
+
 // Blocks [0, dec_blocks): one per (request, kv head), merging the chunks of
-// q_len == 1 requests; blocks beyond: one per split prefill tile.
+// q_len == 1 requests (or, after a refused work list, filling the request's
+// rows with NaN); blocks beyond: one per split prefill tile.
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a, int dec_blocks) {
   constexpr int EPT = 8;
@@ -591,6 +609,10 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a, int dec_b
   }
   const int r = blockIdx.x / a.hkv;
   const int g = blockIdx.x % a.hkv;
+  if (a.cu_q && a.nitems[1]) {  // the planner ran nothing (work list overflow)
+    fill_nan_rows<T, D>(a, r, g);
+    return;
+  }
   if (a.cu_q && a.cu_q[r + 1] - a.cu_q[r] != 1) return;
   const long long qrow = a.cu_q ? (long long)a.cu_q[r] : (long long)r;
   const int L = seq_len_of(a, r);
@@ -1839,15 +1861,21 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   s_pbase[tid] = tot[3] - x[3];
   const bool chunk_major = s_bover == 0;
   // More items than the workspace was sized for means the metadata broke a
-  // precondition (total_q or max_seq_len too small): run nothing.
+  // precondition (cu_seqlens_q not ascending, or total_q / max_seq_len too
+  // small): run nothing, and raise the flag that makes the merge launch fill
+  // every output row of the launch with NaN, so the failure is visible.
   if (total > max_items) {
     if (tid == 0) {
-      *count = 0;
+      count[0] = 0;
+      count[1] = 1;
       if (pf_count) *pf_count = 0;
     }
     return;
   }
-  if (tid == 0) *count = (int)total;
+  if (tid == 0) {
+    count[0] = (int)total;
+    count[1] = 0;
+  }
   // pass 2, per chunk of 1024 requests: decode offsets (request order, when
   // not chunk-major) by a scan, prefill and chunk-major ranks by LDS
   // atomics; then the waves take the chunk's requests in turn and their
@@ -1943,6 +1971,7 @@ static AttnArgs make_args(const AttnHostArgs& h, const WorkspaceLayout& w) {
   a.sin_tab = h.sin_tab;
   a.max_pos = h.max_pos;
   a.num_reqs = h.num_reqs;
+  a.total_q = h.total_q;
   a.hq = h.hq;
   a.hkv = h.hkv;
   a.group = h.hq / h.hkv;
@@ -1966,9 +1995,13 @@ static AttnArgs make_args(const AttnHostArgs& h, const WorkspaceLayout& w) {
   return a;
 }
 
+// all_reqs: one block per (request, kv head) even when no request can have
+// several chunks (the mixed launch: those blocks also report a refused work
+// list).
 template <typename T, int D>
-static void launch_combine(const AttnArgs& a, hipStream_t s, int split_blocks = 0) {
-  const int dec_blocks = a.s_max > 1 ? a.num_reqs * a.hkv : 0;
+static void launch_combine(const AttnArgs& a, hipStream_t s, bool all_reqs,
+                           int split_blocks = 0) {
+  const int dec_blocks = all_reqs || a.s_max > 1 ? a.num_reqs * a.hkv : 0;
   if (dec_blocks + split_blocks > 0)
     hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)(dec_blocks + split_blocks)),
                        dim3(kThreads), 0, s, a, dec_blocks);
@@ -1981,14 +2014,15 @@ static int launch_decode(const AttnArgs& a, hipStream_t s) {
   bool ok = record_before(s);
   hipLaunchKernelGGL((decode_kernel<T, D, ROT>), dim3((unsigned)n), dim3(kThreads), 0, s, a);
   ok = record_after(s) && ok;
-  launch_combine<T, D>(a, s);
+  launch_combine<T, D>(a, s, false);
   return hipGetLastError() == hipSuccess && ok ? PIC_OK : PIC_EHIP;
 }
 
 template <typename T, int D, bool ROT>
 static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnHostArgs& h,
                         hipStream_t s) {
-  if (w.max_items > 0x7fffffffLL) return PIC_EUNSUPPORTED;
+  if (w.max_items > 0x7fffffffLL || (long long)h.num_reqs * h.hkv + kSplitCUs > 0x7fffffffLL)
+    return PIC_EUNSUPPORTED;
   unsigned char* ws = (unsigned char*)h.workspace;
   const int len_cap = (int)min((long long)h.max_seq_len,
                               (long long)h.block_table_stride * kBlockSize);
@@ -2002,17 +2036,9 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
   hipLaunchKernelGGL((mixed_kernel<T, D, ROT>), dim3((unsigned)w.max_items),
                      dim3(64 * mixed_waves<T>()), 0, s, a);
   ok = record_after(s) && ok;
-  // Every request has q_len >= total_q - (num_reqs - 1) * max_q_len; when that
-  // bound is at least 2 the batch has no decode rows and nothing to merge.
-  const long long min_q_len =
-      (long long)h.total_q - (long long)(h.num_reqs - 1) * h.max_q_len;
-  if (min_q_len < 2) {
-    launch_combine<T, D>(a, s, split ? kSplitCUs / 2 : 0);
-  } else if (split) {
-    AttnArgs b = a;
-    b.s_max = 1;  // no decode merges
-    launch_combine<T, D>(b, s, kSplitCUs / 2);
-  }
+  // Always launched: whether a request has q_len == 1 is device data, and its
+  // blocks exit at once where there is nothing to merge.
+  launch_combine<T, D>(a, s, true, split ? kSplitCUs / 2 : 0);
   return hipGetLastError() == hipSuccess && ok ? PIC_OK : PIC_EHIP;
 }
 
@@ -2051,7 +2077,7 @@ static int launch_decode_shared(const AttnArgs& a, const SharedDecodeLayout& w,
   hipLaunchKernelGGL((decode_shared_kernel<T, D>), dim3((unsigned)w.max_items), dim3(kThreads), 0,
                      s, a);
   ok = record_after(s) && ok;
-  launch_combine<T, D>(a, s);
+  launch_combine<T, D>(a, s, false);
   return hipGetLastError() == hipSuccess && ok ? PIC_OK : PIC_EHIP;
 }
 

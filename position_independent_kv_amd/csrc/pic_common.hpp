@@ -65,7 +65,8 @@ constexpr bool prefill_split_possible(long long total_q, long long num_reqs, int
 
 // Byte layout of the attention workspace.
 struct WorkspaceLayout {
-  size_t count_off;     // int: number of work items written by the planner
+  size_t count_off;     // int[2]: work items written by the planner; 1 if it refused an
+                        // overflowing work list (the mixed launch then writes NaN)
   size_t items_off;     // int4[max_items]: work list
   size_t ml_off;        // float2[num_reqs * hkv * s_max * group]: (max, sum) per chunk
   size_t o_off;         // float[num_reqs * hkv * s_max * group * head_dim]: chunk outputs

@@ -68,7 +68,8 @@ class DeviceWorkload:
         if write_context and w.ctx_k.shape[0]:
             pic.pic_cache_write(to_torch(w.ctx_k, w.dtype, dev), to_torch(w.ctx_v, w.dtype, dev),
                                 i32(w.ctx_slots, dev), self.k_pool, self.v_pool)
-        self.out = torch.empty_like(self.q)
+        # outputs start as NaN too: a row that no kernel writes fails every comparison
+        self.out = torch.full_like(self.q, float("nan"))
         ws = pic.pic_attn_workspace_size(w.num_reqs, w.total_q, w.max_seq_len, w.hq, w.hkv, w.d,
                                          tdt)
         self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=dev)

@@ -377,3 +377,92 @@ def test_header_is_c99_and_the_library_links_from_c(tmp_path):
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
     assert run.stdout.startswith("ok ")
+
+
+# ---------------------------------------------------------------------------
+# the Python binding's own checks (no device memory involved: CPU tensors fail
+# the checks before any pointer is taken)
+# ---------------------------------------------------------------------------
+
+def _cpu_decode_args(w):
+    import torch
+
+    def t(a):
+        return torch.from_numpy(np.array(a, dtype=np.int32))  # a copy: tests mutate it
+
+    q = torch.zeros((w.num_reqs, w.hq, w.d), dtype=torch.bfloat16)
+    kp = torch.zeros((w.num_blocks, w.hkv, w.block_size, w.d), dtype=torch.bfloat16)
+    vp = torch.zeros((w.num_blocks, w.hkv, w.d, w.block_size), dtype=torch.bfloat16)
+    cos = torch.zeros((w.max_pos, w.d // 2))
+    return dict(q=q, q_pos=t(w.q_pos), k_pool=kp, v_pool=vp, block_table=t(w.block_table),
+                seq_lens=t(w.seq_lens), cu_seqlens_k=t(w.cu_seqlens_k), k_pos=t(w.k_pos),
+                cos_tab=cos, sin_tab=cos.clone(), max_seq_len=w.max_seq_len,
+                out=torch.zeros_like(q), workspace=torch.zeros(16, dtype=torch.uint8))
+
+
+def test_binding_rejects_short_metadata_and_wrong_table_width():
+    """Every array the kernels index must have the length the call implies, and the table
+    must be built for this head size: a table of d/2 = 32 columns read as d = 128 would put
+    every row lookup past its end on the device."""
+    import torch
+    w = make_workload("x", values=False, builder="decode", seed=3, R=4, seg_len=32, n_seg=2,
+                      n_shared=0, n_spans=0)
+    good = _cpu_decode_args(w)
+    bad = {
+        "cos_tab": torch.zeros((w.max_pos, 32)),
+        "q_pos": good["q_pos"][:-1],
+        "seq_lens": good["seq_lens"][:-1],
+        "cu_seqlens_k": good["cu_seqlens_k"][:-1],
+        "block_table": good["block_table"][:-1],
+        "k_pos": good["k_pos"].view(2, -1),
+    }
+    for name, val in bad.items():
+        kw = dict(good)
+        kw[name] = val
+        if name == "cos_tab":
+            kw["sin_tab"] = val.clone()
+        with pytest.raises(ValueError) as e:
+            pic.pic_attn_decode(**kw)
+        assert "must be on the GPU" not in str(e.value), name
+    # with good shapes the first complaint is that the tensors are not on the GPU
+    with pytest.raises(ValueError, match="GPU"):
+        pic.pic_attn_decode(**good)
+
+
+def test_binding_validate_mode_checks_device_values(monkeypatch):
+    """PIC_VALIDATE=1: the binding copies the metadata to the host and runs
+    pic_validate_metadata (plus the k_pos length and max_q_len) before launching."""
+    w = make_workload("x", values=False, builder="decode", seed=3, R=4, seg_len=32, n_seg=2,
+                      n_shared=0, n_spans=0)
+    monkeypatch.setenv("PIC_VALIDATE", "1")
+    good = _cpu_decode_args(w)
+    with pytest.raises(ValueError, match="GPU"):  # valid metadata: on to the pointer checks
+        pic.pic_attn_decode(**good)
+    cases = {
+        "block id": ("block_table", lambda a: a.fill_(w.num_blocks)),
+        "key position": ("k_pos", lambda a: a.__setitem__(5, w.max_pos)),
+        "query position": ("q_pos", lambda a: a.__setitem__(0, -1)),
+        "seq_len": ("seq_lens", lambda a: a.__setitem__(1, w.max_seq_len + 1)),
+        "k_pos holds": ("k_pos", None),
+    }
+    for what, (name, mutate) in cases.items():
+        kw = _cpu_decode_args(w)
+        if mutate is None:
+            kw[name] = kw[name][:-3].clone()
+        else:
+            mutate(kw[name])
+        with pytest.raises(ValueError, match=what):
+            pic.pic_attn_decode(**kw)
+    # prefill: a request longer than max_q_len
+    import torch
+    pw = make_workload("y", values=False, builder="prefill", seed=4, R=2, n_spans=3, span_len=32,
+                       per_req=2, q_len=20)
+    a = _cpu_decode_args(pw)
+    q = torch.zeros((pw.total_q, pw.hq, pw.d), dtype=torch.bfloat16)
+    cu_q = torch.from_numpy(pw.cu_seqlens_q.copy())
+    args = (q, cu_q, a["q_pos"], a["k_pool"], a["v_pool"], a["block_table"], a["seq_lens"],
+            a["cu_seqlens_k"], a["k_pos"], a["cos_tab"], a["sin_tab"])
+    with pytest.raises(ValueError, match="max_q_len"):
+        pic.pic_attn_prefill(*args, 19, pw.max_seq_len, torch.zeros_like(q), a["workspace"])
+    with pytest.raises(ValueError, match="GPU"):
+        pic.pic_attn_prefill(*args, 20, pw.max_seq_len, torch.zeros_like(q), a["workspace"])

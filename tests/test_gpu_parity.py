@@ -287,43 +287,91 @@ def _oracle_on_rounded_operands(w):
 
 
 # ---------------------------------------------------------------------------
-# full-size configs, sampled outputs
+# full-size configs: every request, every work item
 # ---------------------------------------------------------------------------
+#
+# One GPU run per config (outputs start as NaN, so a row no work item writes
+# is caught by the finiteness check), then the oracle over parts of it:
+# every request of the decode configs, and for prefill requests one token per
+# 64-token tile (256 rows = 64 tokens x 4 group heads: the unit one prefill
+# work item computes) with all 32 q heads, so every (request, kv head, tile)
+# item of the launch is compared.  The token inside each tile is drawn from a
+# seeded generator (first and last tokens of the request always included).
 
-def _sampled(name, requests, rows=None):
-    w = make_workload(name)
-    got = run_workload(w)
-    ref = oracle_outputs(w, requests=requests, rows=rows)
+_FULL = {}
+
+
+def _full(name):
+    """(workload, GPU output, oracle pools) of a config, one config cached at a time."""
+    if name not in _FULL:
+        _FULL.clear()
+        w = make_workload(name)
+        got = run_workload(w)
+        _FULL[name] = (w, got, oracle_pools(w))
+    return _FULL[name]
+
+
+def _tile_rows(q_len, seed, tile_tokens=64):
+    """One token per tile_tokens-token tile of a request's query rows, plus its first and
+    last rows."""
+    rng = np.random.default_rng(seed)
+    rows = {0, q_len - 1}
+    for t0 in range(0, q_len, tile_tokens):
+        rows.add(int(rng.integers(t0, min(t0 + tile_tokens, q_len))))
+    return sorted(rows)
+
+
+def _compare(name, requests, rows=None):
+    w, got, pools = _full(name)
+    assert np.isfinite(got).all(), f"{name}: {int((~np.isfinite(got)).any(axis=(1, 2)).sum())} " \
+                                   "output rows never written"
+    ref = oracle_outputs(w, requests=requests, rows=rows, pools=pools)
     err = _maxerr(select_rows(got, w, requests, rows), ref)
-    print(f"{name}: max abs err {err:.3e} on {len(ref)} rows")
-    assert np.isfinite(got).all()
+    print(f"{name}: max abs err {err:.3e} on {len(ref)} rows x {w.hq} heads")
     assert err <= TOL[w.dtype]
 
 
-def test_full_c2_decode_sampled():
-    _sampled("c2", [0, 17, 63])
+def test_full_c2_decode_every_request():
+    _compare("c2", list(range(64)))
 
 
-def test_full_c2p_decode_sampled():
-    _sampled("c2p", [5, 40])
+def test_full_c2p_decode_every_request():
+    _compare("c2p", list(range(64)))
 
 
-def test_full_c3_prefill_sampled():
-    rows = {0: [0, 1, 255, 511], 5: [17, 300, 511]}
-    _sampled("c3", [0, 5], rows)
-
-
-def test_full_c4_long_decode_sampled():
-    _sampled("c4", [2])
-
-
-def test_full_c5_mixed_sampled():
-    w = make_workload("c5", values=False)
+def test_full_c3_prefill_every_tile():
+    w = _full("c3")[0]
+    reqs = list(range(w.num_reqs))
     ql = w.q_lens()
-    pre = [int(r) for r in np.nonzero(ql > 1)[0][:2]]
-    dec = [int(r) for r in np.nonzero(ql == 1)[0][:3]]
-    rows = {pre[0]: [0, 1, 1000, 2047], pre[1]: [5, 2046]}
-    _sampled("c5", pre + dec, rows)
+    _compare("c3", reqs, {r: _tile_rows(int(ql[r]), 300 + r) for r in reqs})
+
+
+@pytest.mark.parametrize("r", [0, 1, 2, 3])
+def test_full_c4_long_decode_every_request(r):
+    _compare("c4", [r])
+
+
+@pytest.mark.parametrize("part", [0, 1, 2, 3])
+def test_full_c5_mixed_every_decode(part):
+    w = _full("c5")[0]
+    dec = [int(r) for r in np.nonzero(w.q_lens() == 1)[0]]
+    assert len(dec) == 128
+    _compare("c5", dec[part::4])
+
+
+@pytest.mark.parametrize("part", [0, 1])
+def test_full_c5_mixed_every_prefill_tile(part):
+    w = _full("c5")[0]
+    ql = w.q_lens()
+    pre = [int(r) for r in np.nonzero(ql > 1)[0]]
+    assert len(pre) == 16
+    pre = pre[part::2]
+    _compare("c5", pre, {r: _tile_rows(int(ql[r]), 500 + r) for r in pre})
+
+
+def test_full_configs_release():
+    """Drops the cached full-size run (host memory) before the tests that follow."""
+    _FULL.clear()
 
 
 # ---------------------------------------------------------------------------

@@ -349,7 +349,7 @@ def test_kernel_events_bracket_the_main_kernel(kw):
     assert ev[2].elapsed_time(ev[3]) == before
 
 
-@pytest.mark.parametrize("kind", ["decode", "prefill"])
+@pytest.mark.parametrize("kind", ["decode", "prefill", "mixed"])
 def test_needle_at_maximum_sizes(kind):
     """Indexing at sizes far past the benchmark configs: 3 requests of 2^20 + 37 keys each
     (65,539 blocks per request, 196,617 in the pool, ~3.2 GB of K/V), positions drawn from
@@ -357,7 +357,9 @@ def test_needle_at_maximum_sizes(kind):
     in the middle and at the last slot; the query shares the needle's position, so its
     score dominates and every row that sees it must return that slot's V row bit for bit.
     Prefill runs 40 query rows per request: 6 tiles, so each tile's keys are split into
-    chunks merged by the combine launch."""
+    chunks merged by the combine launch.  Mixed runs requests 0 and 2 as one-row decodes
+    (2,731 key chunks each: more than the planner's 1024 chunk-count groups, so its decode
+    items are listed in request order) beside request 1's 40 rows in one prefill launch."""
     torch = _torch()
     rng = np.random.default_rng(11)
     hkv, G, d, B = 2, 4, 128, 16
@@ -386,27 +388,85 @@ def test_needle_at_maximum_sizes(kind):
     pic.pic_rope_table(cos, sin, 500000.0)
     seq = np.full(R, L, np.int32)
     cu_k = (np.arange(R + 1, dtype=np.int64) * L).astype(np.int32)
-    ql = 1 if kind == "decode" else 40
-    q = q1[None].expand(R * ql, hq, d).contiguous().to(torch.bfloat16).cuda()
-    q_pos = i32(np.full(R * ql, t_pos, np.int32))
-    out = torch.empty_like(q)
-    ws = torch.zeros(pic.pic_attn_workspace_size(R, R * ql, L, hq, hkv, d, torch.bfloat16),
+    qls = {"decode": [1] * R, "prefill": [40] * R, "mixed": [1, 40, 1]}[kind]
+    cu_q_h = np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+    total_q = int(cu_q_h[-1])
+    q = q1[None].expand(total_q, hq, d).contiguous().to(torch.bfloat16).cuda()
+    q_pos = i32(np.full(total_q, t_pos, np.int32))
+    out = torch.full_like(q, float("nan"))
+    ws = torch.zeros(pic.pic_attn_workspace_size(R, total_q, L, hq, hkv, d, torch.bfloat16),
                      dtype=torch.uint8, device="cuda")
     args = (k_pool, v_pool, i32(block_table), i32(seq), i32(cu_k), i32(k_pos.reshape(-1)),
             cos, sin)
     if kind == "decode":
         pic.pic_attn_decode(q, q_pos, *args, L, out, ws)
     else:
-        cu_q = i32((np.arange(R + 1) * ql).astype(np.int32))
-        pic.pic_attn_prefill(q, cu_q, q_pos, *args, ql, L, out, ws)
+        pic.pic_attn_prefill(q, i32(cu_q_h), q_pos, *args, max(qls), L, out, ws)
     torch.cuda.synchronize()
+    if kind == "mixed":
+        assert pic.pic_decode_num_splits(L) >= 1024
     checked = 0
     for r, j in enumerate(needles):
         want = v_pool[int(block_table[r, j // B]), :, :, j % B]
+        ql = qls[r]
         for i in range(ql):
             if j <= L - ql + i:  # the row sees the needle
-                got = out[r * ql + i].view(hkv, G, d)
+                got = out[int(cu_q_h[r]) + i].view(hkv, G, d)
                 for h in range(hq):
                     assert _same_bits(got[h // G, h % G], want[h // G]), (kind, r, j, i, h)
                 checked += 1
     assert checked >= R
+
+
+def test_mixed_launch_over_1024_requests():
+    """A prefill launch of 1,104 requests (4 causal span prefills + 1,100 two-chunk decodes
+    over those spans, in shuffled order): the planner handles requests in passes of 1024,
+    so the later requests' items come from its second pass.  Every output row is compared
+    with the oracle (outputs start as NaN, so a dropped item fails)."""
+    from tests.gpu_harness import run_workload
+    from tests.oracle_harness import oracle_outputs
+    w = make_workload("x", builder="mixed", seed=61, n_chunks=4, chunk=208, n_dec=1100,
+                      per_dec=4)
+    assert w.num_reqs > 1024 and pic.pic_decode_num_splits(int(w.seq_lens.max())) == 2
+    got = run_workload(w)
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - oracle_outputs(w)).max())
+    print(f"1104 requests: max abs err {err:.3e}")
+    assert err <= 2e-2
+
+
+def test_refused_work_list_fills_nan():
+    """Metadata that break a precondition (cu_seqlens_q descending between requests, so
+    the rows of requests 0, 2, 4, ... overlap) make the work list larger than the
+    workspace was sized for.  The planner then runs nothing and the launch fills every
+    output row with NaN instead of leaving stale values; the call itself returns PIC_OK
+    (the violation is device data).  With PIC_VALIDATE=1 the binding refuses the call."""
+    import os
+    torch = _torch()
+    w, dw = _fresh(dict(builder="prefill", seed=62, R=9, n_spans=4, span_len=512, per_req=2,
+                        q_len=512))
+    T = 512
+    cu_q = np.array([0] + [T if r % 2 == 0 else 0 for r in range(9)], np.int32)
+    q = dw.q[:T].contiguous()
+    out = torch.zeros_like(q)
+    ws = torch.zeros(pic.pic_attn_workspace_size(9, T, w.max_seq_len, w.hq, w.hkv, w.d,
+                                                 torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    args = (q, i32(cu_q), dw.q_pos[:T].contiguous(), dw.k_pool, dw.v_pool, dw.block_table,
+            dw.seq_lens, dw.cu_k, dw.k_pos, dw.cos, dw.sin, T, w.max_seq_len, out, ws)
+    pic.pic_attn_prefill(*args)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()
+    os.environ["PIC_VALIDATE"] = "1"
+    try:
+        with pytest.raises(ValueError, match="q_len"):
+            pic.pic_attn_prefill(*args)
+    finally:
+        del os.environ["PIC_VALIDATE"]
+    # the same workspace then serves a valid call: request 0's 512 rows alone, which equal
+    # its rows of the whole batch bit for bit
+    cu_ok = np.array([0] + [T] * 9, np.int32)
+    pic.pic_attn_prefill(q, i32(cu_ok), *args[2:])
+    full = dw.attention()
+    torch.cuda.synchronize()
+    assert _same_bits(out, full[:T])
