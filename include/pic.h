@@ -152,6 +152,34 @@ int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool, con
                     size_t workspace_bytes, void* stream);
 
 /*
+ * pic_attn_decode_noalloc -- pic_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and the same results,
+ * bit for bit, with no workspace argument.  The chunk partials go to a
+ * fixed array of 64 MiB that the library holds on each device it runs on
+ * until the process ends (its address is looked up once per device, on the
+ * first call with that device current).  The call itself allocates nothing.
+ * The array needs no initialisation (every call writes what it reads) and
+ * keeps the last call's contents; calls that overlap in time on one device
+ * race on it, so the caller serialises them (one stream, or events).
+ * Arguments, layouts and preconditions as in pic_attn_decode.
+ * Errors as pic_attn_decode, plus PIC_EWORKSPACE when the batch needs more
+ * than the 64 MiB, i.e. when pic_attn_workspace_size(num_reqs, num_reqs,
+ * max_seq_len, ...) without its prefill-split part exceeds 67,108,864 bytes
+ * (for the 32 / 8 heads, d = 128 layer: about 1.5 million keys over the whole
+ * batch; 64 x 4,097 keys use 12.8 MB, 4 x 131,073 keys 22.9 MB), and
+ * PIC_EHIP when the array's device address cannot be obtained.
+ */
+int pic_attn_decode_noalloc(const void* q, const int32_t* q_pos, const void* k_pool,
+                            const void* v_pool, const int32_t* block_table,
+                            int block_table_stride, const int32_t* seq_lens,
+                            const int32_t* cu_seqlens_k, const int32_t* k_pos,
+                            const float* cos_tab, const float* sin_tab, int max_pos,
+                            int num_reqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int block_size, int num_blocks, int max_seq_len, int dtype,
+                            void* out, void* stream);
+
+/*
  * pic_attn_decode_shared -- pic_attn_decode with the key chunks of each
  * request cut where its blocks say, so that blocks shared by several requests
  * are read once per XCD instead of once per request (MiniPIC §2.1: one

@@ -34,7 +34,7 @@ EXPORTS = [
     "pic_attn_decode_rotated", "pic_attn_prefill_rotated", "pic_block_hashes",
     "pic_build_block_tables", "pic_blocks_copy", "pic_sched_create", "pic_sched_destroy",
     "pic_sched_add_span", "pic_sched_add_request", "pic_sched_step", "pic_set_kernel_events",
-    "pic_attn_decode_shared", "pic_attn_decode_shared_workspace_size",
+    "pic_attn_decode_shared", "pic_attn_decode_shared_workspace_size", "pic_attn_decode_noalloc",
 ]
 PIC_SCHED_ISPS, PIC_SCHED_BARRIER = 0, 1
 PIC_SEQ_SPAN, PIC_SEQ_PROMPT, PIC_SEQ_DECODE = 0, 1, 2
@@ -112,6 +112,8 @@ def _load():
     lib.pic_sched_step.argtypes = [c_void, ctypes.POINTER(_SchedBatch)]
     lib.pic_set_kernel_events.argtypes = [c_void, c_void]
     lib.pic_attn_decode_shared.argtypes = lib.pic_attn_decode.argtypes
+    lib.pic_attn_decode_noalloc.argtypes = ([c_void] * 5 + [c_int] + [c_void] * 5 + [c_int] * 9
+                                            + [c_void, c_void])
     lib.pic_attn_decode_shared_workspace_size.restype = c_size
     lib.pic_attn_decode_shared_workspace_size.argtypes = [c_int] * 6
     lib.pic_decode_num_splits.argtypes = [c_int, c_int]
@@ -272,6 +274,32 @@ def pic_attn_decode_shared(q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_s
     the workspace is sized by pic_attn_decode_shared_workspace_size."""
     _decode_call("pic_attn_decode_shared", q, q_pos, k_pool, v_pool, block_table, seq_lens,
                  cu_seqlens_k, k_pos, cos_tab, sin_tab, max_seq_len, out, workspace, stream)
+
+
+def pic_attn_decode_noalloc(q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens_k,
+                            k_pos, cos_tab, sin_tab, max_seq_len, out, stream=None):
+    """pic_attn_decode without a workspace argument: the chunk partials live in the
+    library's fixed per-device scratch array (64 MiB), so the call allocates nothing.
+    Calls that overlap in time on one GPU race on that array."""
+    torch = _torch()
+    i32 = torch.int32
+    fn = "pic_attn_decode_noalloc"
+    R, hq, d = q.shape
+    nb, hkv, bs, pd = _pool_dims(k_pool, v_pool)
+    if pd != d or tuple(out.shape) != (R, hq, d) or out.dtype != q.dtype:
+        raise ValueError("q / out / pool head sizes disagree")
+    _check_meta(fn, R, R, d, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab)
+    if validation_enabled():
+        _validate(fn, None, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos, 1, max_seq_len,
+                  cos_tab.shape[0], nb)
+    _check(_load().pic_attn_decode_noalloc(
+        _ptr(q, "q"), _ptr(q_pos, "q_pos", i32), _ptr(k_pool, "k_pool", q.dtype),
+        _ptr(v_pool, "v_pool", q.dtype), _ptr(block_table, "block_table", i32),
+        block_table.shape[1], _ptr(seq_lens, "seq_lens", i32),
+        _ptr(cu_seqlens_k, "cu_seqlens_k", i32), _ptr(k_pos, "k_pos", i32),
+        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
+        cos_tab.shape[0], R, hq, hkv, d, bs, nb, int(max_seq_len), _dtype_code(q),
+        _ptr(out, "out"), _stream(stream)), fn)
 
 
 def pic_attn_decode_shared_workspace_size(num_reqs, max_seq_len, num_q_heads, num_kv_heads,

@@ -46,6 +46,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "pic.h"
@@ -2045,11 +2046,11 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
 // One decode call: position-free (ROT) or over an already rotated cache.
 template <bool ROT>
 static int attn_decode(const AttnHostArgs& h, hipStream_t s) {
-  int st = check_attn_common(h, ROT);
+  int st = check_attn_common(h, ROT, true);
   if (st || h.num_reqs == 0) return st;
   if (!ROT && h.dtype != PIC_BF16) return PIC_EUNSUPPORTED;
   const WorkspaceLayout w = workspace_layout(h.num_reqs, h.num_reqs, h.max_seq_len, h.hq,
-                                             h.hkv, h.head_dim);
+                                             h.hkv, h.head_dim, true);
   const AttnArgs a = make_args(h, w);
   if (h.dtype == PIC_BF16)
     return h.head_dim == 128 ? launch_decode<bf16, 128, ROT>(a, s)
@@ -2108,9 +2109,30 @@ static int attn_decode_shared(const AttnHostArgs& h, hipStream_t s) {
                            : launch_decode_shared<float, 64>(a, w, h, s);
 }
 
+// Scratch of pic_attn_decode_noalloc: the decode workspace (chunk partials)
+// in a fixed device array instead of caller memory, for callers that cannot
+// allocate.  Each device holds its own copy for the life of the process; its
+// address is looked up once per device with that device current (the array's
+// name is a host-side stand-in, never a device address).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+static void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 template <bool ROT>
 static int attn_prefill(const AttnHostArgs& h, hipStream_t s) {
-  int st = check_attn_common(h, ROT);
+  int st = check_attn_common(h, ROT, false);
   if (st || h.num_reqs == 0 || h.total_q == 0) return st;
   if (!h.cu_seqlens_q || h.max_q_len < 0) return PIC_EINVAL;
   if (!ROT && h.dtype != PIC_BF16) return PIC_EUNSUPPORTED;
@@ -2151,6 +2173,23 @@ extern "C" int pic_attn_decode(const void* q, const int32_t* q_pos, const void* 
                        seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab, max_pos, num_reqs,
                        num_reqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, max_seq_len, dtype, out, workspace, workspace_bytes};
+  return pic::attn_decode<true>(h, (hipStream_t)stream);
+}
+
+extern "C" int pic_attn_decode_noalloc(const void* q, const int32_t* q_pos, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_table,
+                                       int block_table_stride, const int32_t* seq_lens,
+                                       const int32_t* cu_seqlens_k, const int32_t* k_pos,
+                                       const float* cos_tab, const float* sin_tab, int max_pos,
+                                       int num_reqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int num_blocks,
+                                       int max_seq_len, int dtype, void* out, void* stream) {
+  void* ws = pic::scratch_address();
+  if (!ws) return PIC_EHIP;
+  const AttnHostArgs h{q, nullptr, q_pos, k_pool, v_pool, block_table, block_table_stride,
+                       seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab, max_pos, num_reqs,
+                       num_reqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, max_seq_len, dtype, out, ws, pic::kNoAllocScratchBytes};
   return pic::attn_decode<true>(h, (hipStream_t)stream);
 }
 

@@ -83,8 +83,10 @@ struct WorkspaceLayout {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// decode: the layout of a pic_attn_decode call, which never splits prefill
+// tiles (the same offsets, without the split regions at the end).
 inline WorkspaceLayout workspace_layout(int num_reqs, int total_q, int max_seq_len, int hq,
-                                        int hkv, int head_dim) {
+                                        int hkv, int head_dim, bool decode = false) {
   WorkspaceLayout w{};
   const int group = hq / hkv;
   w.s_max = max_splits(max_seq_len);
@@ -105,7 +107,7 @@ inline WorkspaceLayout workspace_layout(int num_reqs, int total_q, int max_seq_l
   off = align_up(off + parts * 8, 256);
   w.o_off = off;
   off = align_up(off + parts * head_dim * 4, 256);
-  w.pf_split = prefill_split_possible(total_q, num_reqs, hq, hkv, max_seq_len);
+  w.pf_split = !decode && prefill_split_possible(total_q, num_reqs, hq, hkv, max_seq_len);
   w.pf_count_off = w.pf_tiles_off = w.pf_ml_off = w.pf_o_off = off;
   if (w.pf_split) {
     w.pf_count_off = off;

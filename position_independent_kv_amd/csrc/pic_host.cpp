@@ -47,11 +47,11 @@ int check_heads(int hq, int hkv) {
   return PIC_OK;
 }
 
-int check_attn_common(const AttnHostArgs& a, bool key_positions) {
+int check_attn_common(const AttnHostArgs& a, bool key_positions, bool decode) {
   if (a.num_reqs < 0 || a.total_q < 0 || a.max_seq_len < 0 || a.hq <= 0 || a.hkv <= 0)
     return check_attn_args(a, key_positions, 0);
   const WorkspaceLayout w = workspace_layout(a.num_reqs, a.total_q, a.max_seq_len, a.hq, a.hkv,
-                                             a.head_dim);
+                                             a.head_dim, decode);
   return check_attn_args(a, key_positions, w.total);
 }
 

@@ -38,8 +38,9 @@ struct AttnHostArgs {
 int check_dtype_dims(int dtype, int head_dim, int block_size);
 int check_heads(int hq, int hkv);
 // Host-visible argument checks of an attention call; key_positions: the call
-// reads cu_seqlens_k and k_pos (the position-free kernels do).
-int check_attn_common(const AttnHostArgs& a, bool key_positions);
+// reads cu_seqlens_k and k_pos (the position-free kernels do); decode: a
+// pic_attn_decode call, whose workspace has no prefill-split regions.
+int check_attn_common(const AttnHostArgs& a, bool key_positions, bool decode);
 // The same checks against a workspace requirement of `need` bytes.
 int check_attn_args(const AttnHostArgs& a, bool key_positions, size_t need);
 
