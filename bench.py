@@ -65,7 +65,39 @@ def step_counts(w, counts):
     return counts["bytes"] + cw
 
 
-def time_config(name, steps, warmup, with_rows=False):
+def pool_layers(w, cap=32):
+    """Copies of a config's KV pools that the timed steps cycle through, as consecutive
+    layers of one model would: at least 4, and enough for 1 GiB of pools (4x the 256 MB
+    Infinity Cache), so every call finds the caches holding other layers' data."""
+    es = 2 if w.dtype == "bf16" else 4
+    pool = 2 * w.num_blocks * w.hkv * w.block_size * w.d * es
+    return int(min(cap, max(4, -(-(1 << 30) // pool))))
+
+
+def _events(n):
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:   # the library records into existing HIP events
+        a.record()
+        b.record()
+    return ev
+
+
+def _ms(ev):
+    return np.asarray([a.elapsed_time(b) for a, b in ev], np.float64)
+
+
+def time_config(name, steps, warmup, with_rows=False, only_timed=False):
+    """Time one config.  Timed region (the benchmark's K steps, after W warm-up steps):
+    step k writes the new tokens into layer k's pools and runs the attention call on them,
+    cycling over pool_layers(w) copies, so every call is cold (the Infinity Cache holds
+    other layers' data).  Each step records HIP events around the whole attention call
+    and has the library record a pair right around its main kernel (same stream), so the
+    kernel and call figures come from the same steps.  Unless only_timed, with >= 10
+    warm-ups and >= 20 samples each: the same cold calls without the kernel events (what
+    recording them costs), and the main kernel and the call warm (one layer back to
+    back)."""
     import torch
 
     import position_independent_kv_amd as pic
@@ -75,66 +107,55 @@ def time_config(name, steps, warmup, with_rows=False):
     t = time.time()
     w = make_workload(name)
     counts = algorithmic_counts(w)
-    dw = DeviceWorkload(w)
+    nl = pool_layers(w)
+    dw = DeviceWorkload(w).add_layers(nl)
     torch.cuda.synchronize()
     log(f"[bench] {name}: built in {time.time() - t:.1f}s; "
-        f"{counts['bytes'] / 1e9:.3f} GB, {counts['flops'] / 1e12:.3f} TFLOP per attention call")
+        f"{counts['bytes'] / 1e9:.3f} GB, {counts['flops'] / 1e12:.3f} TFLOP per attention call; "
+        f"{nl} layer copies of the pools")
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        dw.step()
+
+    def loop(n, layer_of, hooked, first=0):
+        """n steps; returns (kernel ms, call ms) per step (kernel None when not hooked)."""
+        kev, cev = _events(n), _events(n)
+        for k in range(n):
+            dw.use_layer(layer_of(first + k))
+            dw.write_new_tokens()
+            if hooked:
+                pic.pic_set_kernel_events(*kev[k])
+            cev[k][0].record(stream)
+            dw.attention()
+            cev[k][1].record(stream)
+        pic.pic_set_kernel_events(None, None)
+        torch.cuda.synchronize()
+        return (_ms(kev) if hooked else None), _ms(cev)
+
+    def warm_up(n, layer_of):
+        for k in range(n):
+            dw.use_layer(layer_of(k))
+            dw.step()
+
+    warm_up(warmup, lambda k: k)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     t0 = time.perf_counter()
-    for k in range(steps):
-        dw.write_new_tokens()
-        ev[k][0].record(stream)
-        dw.attention()
-        ev[k][1].record(stream)
-    torch.cuda.synchronize()
+    kern, call = loop(steps, lambda k: k, True, first=warmup)
     t1 = time.perf_counter()
-    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    step_ms = (t1 - t0) * 1e3 / steps
-    # the call's main kernel alone (decode_kernel / mixed_kernel): the library
-    # records a pair of events right around its launch, on the launch stream
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for a_, b_ in kev:
-        a_.record(stream)
-        b_.record(stream)
-    for k in range(steps):
-        dw.write_new_tokens()
-        pic.pic_set_kernel_events(*kev[k])
-        dw.attention()
-    pic.pic_set_kernel_events(None, None)
-    torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
-    # cold: before each timed call the 256 MB Infinity Cache is refilled by
-    # reading a 512 MiB buffer, so nothing of the previous call is cached and
-    # no dirty line has to be written back during the call
-    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
-    ncold = max(3, steps // 5)
-    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ncold)]
-    for e in cold:
-        for x in e[2:]:
-            x.record(stream)
-    sink = torch.zeros((), dtype=torch.float32, device="cuda")
-    for e in cold:
-        sink += flush.sum()
-        pic.pic_set_kernel_events(e[2], e[3])
-        e[0].record(stream)
-        dw.attention()
-        e[1].record(stream)
-    pic.pic_set_kernel_events(None, None)
-    torch.cuda.synchronize()
-    cold_call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in cold]))
-    cold_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in cold]))
-    del flush, sink
-    res = dict(name=name, w=w, counts=counts, step_ms=step_ms, kernel_ms=kern_ms,
-               call_ms=call_ms, cold_kernel_ms=cold_ms, cold_call_ms=cold_call_ms,
+    res = dict(name=name, w=w, counts=counts, layers=nl, step_ms=(t1 - t0) * 1e3 / steps,
+               kernel_ms=float(kern.mean()), kernel_median_ms=float(np.median(kern)),
+               call_ms=float(np.median(call)), call_mean_ms=float(call.mean()),
                step_bytes=step_counts(w, counts))
-    if with_rows:
+    if not only_timed:
+        n, nw = max(20, steps), max(10, warmup)
+        warm_up(nw, lambda k: k)
+        _, plain = loop(n, lambda k: k, False)
+        warm_up(nw, lambda k: 0)
+        wk, wc = loop(n, lambda k: 0, True)
+        res.update(call_unhooked_ms=float(np.median(plain)),
+                   warm_kernel_ms=float(np.median(wk)), warm_call_ms=float(np.median(wc)),
+                   samples=n, sample_warmup=nw)
+    if with_rows and not only_timed:
         # the other rows of the path, timed on their own (same stream, events)
+        stream = torch.cuda.current_stream()
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         cos = torch.empty_like(dw.cos)
         sin = torch.empty_like(dw.sin)
@@ -173,7 +194,7 @@ def rope_ablation(name, reps=20):
     dw.write_new_tokens()
     dw.build_rotated_cache()
     stream = torch.cuda.current_stream()
-    for _ in range(3):
+    for _ in range(10):
         dw.attention()
         dw.attention_rotated()
     torch.cuda.synchronize()
@@ -216,7 +237,7 @@ def shared_decode(name, reps=20):
     stream = torch.cuda.current_stream()
     calls = {"uniform_chunks": dw.attention, "shared_chunks": dw.attention_shared}
     for fn in calls.values():
-        for _ in range(3):
+        for _ in range(10):
             fn()
     torch.cuda.synchronize()
     ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
@@ -334,38 +355,58 @@ def scheduled_trace(budget=8192, max_running=32, num_blocks=8192, reps=3):
     return res
 
 
-def ceilings():
-    """What this machine delivers to plain library code: a 2 GiB device copy (bytes read +
-    written per second) and a large bf16 matrix product (torch.matmul, 8192^3)."""
+def ceilings(reps=20):
+    """What this machine delivers outside the path: a plain streaming read (pic_stream_read over
+    2 GiB, the best of a few grid sizes; medians of `reps`), a 2 GiB device copy (bytes read
+    + written per second) and a large bf16 matrix product (torch.matmul, 8192^3)."""
     import torch
-    x = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+
+    import position_independent_kv_amd as pic
+    nbytes = 2 << 30
+    x = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+    read = {}
+    for wgs in (1024, 2048, 4096, 8192, 16384):
+        sink = torch.zeros(wgs * 256, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            pic.pic_stream_read(x, wgs, sink)
+        ev = _events(reps)
+        for a, b in ev:
+            a.record()
+            pic.pic_stream_read(x, wgs, sink)
+            b.record()
+        torch.cuda.synchronize()
+        read[wgs] = nbytes / (float(np.median(_ms(ev))) * 1e-3) / 1e9
+    best = max(read, key=read.get)
     y = torch.empty_like(x)
     y.copy_(x)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
+    ev = _events(reps)
+    for a, b in ev:
+        a.record()
         y.copy_(x)
-    e1.record()
+        b.record()
     torch.cuda.synchronize()
-    copy_gbps = 2 * x.numel() * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    copy_gbps = 2 * nbytes / (float(np.median(_ms(ev))) * 1e-3) / 1e9
     del x, y
     n = 8192
-    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
-    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
-    c = a @ b
+    a_ = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b_ = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    c = a_ @ b_
+    ev = _events(10)
+    for a, b in ev:
+        a.record()
+        c = a_ @ b_
+        b.record()
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(10):
-        c = a @ b
-    e1.record()
-    torch.cuda.synchronize()
-    mm_tflops = 2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
-    del a, b, c
+    mm_tflops = 2 * n ** 3 / (float(np.median(_ms(ev))) * 1e-3) / 1e12
+    del a_, b_, c
     torch.cuda.empty_cache()
-    log(f"[bench] ceilings: device copy {copy_gbps:.0f} GB/s, bf16 matmul {mm_tflops:.0f} TFLOP/s")
-    return {"device_copy_GBps": copy_gbps, "bf16_matmul_TFLOPs": mm_tflops,
-            "note": "2 GiB torch copy (read + write bytes), torch.matmul bf16 8192^3"}
+    log(f"[bench] ceilings: streaming read {read[best]:.0f} GB/s ({best} workgroups), "
+        f"device copy {copy_gbps:.0f} GB/s, bf16 matmul {mm_tflops:.0f} TFLOP/s")
+    return {"stream_read_GBps": read[best], "stream_read_workgroups": best,
+            "stream_read_sweep_GBps": {str(k): v for k, v in read.items()},
+            "device_copy_GBps": copy_gbps, "bf16_matmul_TFLOPs": mm_tflops,
+            "note": "pic_stream_read over 2 GiB (16-byte loads, 8 per lane in flight, best grid); "
+                    "2 GiB torch copy (read + write bytes); torch.matmul bf16 8192^3; medians"}
 
 
 def block_table_build(reps=5):
@@ -400,15 +441,37 @@ def block_table_build(reps=5):
             "physical_blocks": res["num_new_blocks"], "logical_blocks": logical}
 
 
-def cpu_baseline(w, counts, budget_s=12.0):
-    """The fp64 oracle on the host: a bounded sample of the same step."""
-    import oracle
-    from tests.oracle_harness import oracle_pools
+def request_work(w):
+    """Per request: the algorithmic bytes attention must move for it (K and V of its
+    visible slots, its q and out rows, its metadata) and its flops (4 d per unmasked
+    (row, key, q head)).  The cos/sin table is shared by the batch and not split."""
+    es = 2 if w.dtype == "bf16" else 4
+    ql = w.q_lens().astype(np.float64)
+    L = w.seq_lens.astype(np.float64)
+    byts = (L * w.hkv * w.d * es * 2 + 2 * ql * w.hq * w.d * es
+            + 4 * (np.ceil(L / w.block_size) + L + ql + 2))
+    pairs = ql * (L - ql) + ql * (ql + 1) / 2
+    return byts, 4.0 * w.d * w.hq * pairs
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        return 1
+
+
+def oracle_rate(w, counts, budget_s, unit, threads=None):
+    """The fp64 oracle (as it is, untuned) on the host over the first n requests of the
+    config, n chosen so the sample takes about budget_s (at least one request), repeated
+    while the measured time stays under budget_s (at most 8 runs).  Returns the rate in
+    `unit` ("GB/s": the sample's share of the call's algorithmic bytes; "TFLOP/s": the
+    sample's flops) and the sample's description."""
+    import contextlib
+
+    import oracle
+    from tests.oracle_harness import oracle_pools
     kp, vp = oracle_pools(w)
 
     def run(reqs):
@@ -417,33 +480,36 @@ def cpu_baseline(w, counts, budget_s=12.0):
                          w.cu_seqlens_k, w.k_pos, w.base, w.block_size, requests=reqs)
         return time.perf_counter() - t
 
-    t1 = run([0])
-    n = int(max(1, min(w.num_reqs, budget_s / max(t1, 1e-6))))
-    reqs = list(range(n))
-    # repeat the sample until about budget_s of CPU time has been measured
-    dt, reps = 0.0, 0
-    while reps == 0 or (dt < budget_s and reps < 8):
-        dt += run(reqs)
-        reps += 1
-    frac = counts["bytes"] * n / w.num_reqs  # every byte count is per request
-    cpu = os.popen("lscpu 2>/dev/null | grep 'Model name' | head -1").read()
-    cpu = " ".join(cpu.split(":", 1)[-1].split())
-    res = {"value": frac * reps / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-           "sample": f"{n} of {w.num_reqs} requests of the {w.name} attention call, {reps} runs "
-                     f"({dt:.1f} s, numpy fp64, {threads} BLAS threads; {cpu})"}
-    # the same oracle on one core, on a smaller sample (about budget_s / 2 of CPU time)
-    try:
+    ctx = contextlib.nullcontext()
+    if threads is not None:
         from threadpoolctl import threadpool_limits
-        with threadpool_limits(1):
-            t1 = run([0])
-            n1 = int(max(1, min(w.num_reqs, budget_s / 2 / max(t1, 1e-6))))
-            d1 = run(list(range(n1)))
-        res["single_core"] = {"value": counts["bytes"] * n1 / w.num_reqs / d1 / 1e9,
-                              "unit": "GB/s", "cores": 1,
-                              "sample": f"{n1} of {w.num_reqs} requests, one run ({d1:.1f} s)"}
-    except ImportError:  # pragma: no cover
-        pass
-    return res
+        ctx = threadpool_limits(threads)
+    with ctx:
+        nthreads = _blas_threads()
+        t1 = run([0])
+        n = int(max(1, min(w.num_reqs, budget_s / max(t1, 1e-6))))
+        reqs = list(range(n))
+        dt, reps = (t1, 1) if n == 1 else (0.0, 0)
+        while reps == 0 or (dt < budget_s and reps < 8):
+            dt += run(reqs)
+            reps += 1
+    rb, rf = request_work(w)
+    if unit == "GB/s":
+        work = counts["bytes"] * rb[:n].sum() / rb.sum() / 1e9
+    else:
+        work = rf[:n].sum() / 1e12
+    return {"value": work * reps / dt, "unit": unit, "cores": nthreads, "kind": "oracle",
+            "sample": f"first {n} of {w.num_reqs} requests of the {w.name} attention call, "
+                      f"{reps} run(s), {dt:.1f} s, numpy fp64, {nthreads} BLAS threads"}
+
+
+def cpu_model():
+    cpu = os.popen("lscpu 2>/dev/null | grep 'Model name' | head -1").read()
+    return " ".join(cpu.split(":", 1)[-1].split())
+
+
+def config_unit(w):
+    return "GB/s" if w.kind == "decode" else "TFLOP/s"
 
 
 def load_traffic(kernel: str, config: str):
@@ -476,7 +542,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--others", default="c2p,c3,c4,c5",
                     help="comma list of further configs reported under 'configs' ('' for none)")
@@ -487,6 +553,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sched", action="store_true",
                     help="skip the scheduled-trace comparison (ISPS vs barrier)")
+    ap.add_argument("--only-main", action="store_true",
+                    help="only the headline config's timed region (profiling runs: the kernel "
+                         "averages rocprofv3 reports are then those of the timed steps)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a plain copy of this many bytes (PMC scaling run)")
     args = ap.parse_args()
@@ -504,60 +573,100 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5)
         return
+    if args.only_main:
+        args.others = args.ablation = args.shared = ""
+        args.no_cpu_baseline = args.no_sched = True
 
-    main_res = time_config(args.config, args.steps, args.warmup, with_rows=True)
+    main_res = time_config(args.config, args.steps, args.warmup, with_rows=True,
+                           only_timed=args.only_main)
     w, counts = main_res["w"], main_res["counts"]
     decode = w.kind == "decode"
     kernel = "decode_kernel" if decode else "mixed_kernel"
     if decode:
-        achieved = counts["bytes"] / (main_res["kernel_ms"] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS}
+        work, scale, peak, unit = counts["bytes"], 1e9, HBM_PEAK_GBS, "GB/s"
+        roof = {"bound": "hbm"}
         value = main_res["step_bytes"] / (main_res["step_ms"] * 1e-3) / 1e9
         metric = "decode HBM GB/s"
-        unit = "GB/s"
     else:
-        achieved = counts["flops"] / (main_res["kernel_ms"] * 1e-3) / 1e12
+        work, scale, unit = counts["flops"], 1e12, "TFLOP/s"
         peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak}
+        roof = {"bound": "mfma"}
         value = counts["flops"] / (main_res["step_ms"] * 1e-3) / 1e12
         metric = "prefill TFLOP/s"
-        unit = "TFLOP/s"
-    roof["traffic"] = load_traffic(kernel, args.config)
-    roof["kernel"] = kernel
-    roof["kernel_ms"] = main_res["kernel_ms"]
-    roof["cold_kernel_ms"] = main_res["cold_kernel_ms"]
-    roof["cold_frac"] = roof["frac"] * main_res["kernel_ms"] / main_res["cold_kernel_ms"]
-    # the whole attention call (planning / merge launches included)
-    roof["call_ms"] = main_res["call_ms"]
-    roof["call_frac"] = roof["frac"] * main_res["kernel_ms"] / main_res["call_ms"]
-    roof["cold_call_ms"] = main_res["cold_call_ms"]
-    roof["algorithmic_bytes"] = counts["bytes"]
-    roof["algorithmic_flops"] = counts["flops"]
+
+    def rate(ms):
+        return work / (ms * 1e-3) / scale
+
+    achieved = rate(main_res["kernel_ms"])
+    roof.update(achieved=achieved, peak=peak, unit=unit, frac=achieved / peak,
+                traffic=load_traffic(kernel, args.config), kernel=kernel,
+                timing="cold: the timed steps cycle over %d copies of the KV pools (layers), so "
+                       "no call finds its data in the caches; achieved = algorithmic work / mean "
+                       "main-kernel time over the timed steps" % main_res["layers"],
+                kernel_ms=main_res["kernel_ms"], kernel_median_ms=main_res["kernel_median_ms"],
+                algorithmic_bytes=counts["bytes"], algorithmic_flops=counts["flops"],
+                unique_kv_bytes=counts["unique_kv_bytes"])
+    roof.update(call_ms=main_res["call_ms"], call_mean_ms=main_res["call_mean_ms"],
+                call_frac=rate(main_res["call_ms"]) / peak)
+    if "warm_kernel_ms" in main_res:
+        roof.update(call_unhooked_ms=main_res["call_unhooked_ms"],
+                    warm_kernel_ms=main_res["warm_kernel_ms"],
+                    warm_frac=rate(main_res["warm_kernel_ms"]) / peak,
+                    warm_call_ms=main_res["warm_call_ms"],
+                    samples=main_res["samples"], sample_warmup=main_res["sample_warmup"])
+
+    cpu = None
+    per_cfg = {}
+    if not args.no_cpu_baseline:
+        from workloads import make_workload
+        t = time.time()
+        cpu = oracle_rate(w, counts, 12.0, unit)
+        cpu["cpu"] = cpu_model()
+        cpu["single_core"] = oracle_rate(w, counts, 6.0, unit, threads=1)
+        c1 = make_workload("c1a")
+        from workloads import algorithmic_counts
+        c1c = algorithmic_counts(c1)
+        per_cfg["c1a"] = oracle_rate(c1, c1c, 2.0, "TFLOP/s")
+        per_cfg["c1a"]["single_core"] = oracle_rate(c1, c1c, 2.0, "TFLOP/s", threads=1)
+        log(f"[bench] cpu baseline {args.config} + c1a in {time.time() - t:.1f}s: "
+            f"{cpu['value']:.4g} {unit}")
 
     others = {}
     for name in [x for x in args.others.split(",") if x]:
         if name == args.config:
             continue
-        r = time_config(name, max(5, args.steps // 5), 2)
+        r = time_config(name, max(20, args.steps), max(10, args.warmup))
         c = r["counts"]
         others[name] = {
-            "workload": WORKLOAD_TEXT[name],
-            "kernel_ms": r["kernel_ms"], "cold_kernel_ms": r["cold_kernel_ms"],
-            "call_ms": r["call_ms"], "cold_call_ms": r["cold_call_ms"],
-            "call_GBps": c["bytes"] / (r["call_ms"] * 1e-3) / 1e9,
-            "call_TFLOPs": c["flops"] / (r["call_ms"] * 1e-3) / 1e12,
-            "step_ms": r["step_ms"],
+            "workload": WORKLOAD_TEXT[name], "layers": r["layers"],
+            "kernel_ms": r["kernel_ms"], "kernel_median_ms": r["kernel_median_ms"],
+            "call_ms": r["call_ms"], "call_unhooked_ms": r["call_unhooked_ms"],
+            "warm_kernel_ms": r["warm_kernel_ms"],
+            "warm_call_ms": r["warm_call_ms"], "step_ms": r["step_ms"],
+            "samples": r["samples"],
             "kernel_GBps": c["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9,
             "kernel_hbm_frac": c["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "kernel_TFLOPs": c["flops"] / (r["kernel_ms"] * 1e-3) / 1e12,
             "kernel_mfma_frac": c["flops"] / (r["kernel_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "call_GBps": c["bytes"] / (r["call_ms"] * 1e-3) / 1e9,
+            "call_TFLOPs": c["flops"] / (r["call_ms"] * 1e-3) / 1e12,
+            "warm_kernel_GBps": c["bytes"] / (r["warm_kernel_ms"] * 1e-3) / 1e9,
+            "warm_kernel_TFLOPs": c["flops"] / (r["warm_kernel_ms"] * 1e-3) / 1e12,
             "unique_kv_bytes": c["unique_kv_bytes"], "algorithmic_bytes": c["bytes"],
             "flops": c["flops"],
         }
-        log(f"[bench] {name}: call {r['call_ms'] * 1e3:.1f} us, kernel {r['kernel_ms'] * 1e3:.1f} us, "
+        log(f"[bench] {name}: kernel {r['kernel_ms'] * 1e3:.1f} us cold / "
+            f"{r['warm_kernel_ms'] * 1e3:.1f} us warm, call {r['call_ms'] * 1e3:.1f} us; "
             f"{others[name]['kernel_GBps']:.0f} GB/s, {others[name]['kernel_TFLOPs']:.1f} TFLOP/s")
+        if not args.no_cpu_baseline:
+            t = time.time()
+            per_cfg[name] = oracle_rate(r["w"], c, 20.0 if name == "c4" else 6.0,
+                                        config_unit(r["w"]))
+            log(f"[bench] cpu baseline {name} in {time.time() - t:.1f}s: "
+                f"{per_cfg[name]['value']:.4g} {per_cfg[name]['unit']}")
+        del r
+    if cpu is not None:
+        cpu["per_config"] = per_cfg
 
     ablation = {}
     for name in [x for x in args.ablation.split(",") if x]:
@@ -565,16 +674,10 @@ def main():
     shared = {}
     for name in [x for x in args.shared.split(",") if x]:
         shared[name] = shared_decode(name)
-    tables = block_table_build()
+    tables = block_table_build() if not args.only_main else None
     sched = None if args.no_sched else scheduled_trace()
-    ceil = ceilings()
-    offload = offload_bandwidth()
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        t = time.time()
-        cpu = cpu_baseline(w, counts)
-        log(f"[bench] cpu baseline in {time.time() - t:.1f}s: {cpu}")
+    ceil = ceilings() if not args.only_main else None
+    offload = offload_bandwidth() if not args.only_main else None
 
     out = {
         "metric": f"position-free paged attn: {metric}",
@@ -596,8 +699,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "rows": {"rope_table_ms": main_res["rope_table_ms"],
-                 "cache_write_ms": main_res["cache_write_ms"],
+        "rows": {"rope_table_ms": main_res.get("rope_table_ms"),
+                 "cache_write_ms": main_res.get("cache_write_ms"),
                  "attention_call_ms": main_res["call_ms"],
                  "attention_kernel_ms": main_res["kernel_ms"]},
         "configs": others,

@@ -414,6 +414,18 @@ int pic_decode_split_len(int seq_len, int dtype);
 int pic_set_kernel_events(void* before, void* after);
 
 /*
+ * pic_stream_read -- measurement helper: read `bytes` of device memory at
+ * `src` once (16-byte loads, `workgroups` workgroups of 256 lanes striding
+ * over the buffer), the plain streaming-read rate that the memory-bound decode
+ * path is compared with on the same device.  sink: device memory of at least
+ * workgroups * 256 uint32, almost never written (a lane stores only when its
+ * folded data equals a fixed constant; the stores keep the loads alive).
+ * Errors: PIC_EINVAL for null pointers, bytes == 0 or not a multiple of 16,
+ * workgroups outside [1, 2^20].
+ */
+int pic_stream_read(const void* src, size_t bytes, int workgroups, void* sink, void* stream);
+
+/*
  * Interleaved span-prefill scheduling (host)
  * ------------------------------------------
  * MiniPIC §2 (the scheduling paragraph after §2.2, ISPS) and §3,

@@ -35,6 +35,7 @@ EXPORTS = [
     "pic_build_block_tables", "pic_blocks_copy", "pic_sched_create", "pic_sched_destroy",
     "pic_sched_add_span", "pic_sched_add_request", "pic_sched_step", "pic_set_kernel_events",
     "pic_attn_decode_shared", "pic_attn_decode_shared_workspace_size", "pic_attn_decode_noalloc",
+    "pic_stream_read",
 ]
 PIC_SCHED_ISPS, PIC_SCHED_BARRIER = 0, 1
 PIC_SEQ_SPAN, PIC_SEQ_PROMPT, PIC_SEQ_DECODE = 0, 1, 2
@@ -116,6 +117,7 @@ def _load():
                                             + [c_void, c_void])
     lib.pic_attn_decode_shared_workspace_size.restype = c_size
     lib.pic_attn_decode_shared_workspace_size.argtypes = [c_int] * 6
+    lib.pic_stream_read.argtypes = [c_void, c_size, c_int, c_void, c_void]
     lib.pic_decode_num_splits.argtypes = [c_int, c_int]
     lib.pic_decode_split_len.argtypes = [c_int, c_int]
     for name in EXPORTS:
@@ -643,6 +645,16 @@ def pic_decode_num_splits(seq_len: int, dtype: int = PIC_BF16) -> int:
 
 def pic_decode_split_len(seq_len: int, dtype: int = PIC_BF16) -> int:
     return int(_load().pic_decode_split_len(seq_len, dtype))
+
+
+def pic_stream_read(src, workgroups: int, sink, stream=None) -> None:
+    """Measurement helper: read the device tensor `src` once with a plain streaming kernel
+    of `workgroups` x 256 lanes; sink: a device tensor of >= workgroups * 256 int32."""
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() * sink.element_size() < workgroups * 256 * 4:
+        raise ValueError("sink must hold workgroups * 256 uint32")
+    _check(_load().pic_stream_read(_ptr(src, "src"), nbytes, int(workgroups), _ptr(sink, "sink"),
+                                   _stream(stream)), "pic_stream_read")
 
 
 def pic_set_kernel_events(before=None, after=None) -> None:

@@ -18,8 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpic.so")
 
-SOURCES = ["pic_attn.hip", "pic_table.hip", "pic_cache.hip", "pic_host.cpp", "pic_spans.cpp",
-           "pic_sched.cpp"]
+SOURCES = ["pic_attn.hip", "pic_table.hip", "pic_cache.hip", "pic_stream.hip", "pic_host.cpp",
+           "pic_spans.cpp", "pic_sched.cpp"]
 HEADERS = ["pic_common.hpp", "pic_device.hpp", "pic_host.hpp"]
 
 HIPCC_FLAGS = [

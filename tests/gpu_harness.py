@@ -74,6 +74,16 @@ class DeviceWorkload:
                                          tdt)
         self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=dev)
 
+    def add_layers(self, n):
+        """n - 1 further copies of the pools, standing for the KV caches of other layers of one
+        model (same blocks, same metadata); use_layer(i) points the calls at copy i % n."""
+        self.layers = [(self.k_pool, self.v_pool)]
+        self.layers += [(self.k_pool.clone(), self.v_pool.clone()) for _ in range(n - 1)]
+        return self
+
+    def use_layer(self, i):
+        self.k_pool, self.v_pool = self.layers[i % len(self.layers)]
+
     def write_new_tokens(self):
         if self.new_slots.shape[0]:
             pic.pic_cache_write(self.new_k, self.new_v, self.new_slots, self.k_pool, self.v_pool)

@@ -28,7 +28,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = pic.library()
     names = _declared()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(pic.EXPORTS)
@@ -466,3 +466,14 @@ def test_binding_validate_mode_checks_device_values(monkeypatch):
         pic.pic_attn_prefill(*args, 19, pw.max_seq_len, torch.zeros_like(q), a["workspace"])
     with pytest.raises(ValueError, match="GPU"):
         pic.pic_attn_prefill(*args, 20, pw.max_seq_len, torch.zeros_like(q), a["workspace"])
+
+
+def test_stream_read_rejects_bad_arguments_before_launch():
+    lib = pic.library()
+    p = ctypes.c_void_p(4096)
+    assert lib.pic_stream_read(None, 1 << 20, 64, p, None) == pic.PIC_EINVAL
+    assert lib.pic_stream_read(p, 1 << 20, 64, None, None) == pic.PIC_EINVAL
+    assert lib.pic_stream_read(p, 0, 64, p, None) == pic.PIC_EINVAL
+    assert lib.pic_stream_read(p, 1000, 64, p, None) == pic.PIC_EINVAL      # not 16-byte words
+    assert lib.pic_stream_read(p, 1 << 20, 0, p, None) == pic.PIC_EINVAL
+    assert lib.pic_stream_read(p, 1 << 20, (1 << 20) + 1, p, None) == pic.PIC_EINVAL
