@@ -364,19 +364,29 @@ def ceilings(reps=20):
     import position_independent_kv_amd as pic
     nbytes = 2 << 30
     x = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
-    read = {}
-    for wgs in (1024, 2048, 4096, 8192, 16384):
+
+    def stream_rate(wgs, order=None, piece=0):
         sink = torch.zeros(wgs * 256, dtype=torch.int32, device="cuda")
         for _ in range(3):
-            pic.pic_stream_read(x, wgs, sink)
+            pic.pic_stream_read(x, wgs, sink, order, piece)
         ev = _events(reps)
         for a, b in ev:
             a.record()
-            pic.pic_stream_read(x, wgs, sink)
+            pic.pic_stream_read(x, wgs, sink, order, piece)
             b.record()
         torch.cuda.synchronize()
-        read[wgs] = nbytes / (float(np.median(_ms(ev))) * 1e-3) / 1e9
+        return nbytes / (float(np.median(_ms(ev))) * 1e-3) / 1e9
+
+    read = {wgs: stream_rate(wgs) for wgs in (1024, 2048, 4096, 8192, 16384)}
     best = max(read, key=read.get)
+    # the same bytes as randomly placed pieces: 4 KiB (one kv head of one 16-token bf16
+    # block, d = 128), 16 KiB (four heads) and 32 KiB (a whole 8-head block)
+    gather = {}
+    for piece in (4096, 16384, 32768):
+        perm = np.random.default_rng(9).permutation(nbytes // piece).astype(np.int32)
+        order = torch.from_numpy(perm).cuda()
+        gather[str(piece)] = max(stream_rate(wgs, order, piece) for wgs in (2048, 8192))
+        del order
     y = torch.empty_like(x)
     y.copy_(x)
     ev = _events(reps)
@@ -400,12 +410,15 @@ def ceilings(reps=20):
     mm_tflops = 2 * n ** 3 / (float(np.median(_ms(ev))) * 1e-3) / 1e12
     del a_, b_, c
     torch.cuda.empty_cache()
-    log(f"[bench] ceilings: streaming read {read[best]:.0f} GB/s ({best} workgroups), "
-        f"device copy {copy_gbps:.0f} GB/s, bf16 matmul {mm_tflops:.0f} TFLOP/s")
+    log(f"[bench] ceilings: streaming read {read[best]:.0f} GB/s ({best} workgroups), random "
+        f"4/16/32 KiB pieces {gather['4096']:.0f}/{gather['16384']:.0f}/{gather['32768']:.0f} "
+        f"GB/s, device copy {copy_gbps:.0f} GB/s, bf16 matmul {mm_tflops:.0f} TFLOP/s")
     return {"stream_read_GBps": read[best], "stream_read_workgroups": best,
             "stream_read_sweep_GBps": {str(k): v for k, v in read.items()},
+            "gather_read_GBps_by_piece_bytes": gather,
             "device_copy_GBps": copy_gbps, "bf16_matmul_TFLOPs": mm_tflops,
-            "note": "pic_stream_read over 2 GiB (16-byte loads, 8 per lane in flight, best grid); "
+            "note": "pic_stream_read over 2 GiB (16-byte loads, 8 per lane in flight, best grid), "
+                    "front to back and as randomly ordered pieces; "
                     "2 GiB torch copy (read + write bytes); torch.matmul bf16 8192^3; medians"}
 
 

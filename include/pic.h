@@ -167,7 +167,7 @@ int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool, con
  * than the 64 MiB, i.e. when pic_attn_workspace_size(num_reqs, num_reqs,
  * max_seq_len, ...) without its prefill-split part exceeds 67,108,864 bytes
  * (for the 32 / 8 heads, d = 128 layer: about 1.5 million keys over the whole
- * batch; 64 x 4,097 keys use 12.8 MB, 4 x 131,073 keys 22.9 MB), and
+ * batch; 64 x 4,097 keys use 11.7 MB, 4 x 131,073 keys 22.7 MB), and
  * PIC_EHIP when the array's device address cannot be obtained.
  */
 int pic_attn_decode_noalloc(const void* q, const int32_t* q_pos, const void* k_pool,
@@ -415,15 +415,22 @@ int pic_set_kernel_events(void* before, void* after);
 
 /*
  * pic_stream_read -- measurement helper: read `bytes` of device memory at
- * `src` once (16-byte loads, `workgroups` workgroups of 256 lanes striding
- * over the buffer), the plain streaming-read rate that the memory-bound decode
- * path is compared with on the same device.  sink: device memory of at least
- * workgroups * 256 uint32, almost never written (a lane stores only when its
- * folded data equals a fixed constant; the stores keep the loads alive).
- * Errors: PIC_EINVAL for null pointers, bytes == 0 or not a multiple of 16,
- * workgroups outside [1, 2^20].
+ * `src` once, with 16-byte loads (`workgroups` workgroups of 256 lanes
+ * striding over the buffer in 4 KiB segments, 8 segments per iteration), the
+ * plain streaming-read rate that the memory-bound decode path is compared
+ * with on the same device.  order: NULL reads the buffer front to back;
+ * otherwise int32 [bytes / piece_bytes] (device) lists pieces of piece_bytes
+ * (a multiple of 4096) to read whole in that order -- with a random
+ * permutation this is how a paged cache's scattered blocks are read.  Every
+ * order entry must lie in [0, bytes / piece_bytes).  sink: device memory of
+ * at least workgroups * 256 uint32, almost never written (a lane stores only
+ * when its folded data equals a fixed constant; the stores keep the loads
+ * alive).  Errors: PIC_EINVAL for null pointers, bytes == 0 or not a multiple
+ * of 4096, piece_bytes not a positive multiple of 4096 dividing bytes (when
+ * order is given), workgroups outside [1, 2^20].
  */
-int pic_stream_read(const void* src, size_t bytes, int workgroups, void* sink, void* stream);
+int pic_stream_read(const void* src, size_t bytes, const int32_t* order, int piece_bytes,
+                    int workgroups, void* sink, void* stream);
 
 /*
  * Interleaved span-prefill scheduling (host)

@@ -117,7 +117,7 @@ def _load():
                                             + [c_void, c_void])
     lib.pic_attn_decode_shared_workspace_size.restype = c_size
     lib.pic_attn_decode_shared_workspace_size.argtypes = [c_int] * 6
-    lib.pic_stream_read.argtypes = [c_void, c_size, c_int, c_void, c_void]
+    lib.pic_stream_read.argtypes = [c_void, c_size, c_void, c_int, c_int, c_void, c_void]
     lib.pic_decode_num_splits.argtypes = [c_int, c_int]
     lib.pic_decode_split_len.argtypes = [c_int, c_int]
     for name in EXPORTS:
@@ -647,13 +647,20 @@ def pic_decode_split_len(seq_len: int, dtype: int = PIC_BF16) -> int:
     return int(_load().pic_decode_split_len(seq_len, dtype))
 
 
-def pic_stream_read(src, workgroups: int, sink, stream=None) -> None:
+def pic_stream_read(src, workgroups: int, sink, order=None, piece_bytes: int = 0,
+                    stream=None) -> None:
     """Measurement helper: read the device tensor `src` once with a plain streaming kernel
-    of `workgroups` x 256 lanes; sink: a device tensor of >= workgroups * 256 int32."""
+    of `workgroups` x 256 lanes, front to back, or as pieces of piece_bytes in the order of
+    the int32 device tensor `order`; sink: a device tensor of >= workgroups * 256 int32."""
+    torch = _torch()
     nbytes = src.numel() * src.element_size()
     if sink.numel() * sink.element_size() < workgroups * 256 * 4:
         raise ValueError("sink must hold workgroups * 256 uint32")
-    _check(_load().pic_stream_read(_ptr(src, "src"), nbytes, int(workgroups), _ptr(sink, "sink"),
+    if order is not None and (piece_bytes <= 0 or order.numel() * piece_bytes != nbytes):
+        raise ValueError("order must list nbytes / piece_bytes pieces")
+    _check(_load().pic_stream_read(_ptr(src, "src"), nbytes,
+                                   _ptr(order, "order", torch.int32) if order is not None else None,
+                                   int(piece_bytes), int(workgroups), _ptr(sink, "sink"),
                                    _stream(stream)), "pic_stream_read")
 
 

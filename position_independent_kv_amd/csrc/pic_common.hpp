@@ -32,8 +32,11 @@ constexpr int split_len(int L, int kstep) {
   return L <= 0 ? kstep : cdiv(cdiv(L, num_chunks_target(L)), kstep) * kstep;
 }
 constexpr int num_splits(int L, int kstep) { return L <= 0 ? 1 : cdiv(L, split_len(L, kstep)); }
-// Upper bound of num_splits over all L <= max_len.
-constexpr int max_splits(int max_len) { return max_len <= 0 ? 1 : cdiv(max_len, kSplitTarget) + 1; }
+// Upper bound of num_splits over all L <= max_len, and the exact maximum:
+// num_splits(L) <= num_chunks_target(L) (chunks are at least L / target long),
+// which never decreases with L.  The decode grid is sized by it, so a batch
+// of equal contexts launches no empty chunk workgroups.
+constexpr int max_splits(int max_len) { return num_chunks_target(max_len); }
 
 // Work-list item kinds (the mixed launch).
 constexpr int kItemPrefill = 0;

@@ -1,9 +1,12 @@
-// pic_stream_read: a plain streaming read of device memory, the ceiling the
-// memory-bound decode path is measured against on the same machine.  Each
-// workgroup reads contiguous runs of 256 x U 16-byte words (U loads in flight
-// per lane), grid-stride over the buffer; the data is folded into one word per
-// lane, which is stored only when it equals a fixed constant, so no load can
-// be dropped and (almost) nothing is written.
+// pic_stream_read: plain streaming reads of device memory, the ceilings the
+// memory-bound decode path is measured against on the same machine.  The
+// buffer is read as 4 KiB segments (256 lanes x 16 bytes), each workgroup
+// taking U segments per iteration (U loads in flight per lane), grid-stride.
+// Without an order the segments are read front to back; with one, the buffer
+// is a list of pieces of piece_bytes (a multiple of 4 KiB) read whole in the
+// listed order, which is how a paged cache's randomly placed blocks are read.
+// The data is folded into one word per lane, stored only when it equals a
+// fixed constant, so no load can be dropped and (almost) nothing is written.
 #include <hip/hip_runtime.h>
 
 #include "pic.h"
@@ -11,20 +14,23 @@
 namespace pic {
 
 constexpr int kStreamUnroll = 8;
+constexpr long long kSegBytes = 4096;
 
 template <int U>
 __global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restrict__ src,
-                                                          long long n,
+                                                          long long nseg,
+                                                          const int32_t* __restrict__ order,
+                                                          long long seg_per_piece,
                                                           unsigned* __restrict__ sink) {
-  const long long per = 256LL * U;
   unsigned acc = 0;
-  for (long long base = (long long)blockIdx.x * per; base < n;
-       base += (long long)gridDim.x * per) {
+  for (long long s0 = (long long)blockIdx.x * U; s0 < nseg; s0 += (long long)gridDim.x * U) {
     uint4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const long long i = base + u * 256 + threadIdx.x;
-      v[u] = i < n ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+      const long long s = s0 + u;
+      long long seg = s;
+      if (order && s < nseg) seg = (long long)order[s / seg_per_piece] * seg_per_piece + s % seg_per_piece;
+      v[u] = s < nseg ? src[seg * (kSegBytes / 16) + threadIdx.x] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -34,12 +40,19 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restric
 
 }  // namespace pic
 
-extern "C" int pic_stream_read(const void* src, size_t bytes, int workgroups, void* sink,
-                               void* stream) {
-  if (!src || !sink || bytes == 0 || bytes % 16 || workgroups <= 0 || workgroups > (1 << 20))
+extern "C" int pic_stream_read(const void* src, size_t bytes, const int32_t* order,
+                               int piece_bytes, int workgroups, void* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % pic::kSegBytes || workgroups <= 0 ||
+      workgroups > (1 << 20))
     return PIC_EINVAL;
+  long long seg_per_piece = 1;
+  if (order) {
+    if (piece_bytes <= 0 || piece_bytes % pic::kSegBytes || bytes % (size_t)piece_bytes)
+      return PIC_EINVAL;
+    seg_per_piece = piece_bytes / pic::kSegBytes;
+  }
   hipLaunchKernelGGL(pic::stream_read_kernel<pic::kStreamUnroll>, dim3((unsigned)workgroups),
                      dim3(256), 0, (hipStream_t)stream, (const uint4*)src,
-                     (long long)(bytes / 16), (unsigned*)sink);
+                     (long long)(bytes / pic::kSegBytes), order, seg_per_piece, (unsigned*)sink);
   return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }

@@ -471,9 +471,13 @@ def test_binding_validate_mode_checks_device_values(monkeypatch):
 def test_stream_read_rejects_bad_arguments_before_launch():
     lib = pic.library()
     p = ctypes.c_void_p(4096)
-    assert lib.pic_stream_read(None, 1 << 20, 64, p, None) == pic.PIC_EINVAL
-    assert lib.pic_stream_read(p, 1 << 20, 64, None, None) == pic.PIC_EINVAL
-    assert lib.pic_stream_read(p, 0, 64, p, None) == pic.PIC_EINVAL
-    assert lib.pic_stream_read(p, 1000, 64, p, None) == pic.PIC_EINVAL      # not 16-byte words
-    assert lib.pic_stream_read(p, 1 << 20, 0, p, None) == pic.PIC_EINVAL
-    assert lib.pic_stream_read(p, 1 << 20, (1 << 20) + 1, p, None) == pic.PIC_EINVAL
+    f = lib.pic_stream_read
+    assert f(None, 1 << 20, None, 0, 64, p, None) == pic.PIC_EINVAL
+    assert f(p, 1 << 20, None, 0, 64, None, None) == pic.PIC_EINVAL
+    assert f(p, 0, None, 0, 64, p, None) == pic.PIC_EINVAL
+    assert f(p, 1000, None, 0, 64, p, None) == pic.PIC_EINVAL           # not 4 KiB segments
+    assert f(p, 1 << 20, None, 0, 0, p, None) == pic.PIC_EINVAL
+    assert f(p, 1 << 20, None, 0, (1 << 20) + 1, p, None) == pic.PIC_EINVAL
+    assert f(p, 1 << 20, p, 0, 64, p, None) == pic.PIC_EINVAL            # pieces need a size
+    assert f(p, 1 << 20, p, 6144, 64, p, None) == pic.PIC_EINVAL         # not 4 KiB multiples
+    assert f(p, 3 << 12, p, 8192, 64, p, None) == pic.PIC_EINVAL         # does not divide bytes
