@@ -92,12 +92,12 @@ def time_config(name, steps, warmup, with_rows=False, only_timed=False):
     """Time one config.  Timed region (the benchmark's K steps, after W warm-up steps):
     step k writes the new tokens into layer k's pools and runs the attention call on them,
     cycling over pool_layers(w) copies, so every call is cold (the Infinity Cache holds
-    other layers' data).  Each step records HIP events around the whole attention call
-    and has the library record a pair right around its main kernel (same stream), so the
-    kernel and call figures come from the same steps.  Unless only_timed, with >= 10
-    warm-ups and >= 20 samples each: the same cold calls without the kernel events (what
-    recording them costs), and the main kernel and the call warm (one layer back to
-    back)."""
+    other layers' data); the library records HIP events right around the call's main
+    kernel on the launch stream (kernel_*: mean and median over the K steps).  Unless
+    only_timed, with >= 10 warm-ups and >= 20 samples each, cold: events around the whole
+    call and around its main kernel in the same steps (call_ms with call_kernel_ms, the
+    pair to compare), the call with no kernel events (what recording them costs); warm
+    (one layer back to back): the main kernel and the call."""
     import torch
 
     import position_independent_kv_amd as pic
@@ -136,21 +136,31 @@ def time_config(name, steps, warmup, with_rows=False, only_timed=False):
             dw.step()
 
     warm_up(warmup, lambda k: k)
+    kev = _events(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    kern, call = loop(steps, lambda k: k, True, first=warmup)
+    for k in range(steps):
+        dw.use_layer(warmup + k)
+        dw.write_new_tokens()
+        pic.pic_set_kernel_events(*kev[k])
+        dw.attention()
+    pic.pic_set_kernel_events(None, None)
+    torch.cuda.synchronize()
     t1 = time.perf_counter()
+    kern = _ms(kev)
     res = dict(name=name, w=w, counts=counts, layers=nl, step_ms=(t1 - t0) * 1e3 / steps,
                kernel_ms=float(kern.mean()), kernel_median_ms=float(np.median(kern)),
-               call_ms=float(np.median(call)), call_mean_ms=float(call.mean()),
                step_bytes=step_counts(w, counts))
     if not only_timed:
         n, nw = max(20, steps), max(10, warmup)
         warm_up(nw, lambda k: k)
-        _, plain = loop(n, lambda k: k, False)
+        ck, cc = loop(n, lambda k: k, True)        # cold: kernel and call of the same steps
+        warm_up(nw, lambda k: k)
+        _, plain = loop(n, lambda k: k, False)     # cold: the call alone
         warm_up(nw, lambda k: 0)
-        wk, wc = loop(n, lambda k: 0, True)
-        res.update(call_unhooked_ms=float(np.median(plain)),
+        wk, wc = loop(n, lambda k: 0, True)        # warm: one layer back to back
+        res.update(call_kernel_ms=float(np.median(ck)), call_ms=float(np.median(cc)),
+                   call_unhooked_ms=float(np.median(plain)),
                    warm_kernel_ms=float(np.median(wk)), warm_call_ms=float(np.median(wc)),
                    samples=n, sample_warmup=nw)
     if with_rows and not only_timed:
@@ -422,6 +432,80 @@ def ceilings(reps=20):
                     "2 GiB torch copy (read + write bytes); torch.matmul bf16 8192^3; medians"}
 
 
+def attention_ceiling(reps=20):
+    """The box's own dense attention at the chunked-prefill shape, for context: torch's
+    scaled_dot_product_attention restricted to its flash backend (no fallback to a math
+    path), bf16, 8 requests x 32 heads x 512 queries over 4608 keys (kv heads expanded
+    to 32, keys already rotated: no paging, no positions), dense and with the
+    bottom-right causal mask.  Flops counted as for the path: 4 d per unmasked
+    (query, key, head)."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    from torch.nn.attention.bias import causal_lower_right
+    B, H, Tq, Tk, d = 8, 32, 512, 4608, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    q = torch.randn((B, H, Tq, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, H, Tk, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, H, Tk, d), generator=g, device="cuda").to(torch.bfloat16)
+    res = {"shape": f"{B} x {H} heads x {Tq} queries x {Tk} keys, d {d}, bf16"}
+    pairs = {"dense": Tq * Tk, "causal_lower_right": Tq * (Tk - Tq) + Tq * (Tq + 1) // 2}
+    for label, mask in [("dense", None), ("causal_lower_right", causal_lower_right(Tq, Tk))]:
+        try:
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+                torch.cuda.synchronize()
+                ev = _events(reps)
+                for a, b in ev:
+                    a.record()
+                    torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+                    b.record()
+                torch.cuda.synchronize()
+            ms = float(np.median(_ms(ev)))
+            res[label] = {"ms": ms, "TFLOPs": 4 * d * B * H * pairs[label] / (ms * 1e-3) / 1e12}
+        except Exception as e:  # the flash backend may not take this mask on this build
+            res[label] = {"error": f"{type(e).__name__}: {str(e)[:160]}"}
+    del q, k, v
+    torch.cuda.empty_cache()
+    log(f"[bench] attention ceiling (torch SDPA flash): {res}")
+    return res
+
+
+def prefill_scaling(lengths=(512, 1024, 2048, 4096, 8192, 16384), reps=10):
+    """One causal span prefill alone (q_len = seq_len = N, positions 0..N-1, the span
+    written by the step) at growing N: the mixed launch's main kernel time and TFLOP/s
+    (medians of `reps` after 3 warm-ups, warm), the kernel-level counterpart of prefill
+    time growing with the span length."""
+    import torch
+
+    import position_independent_kv_amd as pic
+    from tests.gpu_harness import DeviceWorkload
+    from workloads import algorithmic_counts, make_workload
+    res = {}
+    for n in lengths:
+        w = make_workload(f"span{n}", builder="mixed", seed=7, n_chunks=1, chunk=n, n_dec=0,
+                          per_dec=0)
+        c = algorithmic_counts(w)
+        dw = DeviceWorkload(w)
+        dw.write_new_tokens()
+        for _ in range(3):
+            dw.attention()
+        ev = _events(reps)
+        for a, b in ev:
+            pic.pic_set_kernel_events(a, b)
+            dw.attention()
+        pic.pic_set_kernel_events(None, None)
+        torch.cuda.synchronize()
+        ms = float(np.median(_ms(ev)))
+        res[str(n)] = {"kernel_ms": ms, "TFLOPs": c["flops"] / (ms * 1e-3) / 1e12,
+                       "flops": c["flops"]}
+        del dw
+        torch.cuda.empty_cache()
+    log("[bench] prefill scaling (one causal span): " +
+        ", ".join(f"{k}: {v['kernel_ms'] * 1e3:.0f} us {v['TFLOPs']:.0f} TF/s" for k, v in res.items()))
+    return res
+
+
 def block_table_build(reps=5):
     """Host cost of the span-aware block tables (pic_build_block_tables) for a batch
     composed like the default decode workload: 64 prompts of 4 x 1024 tokens, two of
@@ -619,10 +703,10 @@ def main():
                 kernel_ms=main_res["kernel_ms"], kernel_median_ms=main_res["kernel_median_ms"],
                 algorithmic_bytes=counts["bytes"], algorithmic_flops=counts["flops"],
                 unique_kv_bytes=counts["unique_kv_bytes"])
-    roof.update(call_ms=main_res["call_ms"], call_mean_ms=main_res["call_mean_ms"],
-                call_frac=rate(main_res["call_ms"]) / peak)
     if "warm_kernel_ms" in main_res:
-        roof.update(call_unhooked_ms=main_res["call_unhooked_ms"],
+        roof.update(call_ms=main_res["call_ms"], call_kernel_ms=main_res["call_kernel_ms"],
+                    call_frac=rate(main_res["call_unhooked_ms"]) / peak,
+                    call_unhooked_ms=main_res["call_unhooked_ms"],
                     warm_kernel_ms=main_res["warm_kernel_ms"],
                     warm_frac=rate(main_res["warm_kernel_ms"]) / peak,
                     warm_call_ms=main_res["warm_call_ms"],
@@ -653,7 +737,8 @@ def main():
         others[name] = {
             "workload": WORKLOAD_TEXT[name], "layers": r["layers"],
             "kernel_ms": r["kernel_ms"], "kernel_median_ms": r["kernel_median_ms"],
-            "call_ms": r["call_ms"], "call_unhooked_ms": r["call_unhooked_ms"],
+            "call_ms": r["call_ms"], "call_kernel_ms": r["call_kernel_ms"],
+            "call_unhooked_ms": r["call_unhooked_ms"],
             "warm_kernel_ms": r["warm_kernel_ms"],
             "warm_call_ms": r["warm_call_ms"], "step_ms": r["step_ms"],
             "samples": r["samples"],
@@ -661,15 +746,15 @@ def main():
             "kernel_hbm_frac": c["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "kernel_TFLOPs": c["flops"] / (r["kernel_ms"] * 1e-3) / 1e12,
             "kernel_mfma_frac": c["flops"] / (r["kernel_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "call_GBps": c["bytes"] / (r["call_ms"] * 1e-3) / 1e9,
-            "call_TFLOPs": c["flops"] / (r["call_ms"] * 1e-3) / 1e12,
+            "call_GBps": c["bytes"] / (r["call_unhooked_ms"] * 1e-3) / 1e9,
+            "call_TFLOPs": c["flops"] / (r["call_unhooked_ms"] * 1e-3) / 1e12,
             "warm_kernel_GBps": c["bytes"] / (r["warm_kernel_ms"] * 1e-3) / 1e9,
             "warm_kernel_TFLOPs": c["flops"] / (r["warm_kernel_ms"] * 1e-3) / 1e12,
             "unique_kv_bytes": c["unique_kv_bytes"], "algorithmic_bytes": c["bytes"],
             "flops": c["flops"],
         }
         log(f"[bench] {name}: kernel {r['kernel_ms'] * 1e3:.1f} us cold / "
-            f"{r['warm_kernel_ms'] * 1e3:.1f} us warm, call {r['call_ms'] * 1e3:.1f} us; "
+            f"{r['warm_kernel_ms'] * 1e3:.1f} us warm, call {r['call_unhooked_ms'] * 1e3:.1f} us; "
             f"{others[name]['kernel_GBps']:.0f} GB/s, {others[name]['kernel_TFLOPs']:.1f} TFLOP/s")
         if not args.no_cpu_baseline:
             t = time.time()
@@ -690,6 +775,9 @@ def main():
     tables = block_table_build() if not args.only_main else None
     sched = None if args.no_sched else scheduled_trace()
     ceil = ceilings() if not args.only_main else None
+    if ceil is not None:
+        ceil["attention"] = attention_ceiling()
+    scaling = prefill_scaling() if not args.only_main else None
     offload = offload_bandwidth() if not args.only_main else None
 
     out = {
@@ -714,7 +802,7 @@ def main():
         "cpu_baseline": cpu,
         "rows": {"rope_table_ms": main_res.get("rope_table_ms"),
                  "cache_write_ms": main_res.get("cache_write_ms"),
-                 "attention_call_ms": main_res["call_ms"],
+                 "attention_call_ms": main_res.get("call_unhooked_ms"),
                  "attention_kernel_ms": main_res["kernel_ms"]},
         "configs": others,
         "rope_ablation": ablation,
@@ -722,6 +810,7 @@ def main():
         "block_tables": tables,
         "scheduled_trace": sched,
         "ceilings": ceil,
+        "prefill_scaling": scaling,
         "offload": offload,
         "source_hash": source_hash(),
     }
