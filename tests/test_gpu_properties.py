@@ -470,3 +470,18 @@ def test_refused_work_list_fills_nan():
     full = dw.attention()
     torch.cuda.synchronize()
     assert _same_bits(out, full[:T])
+
+
+@pytest.mark.parametrize("kw", [SMALL_DEC, SMALL_PRE, SMALL_MIX], ids=["decode", "prefill", "mixed"])
+def test_validate_mode_accepts_valid_batches(kw, monkeypatch):
+    """PIC_VALIDATE=1 runs the host checks before every launch: valid batches pass them and
+    give the same bytes as without the checks."""
+    torch = _torch()
+    w, dw = _fresh(kw)
+    ref = dw.attention(out=torch.full_like(dw.q, float("nan")))
+    monkeypatch.setenv("PIC_VALIDATE", "1")
+    got = dw.attention(out=torch.full_like(dw.q, float("nan")))
+    rot = dw.build_rotated_cache().attention_rotated(out=torch.full_like(dw.q, float("nan")))
+    torch.cuda.synchronize()
+    assert _same_bits(got, ref)
+    assert torch.isfinite(rot.float()).all()
