@@ -47,11 +47,12 @@ def log(*a):
 
 
 def source_hash() -> str:
-    """Hash of the GPU kernel sources (.hip, .hpp): traffic counters are only valid for
-    this exact device code.  Host-only C++ (.cpp) does not enter."""
+    """Hash of the attention kernels' sources (pic_attn.hip and the headers it includes):
+    the traffic counters of the profiled kernels are only valid for this exact device
+    code.  The other kernels' files and host-only C++ do not enter."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "position_independent_kv_amd", "csrc")
-    for name in sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".hpp"))):
+    for name in ["pic_attn.hip", "pic_common.hpp", "pic_device.hpp", "pic_host.hpp"]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())

@@ -421,8 +421,8 @@ int pic_set_kernel_events(void* before, void* after);
  * with on the same device.  order: NULL reads the buffer front to back;
  * otherwise int32 [bytes / piece_bytes] (device) lists pieces of piece_bytes
  * (a multiple of 4096) to read whole in that order -- with a random
- * permutation this is how a paged cache's scattered blocks are read.  Every
- * order entry must lie in [0, bytes / piece_bytes).  sink: device memory of
+ * permutation this is how a paged cache's scattered blocks are read.  An
+ * entry outside [0, bytes / piece_bytes) reads the last piece.  sink: device memory of
  * at least workgroups * 256 uint32, almost never written (a lane stores only
  * when its folded data equals a fixed constant; the stores keep the loads
  * alive).  Errors: PIC_EINVAL for null pointers, bytes == 0 or not a multiple

@@ -22,6 +22,7 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restric
                                                           const int32_t* __restrict__ order,
                                                           long long seg_per_piece,
                                                           unsigned* __restrict__ sink) {
+  const unsigned long long last_piece = (unsigned long long)(nseg / seg_per_piece) - 1;
   unsigned acc = 0;
   for (long long s0 = (long long)blockIdx.x * U; s0 < nseg; s0 += (long long)gridDim.x * U) {
     uint4 v[U];
@@ -29,7 +30,11 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restric
     for (int u = 0; u < U; ++u) {
       const long long s = s0 + u;
       long long seg = s;
-      if (order && s < nseg) seg = (long long)order[s / seg_per_piece] * seg_per_piece + s % seg_per_piece;
+      if (order && s < nseg) {  // an entry outside the buffer reads its last piece
+        const unsigned long long piece =
+            min((unsigned long long)(unsigned)order[s / seg_per_piece], last_piece);
+        seg = (long long)piece * seg_per_piece + s % seg_per_piece;
+      }
       v[u] = s < nseg ? src[seg * (kSegBytes / 16) + threadIdx.x] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll

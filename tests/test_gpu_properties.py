@@ -485,3 +485,24 @@ def test_validate_mode_accepts_valid_batches(kw, monkeypatch):
     torch.cuda.synchronize()
     assert _same_bits(got, ref)
     assert torch.isfinite(rot.float()).all()
+
+
+def test_stream_read_helper_orders():
+    """The streaming-read measurement helper over a buffer front to back, as a permutation
+    of 16 KiB pieces, and with piece ids outside the buffer (read as its last piece): each
+    call completes and stores nothing (the sink keeps its fill)."""
+    torch = _torch()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)  # fixed data: whether a lane's folded word hits the store constant is fixed
+    x = torch.randint(0, 255, (64 << 20,), dtype=torch.uint8, device="cuda", generator=g)
+    sink = torch.full((512 * 256,), 7, dtype=torch.int32, device="cuda")
+    n = (64 << 20) // 16384
+    perm = torch.from_numpy(np.random.default_rng(1).permutation(n).astype(np.int32)).cuda()
+    bad = perm.clone()
+    bad[::3] = n + 5
+    bad[1::3] = -2
+    pic.pic_stream_read(x, 512, sink)
+    pic.pic_stream_read(x, 512, sink, perm, 16384)
+    pic.pic_stream_read(x, 512, sink, bad, 16384)
+    torch.cuda.synchronize()
+    assert bool((sink == 7).all())
