@@ -166,8 +166,8 @@ int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool, con
  * Errors as pic_attn_decode, plus PIC_EWORKSPACE when the batch needs more
  * than the 64 MiB, i.e. when pic_attn_workspace_size(num_reqs, num_reqs,
  * max_seq_len, ...) without its prefill-split part exceeds 67,108,864 bytes
- * (for the 32 / 8 heads, d = 128 layer: about 1.5 million keys over the whole
- * batch; 64 x 4,097 keys use 11.7 MB, 4 x 131,073 keys 22.7 MB), and
+ * (for the 32 / 8 heads, d = 128 layer: about 2 million keys over the whole
+ * batch; 64 x 4,097 keys use 8.5 MB, 4 x 131,073 keys 17.1 MB), and
  * PIC_EHIP when the array's device address cannot be obtained.
  */
 int pic_attn_decode_noalloc(const void* q, const int32_t* q_pos, const void* k_pool,

@@ -24,7 +24,7 @@
 //
 // Kernels:
 // - decode_kernel (batches of q_len == 1, HBM bound): one workgroup of four
-//   waves per (request, key chunk of about 384 keys, four kv heads), one wave
+//   waves per (request, key chunk of about 512 keys, four kv heads), one wave
 //   per kv head, the G query heads of the kv head as the columns of a
 //   16x16x32 tile.  The chunk's block ids and positions, and each 32-key
 //   step's cos/sin rows, are staged in LDS once per workgroup; every wave

@@ -65,16 +65,24 @@ def test_workspace_size_rules():
     assert f(8, 100, 5000, 32, 8, 128, pic.PIC_BF16) >= a
 
 
+SPLIT_TARGET = 512  # keys per decode chunk the library aims at (pic_common.hpp)
+
+
 @pytest.mark.parametrize("dtype,kstep", [(pic.PIC_BF16, 32), (pic.PIC_F32, 16)])
 def test_split_policy(dtype, kstep):
-    for L in list(range(1, 3000)) + [4097, 8193, 131073, 131072, 65537]:
+    t = SPLIT_TARGET
+    prev = 1
+    for L in list(range(1, 4000)) + [4097, 8193, 131073, 131072, 65537]:
         S = pic.pic_decode_num_splits(L, dtype)
         c = pic.pic_decode_split_len(L, dtype)
         assert c % kstep == 0
         assert (S - 1) * c < L <= S * c          # every chunk non-empty, all keys covered
-        assert S <= -(-L // 384) + 1             # within the workspace bound
-        assert S <= max(1, (L + 192) // 384)     # at most round(L / 384) chunks
-        assert c <= 576 + kstep                  # chunks stay near the 384-key target
+        bound = max(1, (L + t // 2) // t)        # round(L / target): what the grid is sized by
+        assert S <= bound                        # ... so no request has more chunks
+        assert c <= t + t // 2 + kstep           # chunks stay near the target
+        if L < 4000:
+            assert bound >= prev                 # the bound never falls as L grows
+            prev = bound
 
 
 def _c_args(n):
