@@ -158,7 +158,8 @@ int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool, con
  * bit for bit, with no workspace argument.  The chunk partials go to a
  * fixed array of 64 MiB that the library holds on each device it runs on
  * until the process ends (its address is looked up once per device, on the
- * first call with that device current).  The call itself allocates nothing.
+ * first call with that device current: make that first call outside HIP graph
+ * capture; later calls can be captured).  The call itself allocates nothing.
  * The array needs no initialisation (every call writes what it reads) and
  * keeps the last call's contents; calls that overlap in time on one device
  * race on it, so the caller serialises them (one stream, or events).

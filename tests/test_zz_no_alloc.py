@@ -74,3 +74,37 @@ def test_noalloc_full_size_decode_matches_and_refuses_oversized_batches():
     assert e.value.status == pic.PIC_EWORKSPACE
     torch.cuda.synchronize()
     assert bool((keep == 3.0).all())
+
+
+def test_noalloc_step_replays_from_a_hip_graph():
+    """What the entry point is for: a decode step (cache write + attention) captured in a
+    HIP graph with no workspace to allocate, replayed four times with eager work (the
+    workspace decode, which writes different memory) between replays; every replay equals
+    the eager result bit for bit.  The first call on a device looks up the array's address
+    (hipGetSymbolAddress), so it is made before capturing."""
+    torch = _torch()
+    w = make_workload("noalloc_graph", builder="decode", seed=75, R=8, seg_len=400, n_seg=3,
+                      n_shared=1, n_spans=4)
+    dw = DeviceWorkload(w)
+    dw.write_new_tokens()
+    eager = _noalloc(dw, torch.full_like(dw.q, float("nan"))).clone()
+    static_out = torch.empty_like(dw.q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the side stream, outside the graph
+        dw.write_new_tokens()
+        _noalloc(dw, static_out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dw.write_new_tokens()
+        _noalloc(dw, static_out)
+    for i in range(4):
+        static_out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(static_out), _bits(eager)), i
+        other = dw.attention(out=torch.empty_like(dw.q))
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(other), _bits(eager)), i
