@@ -875,6 +875,27 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
+// Swizzle of the V^T stage: row r's unit u sits at slot u ^ vswz(r), so the
+// PV operand reads (32 rows, one unit each, per half wave) and the direct
+// loads (8 rows x 8 units per 64 lanes) hit distinct LDS banks.
+__device__ __forceinline__ int vswz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
+
+// One 16-byte direct load per lane from global memory into LDS: lane i's
+// bytes land at LDS byte address lds_base + 16 i (lds_base: wave-uniform).
+// Inline assembly, so the compiler neither orders LDS reads behind it nor
+// counts it: callers wait for it with vm_wait_all() before the barrier that
+// publishes the stage.
+__device__ __forceinline__ void lds_direct_load16(const void* src, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 template <int D, int NW, int KS>
 struct Pf {
   static constexpr int NTH = NW * 64;              // threads
@@ -885,7 +906,7 @@ struct Pf {
   static constexpr int NHC = NCH / 2;              // chunks of the first half of d
   static constexpr int NDB = D / 32;               // 32-row d blocks of O^T
   static constexpr int KLD = D + 8;                // LDS K row stride (bf16)
-  static constexpr int VLD = KSTEP + 8;            // LDS V^T row stride (bf16)
+  static constexpr int VLD = KSTEP;                // LDS V^T row length (bf16), swizzled
   static constexpr int QLD = D + 8;                // LDS row stride of the query operand
   static constexpr int KBUF = KSTEP * KLD;         // bf16 elements of one K stage
   static constexpr int VBUF = D * VLD;             // bf16 elements of one V^T stage
@@ -895,12 +916,10 @@ struct Pf {
   static constexpr int BYTES = (Q_OFF + ROWS * QLD) * 2;
   static constexpr int KPT = KSTEP * (D / 2) / NTH;  // rotation pairs per thread
   static constexpr int KTPK = (D / 2) / KPT;         // threads per key
-  static constexpr int VPT = KSTEP * D / NTH;        // V^T elements per thread
-  static constexpr int VTPR = KSTEP / VPT;           // threads per V^T row
-  static constexpr int VR = VPT < kBlockSize ? VPT : kBlockSize;  // keys per V load
-  static constexpr int NVR = VPT / VR;                             // V loads per thread
+  // V^T stage: D rows x 64 keys as 16-byte units (8 keys), unit u of row
+  // r at position 8r + (u ^ vswz(r)); each wave fills NDMA runs of 64 units
+  static constexpr int NDMA = D * KSTEP * 2 / (NW * 64 * 16);
   static_assert(KPT % 4 == 0 && KPT <= D / 2, "whole 8-byte K pieces per thread");
-  static_assert(VPT % VR == 0 && kBlockSize % VR == 0, "V runs stay inside one block");
 };
 
 // One prefill tile, bf16, software-pipelined over 32-key blocks so each wave
@@ -909,11 +928,13 @@ struct Pf {
 // run while the next K step is rotated into LDS.
 //
 // Staging: each 64-key step is gathered from the paged pools once per
-// workgroup.  Every thread loads its share of K rows, cos/sin rows and V^T
-// runs into registers one step before they are written; K is rotated on the
-// way into LDS.  K is staged two steps ahead (three K stages: the block
-// being exponentiated may be re-read, the next block is being multiplied,
-// and the step after is being written), V^T one step ahead (two stages).
+// workgroup.  Every thread loads its share of K rows and cos/sin rows into
+// registers one step before they are written; K is rotated on the way into
+// LDS.  V^T needs no arithmetic, so it goes from the pool straight into LDS
+// (16-byte direct loads, no registers, no LDS write instructions).  K is
+// staged two steps ahead (three K stages: the block being exponentiated may
+// be re-read, the next block is being multiplied, and the step after is
+// being written), V^T one step ahead (two stages).
 // One barrier per step.  The rotated query rows (the B operand, pre-scaled
 // by log2(e)/sqrt(d) so scores come out in base-2 units) sit in a per-wave
 // LDS slice.  Steps that lie wholly below the causal diagonal skip the mask.
@@ -921,6 +942,9 @@ template <int D, int NW, int KS, bool ROT>
 __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int split,
                                   int nsplit, int pslot, unsigned char* smem) {
   using P = Pf<D, NW, KS>;
+  static_assert(P::KSTEP == 64 && P::NDMA >= 1 && P::NDMA <= 2 &&
+                    P::NDMA * NW * 64 * 8 == D * P::KSTEP,
+                "V^T stages fill in whole 1 KiB direct-load runs per wave");
   typedef Mma32::Op Op;
   typedef Mma32::Acc Acc;
   const int tid = threadIdx.x;
@@ -976,54 +1000,57 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
   const size_t blk_bytes = (size_t)a.hkv * kBlockSize * D * sizeof(bf16);
 
   // staging: thread -> (key skey, pairs si0..si0+KPT) for K and the table,
-  // (d row vd, keys vk0..vk0+VPT) for V^T.  Every step starts at a multiple
-  // of 64, so a thread always reads the same row of a block (skey % 16) and
-  // the same key offset of a V run: the per-step address is block base plus a
-  // fixed per-thread offset.  A key at or beyond L reads a valid slot of the
-  // last block (its score is masked, its V zeroed); a step past the end
-  // re-reads valid slots and is never used.
+  // V^T units as below.  Every step starts at a multiple of 64, so a thread
+  // always reads the same row of a block (skey % 16) and the same units of
+  // V^T: the per-step address is block base plus a fixed per-thread offset.
+  // A key at or beyond L reads a valid slot of the last block (its score is
+  // masked, its V zeroed); a step past the end re-reads valid slots and is
+  // never used.
   const int skey = tid / P::KTPK;
   const int si0 = (tid % P::KTPK) * P::KPT;
-  const int vd = tid / P::VTPR;
-  const int vk0 = (tid % P::VTPR) * P::VPT;
+  // V^T direct loads: the wave fills LDS runs vrun0 .. vrun0 + NDMA - 1 (64
+  // units each, in slot order); in run i this lane's unit is row
+  // vrow0 + 8i, unit vu ^ i (the swizzle of row vrow0 + 8i is that of vrow0
+  // with bit 0 flipped), so both of its units lie in the same 16-key block
+  const int vrun0 = P::NDMA * wave;
+  const int vrow0 = vrun0 * 8 + (lane >> 3);
+  const int vu = (lane & 7) ^ vswz(vrow0);
+  const int vbi = vu >> 1;  // block of the step this lane's units lie in
   const char* kthr = (const char*)a.k_pool +
                      (((size_t)g * kBlockSize + (skey & 15)) * D + si0) * sizeof(bf16);
   const char* cthr = (const char*)(a.cos_tab + si0);
   const char* sthr = (const char*)(a.sin_tab + si0);
-  const char* vthr = (const char*)a.v_pool +
-                     (((size_t)g * D + vd) * kBlockSize + (vk0 & 15)) * sizeof(bf16);
+  const char* vthr = (const char*)a.v_pool + ((size_t)g * D + vrow0) * kBlockSize * sizeof(bf16);
+  const unsigned v_lds0 = __builtin_amdgcn_readfirstlane(
+      lds_address(lds + P::V_OFF) + (unsigned)vrun0 * 1024u);
   typedef vec<bf16, P::KPT> KV;
   typedef vec<float, P::KPT> TV;
-  typedef vec<bf16, P::VR> VRun;
   struct KRegs {
     KV lo, hi;  // unrotated halves of the thread's K piece
     TV c, s;    // their cos/sin
   };
   KRegs kr;
-  VRun vr[P::NVR];
   // Addresses (block ids, position) of the next loads, looked up one step
   // before those loads are issued: kmeta_* / vmeta_* hold the ones in use,
   // the *_nx copies the ones being fetched.  Lookups are issued before the
   // data loads of a step, so waiting for a lookup never waits for data (the
   // load counter completes in issue order).
-  int kmeta_blk, kmeta_pos, vmeta_blk[P::NVR];
-  int kmeta_blk_nx, kmeta_pos_nx = 0, vmeta_blk_nx[P::NVR];
+  int kmeta_blk, kmeta_pos, vmeta_blk;
+  int kmeta_blk_nx, kmeta_pos_nx = 0, vmeta_blk_nx;
   auto kmeta = [&](int kb) {  // kb: absolute key index of a step's first key
     const int kc = min(kb + skey, L - 1);
     kmeta_blk_nx = bt[kc >> 4];
     if constexpr (ROT) kmeta_pos_nx = kp[kc];
   };
   auto vmeta = [&](int kb) {
-#pragma unroll
-    for (int u = 0; u < P::NVR; ++u) vmeta_blk_nx[u] = bt[min(kb + vk0 + u * P::VR, L - 1) >> 4];
+    vmeta_blk_nx = bt[min(kb + 16 * vbi, L - 1) >> 4];
   };
   auto kmeta_use = [&]() {
     kmeta_blk = kmeta_blk_nx;
     kmeta_pos = kmeta_pos_nx;
   };
   auto vmeta_use = [&]() {
-#pragma unroll
-    for (int u = 0; u < P::NVR; ++u) vmeta_blk[u] = vmeta_blk_nx[u];
+    vmeta_blk = vmeta_blk_nx;
   };
   // the (block, position) of key kb + skey, looked up without touching the
   // pipeline's *_nx registers
@@ -1046,12 +1073,15 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     }
   };
   auto kload = [&]() { kload_to(kr, kmeta_blk, kmeta_pos); };
-  auto vload = [&]() {
+  // V^T of step `step` straight into its LDS stage (no registers)
+  auto vdma = [&](int step) {
+    const unsigned vb = min((unsigned)vmeta_blk, (unsigned)nb_max);
+    const char* src = vthr + (size_t)vb * blk_bytes;
+    const unsigned dst = v_lds0 + (unsigned)((step % P::NVB) * P::VBUF * 2);
 #pragma unroll
-    for (int u = 0; u < P::NVR; ++u) {
-      const unsigned vb = min((unsigned)vmeta_blk[u], (unsigned)nb_max);
-      vr[u] = *reinterpret_cast<const VRun*>(vthr + (size_t)vb * blk_bytes);
-    }
+    for (int i = 0; i < P::NDMA; ++i)  // run i: 8 rows further, unit vu ^ i
+      lds_direct_load16(src + (i * 8 * kBlockSize + 8 * ((vu ^ i) & 1)) * sizeof(bf16),
+                        dst + i * 1024u);
   };
   auto kstore_from = [&](int step, const KRegs& d) {  // rotate a K piece into K stage `step`
     KV lo = d.lo, hi = d.hi;
@@ -1068,21 +1098,20 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     *reinterpret_cast<KV*>(kd + D / 2) = hi;
   };
   auto kstore = [&](int step) { kstore_from(step, kr); };
-  auto vstore = [&](int step) {  // the loaded V^T runs into V stage `step`
+  // Slots at or beyond L hold no data: once this lane's own direct loads
+  // into V stage `step` have landed, it overwrites those keys of its units
+  // with zeros (only the last step has any).
+  auto vfix = [&](int step) {
     const int kb = kofs + step * P::KSTEP;
-    bf16* vdst = lds + P::V_OFF + (step % P::NVB) * P::VBUF + vd * P::VLD + vk0;
-#pragma unroll
-    for (int u = 0; u < P::NVR; ++u) *reinterpret_cast<VRun*>(vdst + u * P::VR) = vr[u];
-    // Slots at or beyond L hold no data: overwrite them with zeros (only the
-    // last step has any).  Done as separate LDS stores after the plain ones
-    // so that the steady-state steps carry no per-element selects.
     if (kb + P::KSTEP > L) {
+      vm_wait_all();
+      bf16* vdst = lds + P::V_OFF + (step % P::NVB) * P::VBUF + (vrun0 * 64 + lane) * 8;
 #pragma unroll
-      for (int u = 0; u < P::NVR; ++u) {
-        const int key0 = kb + vk0 + u * P::VR;
+      for (int i = 0; i < P::NDMA; ++i) {
+        const int key0 = kb + 8 * (vu ^ i);
 #pragma unroll
-        for (int e = 0; e < P::VR; ++e)
-          if (key0 + e >= L) vdst[u * P::VR + e] = (bf16)0.0f;
+        for (int e = 0; e < 8; ++e)
+          if (key0 + e >= L) vdst[i * 512 + e] = (bf16)0.0f;
       }
     }
   };
@@ -1149,7 +1178,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     kload_to(k1, b1, p1);
     if (with_v) {
       vmeta_use();
-      vload();
+      vdma(0);
     }
     kmeta(kofs + 2 * P::KSTEP);
     if (with_v) vmeta(kofs + P::KSTEP);
@@ -1170,7 +1199,8 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     }
     kstore_from(0, kr);
     kstore_from(1, k1);
-    if (with_v) vstore(0);
+    vm_wait_all();
+    if (with_v) vfix(0);
     __syncthreads();
   };
   // steps below every row's diagonal (kofs is a multiple of the step)
@@ -1235,16 +1265,18 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     // O^T += V^T P^T for block h of V stage `step`: two 16-key groups, the
     // second group's operands read as the first group's multiply issue
     auto pv_block = [&](int step, int h) {
-      const bf16* vb =
-          lds + P::V_OFF + (step % P::NVB) * P::VBUF + col * P::VLD + h * 32 + 8 * hh;
+      // keys h*32 + 16m + 8hh .. +7 of row db*32 + col: unit 4h + 2m + hh
+      const bf16* vb = lds + P::V_OFF + (step % P::NVB) * P::VBUF + col * P::VLD;
+      const int y = hh ^ vswz(col);
+      const int u0 = ((4 * h) ^ y) * 8, u1 = ((4 * h + 2) ^ y) * 8;
       Op va[P::NDB];
 #pragma unroll
       for (int db = 0; db < P::NDB; ++db)
-        va[db] = *reinterpret_cast<const Op*>(vb + db * 32 * P::VLD);
+        va[db] = *reinterpret_cast<const Op*>(vb + db * 32 * P::VLD + u0);
 #pragma unroll
       for (int db = 0; db < P::NDB; ++db) {
         o[db] = Mma32::run(va[db], pb[0], o[db]);
-        va[db] = *reinterpret_cast<const Op*>(vb + db * 32 * P::VLD + 16);
+        va[db] = *reinterpret_cast<const Op*>(vb + db * 32 * P::VLD + u1);
       }
 #pragma unroll
       for (int db = 0; db < P::NDB; ++db) o[db] = Mma32::run(va[db], pb[1], o[db]);
@@ -1287,8 +1319,8 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
       vmeta_use();
       kmeta(kb + 3 * P::KSTEP);
       vmeta(kb + 2 * P::KSTEP);
-      kload();  // K step j+2 (past the end: valid slots, never used)
-      vload();  // V step j+1
+      vdma(j + 1);  // V step j+1
+      kload();      // K step j+2 (past the end: valid slots, never used)
       // keep the loads at the top of the step: they have the whole step to land
       __builtin_amdgcn_sched_barrier(0);
 
@@ -1302,7 +1334,8 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
       }
 
       kstore(j + 2);
-      vstore(j + 1);
+      vm_wait_all();
+      vfix(j + 1);
       // Instruction order for the step (the wave issues in order, so a
       // dependent MFMA chain would otherwise hold back the vector work
       // behind it): each score MFMA of the next block is followed by a slice
