@@ -881,15 +881,25 @@ __device__ __forceinline__ void sched_interleave() {
 __device__ __forceinline__ int vswz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 
 // One 16-byte direct load per lane from global memory into LDS: lane i's
-// bytes land at LDS byte address lds_base + 16 i (lds_base: wave-uniform).
-// Inline assembly, so the compiler neither orders LDS reads behind it nor
-// counts it: callers wait for it with vm_wait_all() before the barrier that
-// publishes the stage.
+// bytes land at LDS byte address lds_base + 16 i (lds_base: wave-uniform,
+// passed in M0, whose previous value the sequence restores).  Inline
+// assembly on purpose: the compiler neither counts it nor makes later LDS
+// reads wait on it (with the builtin form it may put a wait for every
+// outstanding load in front of the step's first LDS read, which serialises
+// the load pipeline), so callers wait with vm_wait_all() before the barrier
+// that publishes the stage.
 __device__ __forceinline__ void lds_direct_load16(const void* src, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_base)
-               : "memory", "m0");
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
 }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ unsigned lds_address(const void* p) {
