@@ -1428,10 +1428,17 @@ __device__ __forceinline__ unsigned xcd_position(unsigned l, unsigned n) {
   return k * 8 + x;
 }
 
-// Context-length bucket of a prefill request (64-key units, capped): the
-// mixed launch dispatches tiles of longer contexts first, so the longest
-// tiles never start last and leave the rest of the GPU idle at the end.
+// Key-count bucket of a prefill tile (64-key units, capped): the mixed
+// launch dispatches the tiles that see more keys first, so the longest tiles
+// never start last and leave the rest of the GPU idle at the end.
 __device__ __forceinline__ int len_bucket(int L) { return min(max(L, 0) >> 6, 1023); }
+// Keys tile k of a request (q_len ql, seq_len L) sees: the slots up to the
+// causal limit of its last query row (rows query rows per tile, group heads
+// per token), as the tile kernels bound their key loop.
+__device__ __forceinline__ int tile_keys(int L, int ql, int k, int rows, int group) {
+  const int last_tok = min((int)(((long long)k * rows + rows - 1) / group), ql - 1);
+  return min(L, L - ql + last_tok + 1);
+}
 
 // Steps of K/V loads each decode wave keeps in flight.  Measured on MI355X:
 // one step at two waves per SIMD beats deeper rings at one wave per SIMD.
@@ -1773,14 +1780,16 @@ __global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
 // fill the tail.  (A workgroup of either kind fills a compute unit's LDS and
 // registers, so the two kinds cannot share one; interleaving them evenly
 // measured 3% slower on the mixed 16-prefill + 128-decode batch.)
-// Prefill tiles are ordered longest first: requests by context-length bucket
-// (longest first; ranks inside a bucket from LDS atomics), inside a request
-// the last tile first (the later query rows see more keys) with the kv heads
-// innermost, and item i is dispatched as workgroup i, so consecutive tiles
-// go to different XCDs.  A tile's time grows with its context, and the
-// workgroups of one XCD run in dispatch order: long tiles bunched on one XCD
-// would end the launch alone.  With 8 kv heads every tile of one (request,
-// head) still lands on the same XCD.
+// Prefill tiles are ordered longest first by the keys each tile sees, over
+// all requests (buckets of 64 keys; ranks inside a bucket from LDS atomics),
+// the kv heads (and key chunks) of one tile next to each other, and item i
+// is dispatched as workgroup i, so consecutive tiles go to different XCDs.
+// A tile's time grows with its keys: with the longest first, the items that
+// start last are the shortest and the compute units run out of work nearly
+// together (ordering whole requests instead left the tiles of equally long
+// requests in request order, and some units idle for 12% of a launch).
+// With 8 kv heads every tile of one (request, head) still lands on the same
+// XCD.
 // Decode chunks are ordered chunk-major inside groups of requests with the
 // same chunk count (longest group first): chunk s of every request of a
 // group, then chunk s + 1, ...  Consecutive items then read the same key
@@ -1851,6 +1860,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   __shared__ int s_ptot[1024];         // prefill tiles per context-length bucket
   __shared__ int s_prank[1024];        // prefill tiles placed so far per bucket
   __shared__ long long s_pbase[1024];  // first prefill-list index of each bucket
+  __shared__ int s_ql[1024], s_len[1024];  // q_len, seq_len of the chunk's requests
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   s_bcnt[tid] = 0;
@@ -1875,24 +1885,38 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   auto nsplit_of = [&](int L) {
     return split_max > 1 ? max(1, min(split_max, L / kPrefillChunkMin)) : 1;
   };
-  // pass 1b: item totals, decode requests per chunk count, prefill items per
-  // context-length bucket
+  // pass 1b, per chunk of 1024 requests: item totals, decode requests per
+  // chunk count; then prefill items per key-count bucket, the waves taking
+  // the chunk's requests in turn and their lanes the request's tiles
   long long pf = 0, dc = 0;
-  for (int r = tid; r < num_reqs; r += 1024) {
-    const int ql = cu_q[r + 1] - cu_q[r];
-    if (ql > 1) {
-      const int L = min(seq_lens[r], len_cap);
-      const int n = hkv * cdiv(ql * group, rows) * nsplit_of(L);
-      pf += n;
-      atomicAdd(&s_ptot[len_bucket(L)], n);
-    } else if (ql == 1) {
-      const int S = num_splits(min(seq_lens[r], len_cap), kstep);
-      dc += (long long)nhg * S;
-      if (S < 1024) atomicAdd(&s_bcnt[S], 1);
-      else s_bover = 1;
+  for (int base = 0; base < num_reqs; base += 1024) {
+    const int r = base + tid;
+    int ql = 0, L = 0;
+    if (r < num_reqs) {
+      ql = cu_q[r + 1] - cu_q[r];
+      L = min(seq_lens[r], len_cap);
+      if (ql > 1) {
+        pf += (long long)hkv * cdiv(ql * group, rows) * nsplit_of(L);
+      } else if (ql == 1) {
+        const int S = num_splits(L, kstep);
+        dc += (long long)nhg * S;
+        if (S < 1024) atomicAdd(&s_bcnt[S], 1);
+        else s_bover = 1;
+      }
     }
+    s_ql[tid] = ql;
+    s_len[tid] = L;
+    __syncthreads();
+    const int nr = min(1024, num_reqs - base);
+    for (int rr = wave; rr < nr; rr += 16) {
+      const int qr = s_ql[rr], Lr = s_len[rr];
+      if (qr <= 1) continue;
+      const int n = hkv * nsplit_of(Lr);
+      for (int k = lane; k < cdiv(qr * group, rows); k += 64)
+        atomicAdd(&s_ptot[len_bucket(tile_keys(Lr, qr, k, rows, group))], n);
+    }
+    __syncthreads();
   }
-  __syncthreads();
   // totals, and the group / bucket bases (longest first: exclusive suffix
   // sums, total minus the inclusive prefix): thread b holds bucket b
   long long x[4] = {pf, dc, (long long)s_bcnt[tid] * tid * nhg, (long long)s_ptot[tid]};
@@ -1940,10 +1964,9 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
     s_kind[tid] = ql > 1 ? 1 : (ql == 1 ? 2 : 0);
     s_cnt[tid] = ql > 1 ? cdiv(ql * group, rows) : (ql == 1 ? num_splits(L, kstep) : 0);
     s_nsp[tid] = ql > 1 ? nsplit_of(L) : 1;
-    if (ql > 1) {
-      const int b = len_bucket(L);
-      s_off[tid] = s_pbase[b] + atomicAdd(&s_prank[b], hkv * s_cnt[tid] * s_nsp[tid]);
-    } else if (ql == 1) {
+    s_ql[tid] = ql;
+    s_len[tid] = L;
+    if (ql == 1) {
       s_off[tid] = chunk_major ? (long long)atomicAdd(&s_brank[s_cnt[tid]], 1)
                                : dc_base + y[0] - ndc;
     } else {
@@ -1956,16 +1979,20 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
       const int kind = s_kind[rr];
       const int cnt = s_cnt[rr];
       const long long off = s_off[rr];
-      if (kind == 1) {  // prefill tiles, last (longest) tile first, kv heads, then chunks
+      if (kind == 1) {  // prefill tiles: each at a place in its bucket, kv heads, then chunks
         const int S = s_nsp[rr];
-        for (int it = lane; it < hkv * cnt * S; it += 64) {
-          const int sp = it % S, k = (it / S) / hkv, g = (it / S) % hkv;
-          items[off + it] = make_int4(item_code(kItemPrefill, S > 1 ? sp : 0, S > 1 ? S : 0),
-                                      base + rr, g, cnt - 1 - k);
-          if (S > 1 && sp == 0) {
-            const int slot = atomicAdd(&s_pfn, 1);
-            if (slot < kSplitCUs / 2)
-              pf_tiles[slot] = make_int4(base + rr, g, cnt - 1 - k, (int)(off + it));
+        const int n = hkv * S;
+        for (int k = lane; k < cnt; k += 64) {
+          const int b = len_bucket(tile_keys(s_len[rr], s_ql[rr], k, rows, group));
+          const long long o = s_pbase[b] + atomicAdd(&s_prank[b], n);
+          for (int j = 0; j < n; ++j) {
+            const int sp = j % S, g = j / S;
+            items[o + j] = make_int4(item_code(kItemPrefill, S > 1 ? sp : 0, S > 1 ? S : 0),
+                                     base + rr, g, k);
+            if (S > 1 && sp == 0) {
+              const int slot = atomicAdd(&s_pfn, 1);
+              if (slot < kSplitCUs / 2) pf_tiles[slot] = make_int4(base + rr, g, k, (int)(o + j));
+            }
           }
         }
       } else if (kind == 2) {  // decode chunks, per chunk the kv-head groups
