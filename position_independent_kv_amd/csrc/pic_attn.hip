@@ -1428,6 +1428,11 @@ __device__ __forceinline__ unsigned xcd_position(unsigned l, unsigned n) {
   return k * 8 + x;
 }
 
+// Keys of a prefill tile that takes about as long as one decode chunk of the
+// mixed launch (8 kv heads, about kSplitTarget keys): measured 61 us per
+// chunk against 2.3 us per 64-key step of a tile.
+constexpr int kDecodeTileKeys = 4 * kSplitTarget;
+
 // Key-count bucket of a prefill tile (64-key units, capped): the mixed
 // launch dispatches the tiles that see more keys first, so the longest tiles
 // never start last and leave the rest of the GPU idle at the end.
@@ -1775,11 +1780,16 @@ __global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
 }
 
 // Planner: one workgroup of 1024 threads turns (cu_seqlens_q, seq_lens) into
-// the work list: first the prefill tiles, then the chunks of q_len == 1
-// requests, so the long MFMA-bound tiles start early and the short chunks
-// fill the tail.  (A workgroup of either kind fills a compute unit's LDS and
-// registers, so the two kinds cannot share one; interleaving them evenly
-// measured 3% slower on the mixed 16-prefill + 128-decode batch.)
+// the work list, longest items first so that the items that start last are
+// short and the compute units run out of work nearly together: the prefill
+// tiles that see at least kDecodeTileKeys keys, then the chunks of
+// q_len == 1 requests (a decode chunk of about kSplitTarget keys takes about
+// as long as a tile over kDecodeTileKeys keys), then the shorter tiles.  A
+// launch that splits tiles keeps all prefill items first (a split item's
+// partial slot is its list position, below kSplitCUs).  (A workgroup of
+// either kind fills a compute unit's LDS and registers, so the two kinds
+// cannot share one; interleaving them evenly measured 3% slower on the mixed
+// 16-prefill + 128-decode batch.)
 // Prefill tiles are ordered longest first by the keys each tile sees, over
 // all requests (buckets of 64 keys; ranks inside a bucket from LDS atomics),
 // the kv heads (and key chunks) of one tile next to each other, and item i
@@ -1928,6 +1938,14 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   s_bbase[tid] = tot[2] - x[2];
   s_pbase[tid] = tot[3] - x[3];
   const bool chunk_major = s_bover == 0;
+  // the decode items start after the prefill items of buckets bd and above
+  // (s_pbase[bd - 1] of them); the buckets below move behind the decode items
+  constexpr int bd = kDecodeTileKeys / 64;
+  static_assert(bd >= 1 && bd < 1024, "decode items sit between two buckets");
+  __syncthreads();
+  const long long dec_base = split_max > 1 ? total_pf : s_pbase[bd - 1];
+  __syncthreads();
+  if (split_max == 1 && tid < bd) s_pbase[tid] += total_dc;
   // More items than the workspace was sized for means the metadata broke a
   // precondition (cu_seqlens_q not ascending, or total_q / max_seq_len too
   // small): run nothing, and raise the flag that makes the merge launch fill
@@ -2001,7 +2019,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
           const long long di = chunk_major
                                    ? s_bbase[cnt] + ((long long)sc * s_bcnt[cnt] + off) * nhg + hg
                                    : off + it;
-          items[total_pf + xcd_position((unsigned)di, (unsigned)total_dc)] =
+          items[dec_base + xcd_position((unsigned)di, (unsigned)total_dc)] =
               make_int4(kItemDecode, base + rr, hg, sc);
         }
       }
