@@ -437,6 +437,74 @@ def test_mixed_launch_over_1024_requests():
     assert err <= 2e-2
 
 
+def _tile_keys(L, ql, k, G, rows=256):
+    """Keys tile k of a request sees: up to the causal limit of its last query row."""
+    return min(L, L - ql + min((k * rows + rows - 1) // G, ql - 1) + 1)
+
+
+@pytest.mark.parametrize("case", ["mixed", "c3"])
+def test_work_list_holds_every_item_once_longest_first(case):
+    """The mixed launch's work list, read back from the workspace (int[2] at byte 0, the
+    item count first; int4 items from byte 256: kind | split << 4 | nsplit << 16, request,
+    kv head (prefill) or head group (decode), tile or chunk).  Every prefill tile of every
+    kv head and every decode chunk appears exactly once.  With 256 tiles or more (no key
+    splitting) the list is longest first across both kinds: the tiles that see at least
+    2,048 keys by 64-key bucket, then the decode chunks in one contiguous run, then the
+    shorter tiles by bucket; the kv heads of one tile sit next to each other in head
+    order.  'mixed': 4 causal 4096-token span prefills (tiles of 64 to 4,096 keys) and 24
+    decodes over two of those spans; 'c3': 8 chunked prefills of 512 queries over 4,096
+    cached keys."""
+    torch = _torch()
+    if case == "mixed":
+        w = make_workload("x", values=False, builder="mixed", seed=63, n_chunks=4, chunk=4096,
+                          n_dec=24, per_dec=2)
+    else:
+        w = make_workload(case, values=False)
+    dw = DeviceWorkload(w, write_context=False)
+    dw.k_pool.normal_()
+    dw.v_pool.normal_()
+    dw.attention(decode=False)
+    torch.cuda.synchronize()
+    ws = dw.workspace.cpu().numpy()
+    n = int(ws[:4].view(np.int32)[0])
+    items = ws[256:256 + 16 * n].view(np.int32).reshape(n, 4)
+    G = w.hq // w.hkv
+    ql, L = w.q_lens(), w.seq_lens
+    want_pf = {(r, g, k) for r in range(w.num_reqs) if ql[r] > 1
+               for k in range(-(-int(ql[r]) * G // 256)) for g in range(w.hkv)}
+    want_dc = {(r, 0, c) for r in range(w.num_reqs) if ql[r] == 1
+               for c in range(pic.pic_decode_num_splits(int(L[r])))}
+    kind = items[:, 0] & 15
+    assert (items[:, 0] >> 4 == 0).all(), "no key-split items in launches of 256+ tiles"
+    pf = [tuple(int(v) for v in it[1:]) for it in items[kind == 0]]
+    dc = [tuple(int(v) for v in it[1:]) for it in items[kind == 1]]
+    assert len(pf) == len(set(pf)) and set(pf) == want_pf
+    assert len(dc) == len(set(dc)) and set(dc) == want_dc
+    assert len(want_pf) >= 256
+    # decode chunks: one contiguous run
+    pos = np.flatnonzero(kind == 1)
+    if len(pos):
+        assert (np.diff(pos) == 1).all()
+        d0, d1 = int(pos[0]), int(pos[-1]) + 1
+    else:
+        d0 = d1 = n
+    buckets = np.array([min(_tile_keys(int(L[r]), int(ql[r]), k, G) >> 6, 1023)
+                        if kd == 0 else -1 for kd, r, k in zip(kind, items[:, 1], items[:, 3])])
+    before, after = buckets[:d0], buckets[d1:]
+    assert (before >= 32).all() and (after < 32).all() and (after >= 0).all()
+    for part in (before, after):
+        assert (np.diff(part) <= 0).all(), "prefill tiles longest first"
+    # the kv heads of a tile: adjacent, in head order
+    for part0 in (0, d1):
+        part = items[part0:d0 if part0 == 0 else n]
+        assert len(part) % w.hkv == 0
+        grp = part.reshape(-1, w.hkv, 4)
+        assert (grp[:, :, 1] == grp[:, :1, 1]).all() and (grp[:, :, 3] == grp[:, :1, 3]).all()
+        assert (grp[:, :, 2] == np.arange(w.hkv)[None, :]).all()
+    print(f"{case}: {len(pf)} prefill items ({len(before)} before the {len(dc)} decode "
+          f"chunks, {len(after)} after)")
+
+
 def test_refused_work_list_fills_nan():
     """Metadata that break a precondition (cu_seqlens_q descending between requests, so
     the rows of requests 0, 2, 4, ... overlap) make the work list larger than the
