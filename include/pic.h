@@ -392,11 +392,18 @@ int pic_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* q_pos,
                           int max_pos, int num_blocks, int block_size, char* msg, int msg_len);
 
 /*
- * pic_decode_num_splits -- number of key chunks a request with seq_len keys
- * is split into by the attention kernels (a pure function of seq_len and
- * dtype), and pic_decode_split_len the keys per chunk (all but the last).
+ * pic_decode_num_splits -- number of key chunks S a q_len == 1 request with
+ * seq_len keys is split into by the attention kernels: round(seq_len / 512),
+ * at least 1, at most one per inner step of 32 (bf16) or 16 (fp32) keys.  A
+ * pure function of seq_len and dtype, so a request's result does not depend
+ * on its batch.  pic_decode_chunk_start gives the first key of chunk
+ * 0 <= chunk <= S (chunk S starts at seq_len; -1 outside that range): the
+ * inner steps are dealt out evenly, so chunks differ by at most one step.
+ * pic_decode_split_len gives the key slots of the longest chunk (its inner
+ * steps times 32 or 16).
  */
 int pic_decode_num_splits(int seq_len, int dtype);
+int pic_decode_chunk_start(int seq_len, int chunk, int dtype);
 int pic_decode_split_len(int seq_len, int dtype);
 
 /*

@@ -30,7 +30,8 @@ BLOCK_SIZE = 16
 EXPORTS = [
     "pic_status_string", "pic_version", "pic_rope_table", "pic_cache_write",
     "pic_attn_workspace_size", "pic_attn_decode", "pic_attn_prefill", "pic_validate_metadata",
-    "pic_decode_num_splits", "pic_decode_split_len", "pic_cache_write_rotated",
+    "pic_decode_num_splits", "pic_decode_chunk_start", "pic_decode_split_len",
+    "pic_cache_write_rotated",
     "pic_attn_decode_rotated", "pic_attn_prefill_rotated", "pic_block_hashes",
     "pic_build_block_tables", "pic_blocks_copy", "pic_sched_create", "pic_sched_destroy",
     "pic_sched_add_span", "pic_sched_add_request", "pic_sched_step", "pic_set_kernel_events",
@@ -120,6 +121,7 @@ def _load():
     lib.pic_stream_read.argtypes = [c_void, c_size, c_void, c_int, c_int, c_void, c_void]
     lib.pic_decode_num_splits.argtypes = [c_int, c_int]
     lib.pic_decode_split_len.argtypes = [c_int, c_int]
+    lib.pic_decode_chunk_start.argtypes = [c_int, c_int, c_int]
     for name in EXPORTS:
         getattr(lib, name)  # every declared symbol must resolve
     _lib = lib
@@ -645,6 +647,10 @@ def pic_decode_num_splits(seq_len: int, dtype: int = PIC_BF16) -> int:
 
 def pic_decode_split_len(seq_len: int, dtype: int = PIC_BF16) -> int:
     return int(_load().pic_decode_split_len(seq_len, dtype))
+
+
+def pic_decode_chunk_start(seq_len: int, chunk: int, dtype: int = PIC_BF16) -> int:
+    return int(_load().pic_decode_chunk_start(seq_len, chunk, dtype))
 
 
 def pic_stream_read(src, workgroups: int, sink, order=None, piece_bytes: int = 0,

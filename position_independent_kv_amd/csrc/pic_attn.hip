@@ -364,9 +364,8 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     k1 = min(min(L, min(max(st[s + 1], 0), nb) * kBlockSize), k0 + kCdcMaxKeys);
     if (k1 <= k0) return;
   } else {
-    const int chunk = split_len(L, C::KSTEP);
-    k0 = s * chunk;
-    k1 = min(L, k0 + chunk);
+    k0 = chunk_start(L, s, C::KSTEP);
+    k1 = chunk_start(L, s + 1, C::KSTEP);
   }
   const int nsteps = cdiv(k1 - k0, C::KSTEP);
 

@@ -24,17 +24,32 @@ constexpr int kstep_for(int dtype) { return dtype == 1 ? 32 : 16; }
 
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Key chunks of a request with L keys: round(L / kSplitTarget) chunks (at
-// least one), of equal length rounded up to whole inner steps, so chunks stay
-// within [0.67, 1.5] x the target.  A pure function of L: a request is split
-// the same way in any batch, so its result does not depend on the batch.
+// Key chunks of a request with L keys: S = round(L / kSplitTarget) chunks (at
+// least one, at most one per inner step), the n = cdiv(L, kstep) inner steps
+// dealt out evenly: chunk s covers steps [s n / S, (s + 1) n / S), so no chunk
+// is more than one step longer than another and all stay within about
+// [0.67, 1.5] x the target.  (Equal chunks rounded up to whole steps left a
+// short last chunk, and the mixed launch, which deals its decode chunks to the
+// XCDs chunk level by chunk level, gave all of a batch's short chunks to one
+// XCD.)  A pure function of L: a request is split the same way in any batch,
+// so its result does not depend on the batch.
 constexpr int num_chunks_target(int L) {
   return L <= 0 ? 1 : ((L + kSplitTarget / 2) / kSplitTarget > 0 ? (L + kSplitTarget / 2) / kSplitTarget : 1);
 }
-constexpr int split_len(int L, int kstep) {
-  return L <= 0 ? kstep : cdiv(cdiv(L, num_chunks_target(L)), kstep) * kstep;
+constexpr int num_splits(int L, int kstep) {
+  return L <= 0 ? 1 : (num_chunks_target(L) < cdiv(L, kstep) ? num_chunks_target(L) : cdiv(L, kstep));
 }
-constexpr int num_splits(int L, int kstep) { return L <= 0 ? 1 : cdiv(L, split_len(L, kstep)); }
+// First key of chunk s (chunk num_splits(L) starts at L).
+constexpr int chunk_start(int L, int s, int kstep) {
+  return L <= 0 ? 0
+                : ((long long)s * cdiv(L, kstep) / num_splits(L, kstep) * kstep < L
+                       ? (int)((long long)s * cdiv(L, kstep) / num_splits(L, kstep) * kstep)
+                       : L);
+}
+// Key slots of the longest chunk (whole inner steps).
+constexpr int split_len(int L, int kstep) {
+  return L <= 0 ? kstep : cdiv(cdiv(L, kstep), num_splits(L, kstep)) * kstep;
+}
 // Upper bound of num_splits over all L <= max_len, and the exact maximum:
 // num_splits(L) <= num_chunks_target(L) (chunks are at least L / target long),
 // which never decreases with L.  The decode grid is sized by it, so a batch

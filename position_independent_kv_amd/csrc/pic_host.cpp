@@ -30,6 +30,12 @@ extern "C" int pic_decode_split_len(int seq_len, int dtype) {
   return pic::split_len(seq_len, pic::kstep_for(dtype));
 }
 
+extern "C" int pic_decode_chunk_start(int seq_len, int chunk, int dtype) {
+  const int S = pic::num_splits(seq_len, pic::kstep_for(dtype));
+  if (chunk < 0 || chunk > S) return -1;
+  return pic::chunk_start(seq_len, chunk, pic::kstep_for(dtype));
+}
+
 namespace pic {
 
 int check_dtype_dims(int dtype, int head_dim, int block_size) {

@@ -28,7 +28,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = pic.library()
     names = _declared()
-    assert len(names) == 26
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(pic.EXPORTS)
@@ -74,12 +74,20 @@ def test_split_policy(dtype, kstep):
     prev = 1
     for L in list(range(1, 4000)) + [4097, 8193, 131073, 131072, 65537]:
         S = pic.pic_decode_num_splits(L, dtype)
-        c = pic.pic_decode_split_len(L, dtype)
-        assert c % kstep == 0
-        assert (S - 1) * c < L <= S * c          # every chunk non-empty, all keys covered
+        starts = [pic.pic_decode_chunk_start(L, s, dtype) for s in range(S + 1)]
+        assert starts[0] == 0 and starts[-1] == L  # all keys covered, once
+        assert pic.pic_decode_chunk_start(L, S + 1, dtype) == -1
+        assert pic.pic_decode_chunk_start(L, -1, dtype) == -1
+        assert all(x % kstep == 0 for x in starts[:-1])  # chunks start on whole steps
+        lens = np.diff(starts)
+        assert (lens > 0).all()                  # every chunk non-empty
+        steps = -(-lens // kstep)
+        assert steps.max() - steps.min() <= 1    # steps dealt out evenly
+        assert steps.max() * kstep == pic.pic_decode_split_len(L, dtype)
         bound = max(1, (L + t // 2) // t)        # round(L / target): what the grid is sized by
         assert S <= bound                        # ... so no request has more chunks
-        assert c <= t + t // 2 + kstep           # chunks stay near the target
+        assert S == min(bound, -(-L // kstep))   # ... and no fewer, unless steps run out
+        assert lens.max() <= t + t // 2 + kstep  # chunks stay near the target
         if L < 4000:
             assert bound >= prev                 # the bound never falls as L grows
             prev = bound
@@ -270,8 +278,9 @@ int main() {
   int fails = 0;
   for (int s = -6; s <= 1; ++s) if (!pic_status_string(s)) ++fails;
   for (int L = 0; L < 200000; L += 37) {
-    int S = pic_decode_num_splits(L, 1), c = pic_decode_split_len(L, 1);
-    if (L > 0 && ((S - 1) * c >= L || S * c < L)) ++fails;
+    int S = pic_decode_num_splits(L, 1);
+    if (L > 0 && (pic_decode_chunk_start(L, 0, 1) != 0 || pic_decode_chunk_start(L, S, 1) != L ||
+                  pic_decode_chunk_start(L, S - 1, 1) >= L)) ++fails;
   }
   if (pic_attn_workspace_size(1000, 100000, 200000, 64, 8, 128, 1) == 0) ++fails;
   int cu_q[3] = {0, 2, 3}, q_pos[3] = {5, 6, 9}, bt[6] = {0, 1, 0, 2, 3, 1}, sl[2] = {7, 10};

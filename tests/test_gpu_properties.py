@@ -62,8 +62,9 @@ def test_needle_every_slot_decode(dtype, d, G):
     hq = hkv * G
     B = 16
     L = 1500                                     # several decode chunks
-    c = pic.pic_decode_split_len(L, pic.PIC_F32 if dtype == "f32" else pic.PIC_BF16)
-    edges = [k * c + e for k in range(1, -(-L // c)) for e in (-1, 0, 1)]  # chunk boundaries
+    dt = pic.PIC_F32 if dtype == "f32" else pic.PIC_BF16
+    starts = [pic.pic_decode_chunk_start(L, k, dt) for k in range(1, pic.pic_decode_num_splits(L, dt))]
+    edges = [x + e for x in starts for e in (-1, 0, 1)]  # chunk boundaries
     slots = sorted(set(list(range(0, 48)) + edges + [383, 384, 385, 575, 576, 767, 768, 1023,
                                                      1024, 1100, 1311, 1312, 1498, 1499]))
     R = len(slots)
