@@ -443,7 +443,7 @@ def _tile_keys(L, ql, k, G, rows=256):
     return min(L, L - ql + min((k * rows + rows - 1) // G, ql - 1) + 1)
 
 
-@pytest.mark.parametrize("case", ["mixed", "c3"])
+@pytest.mark.parametrize("case", ["mixed", "c3", "split"])
 def test_work_list_holds_every_item_once_longest_first(case):
     """The mixed launch's work list, read back from the workspace (int[2] at byte 0, the
     item count first; int4 items from byte 256: kind | split << 4 | nsplit << 16, request,
@@ -452,13 +452,19 @@ def test_work_list_holds_every_item_once_longest_first(case):
     splitting) the list is longest first across both kinds: the tiles that see at least
     2,048 keys by 64-key bucket, then the decode chunks in one contiguous run, then the
     shorter tiles by bucket; the kv heads of one tile sit next to each other in head
-    order.  'mixed': 4 causal 4096-token span prefills (tiles of 64 to 4,096 keys) and 24
-    decodes over two of those spans; 'c3': 8 chunked prefills of 512 queries over 4,096
-    cached keys."""
+    order.  A launch with fewer tiles splits each tile's keys into chunks (one item each)
+    and keeps every prefill item ahead of the decode chunks (a split item's partial slot
+    is its list position).  'mixed': 4 causal 4096-token span prefills (tiles of 64 to
+    4,096 keys) and 24 decodes over two of those spans; 'c3': 8 chunked prefills of 512
+    queries over 4,096 cached keys; 'split': one causal 2048-token span prefill with 2 kv
+    heads (64 tiles, so 2 key chunks per tile) and 6 decodes over that span."""
     torch = _torch()
     if case == "mixed":
         w = make_workload("x", values=False, builder="mixed", seed=63, n_chunks=4, chunk=4096,
                           n_dec=24, per_dec=2)
+    elif case == "split":
+        w = make_workload("x", values=False, builder="mixed", seed=64, n_chunks=1, chunk=2048,
+                          n_dec=6, per_dec=1, hq=8, hkv=2)
     else:
         w = make_workload(case, values=False)
     dw = DeviceWorkload(w, write_context=False)
@@ -471,17 +477,28 @@ def test_work_list_holds_every_item_once_longest_first(case):
     items = ws[256:256 + 16 * n].view(np.int32).reshape(n, 4)
     G = w.hq // w.hkv
     ql, L = w.q_lens(), w.seq_lens
-    want_pf = {(r, g, k) for r in range(w.num_reqs) if ql[r] > 1
-               for k in range(-(-int(ql[r]) * G // 256)) for g in range(w.hkv)}
+    tiles = sum(-(-int(q) * G // 256) for q in ql if q > 1) * w.hkv
+    split = max(1, 256 // tiles) if tiles < 256 else 1     # chunks a long tile may take
+    nsp = [max(1, min(split, int(L[r]) // 1024)) for r in range(w.num_reqs)]
+    want_pf = {(r, g, k, sp) for r in range(w.num_reqs) if ql[r] > 1
+               for k in range(-(-int(ql[r]) * G // 256)) for g in range(w.hkv)
+               for sp in range(nsp[r])}
     want_dc = {(r, 0, c) for r in range(w.num_reqs) if ql[r] == 1
                for c in range(pic.pic_decode_num_splits(int(L[r])))}
     kind = items[:, 0] & 15
-    assert (items[:, 0] >> 4 == 0).all(), "no key-split items in launches of 256+ tiles"
-    pf = [tuple(int(v) for v in it[1:]) for it in items[kind == 0]]
+    sp_of, ns_of = (items[:, 0] >> 4) & 0xfff, (items[:, 0] >> 16) & 0xfff
+    pf = [(int(it[1]), int(it[2]), int(it[3]), int(s))
+          for it, s in zip(items[kind == 0], sp_of[kind == 0])]
     dc = [tuple(int(v) for v in it[1:]) for it in items[kind == 1]]
     assert len(pf) == len(set(pf)) and set(pf) == want_pf
     assert len(dc) == len(set(dc)) and set(dc) == want_dc
-    assert len(want_pf) >= 256
+    for it, ns in zip(items[kind == 0], ns_of[kind == 0]):
+        assert ns == (nsp[it[1]] if nsp[it[1]] > 1 else 0)
+    if case == "split":
+        assert max(nsp) > 1
+        assert (kind[:len(pf)] == 0).all(), "a splitting launch keeps prefill items first"
+        return
+    assert tiles >= 256 and max(nsp) == 1
     # decode chunks: one contiguous run
     pos = np.flatnonzero(kind == 1)
     if len(pos):
@@ -495,7 +512,7 @@ def test_work_list_holds_every_item_once_longest_first(case):
     assert (before >= 32).all() and (after < 32).all() and (after >= 0).all()
     for part in (before, after):
         assert (np.diff(part) <= 0).all(), "prefill tiles longest first"
-    # the kv heads of a tile: adjacent, in head order
+    # the kv heads of a tile: adjacent, in head order (one item per tile and head here)
     for part0 in (0, d1):
         part = items[part0:d0 if part0 == 0 else n]
         assert len(part) % w.hkv == 0
