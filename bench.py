@@ -367,7 +367,7 @@ def scheduled_trace(budget=8192, max_running=32, num_blocks=8192, reps=3):
 
 
 def ceilings(reps=20):
-    """What this machine delivers outside the path: a plain streaming read (pic_stream_read over
+    """What this GPU delivers outside the path: a plain streaming read (pic_stream_read over
     2 GiB, the best of a few grid sizes; medians of `reps`), a 2 GiB device copy (bytes read
     + written per second) and a large bf16 matrix product (torch.matmul, 8192^3)."""
     import torch
@@ -434,7 +434,7 @@ def ceilings(reps=20):
 
 
 def attention_ceiling(reps=20):
-    """The box's own dense attention at the chunked-prefill shape, for context: torch's
+    """This GPU's library dense attention at the chunked-prefill shape, for context: torch's
     scaled_dot_product_attention restricted to its flash backend (no fallback to a math
     path), bf16, 8 requests x 32 heads x 512 queries over 4608 keys (kv heads expanded
     to 32, keys already rotated: no paging, no positions), dense and with the
