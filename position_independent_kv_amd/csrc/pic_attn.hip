@@ -160,17 +160,29 @@ __device__ __forceinline__ void rotate_ops(OpT<T>* x, const float* cs, const flo
   }
 }
 
-// Same rotation with the cos/sin values read from an LDS table row, one
-// chunk at a time (cs/sn point at the lane's first pair of the row).
+// Swizzle of a decode table row (D/2 floats in 16-byte units): unit u of key
+// row r sits at u ^ tab_swz(r), even, so an 8-float run stays contiguous and
+// the rotation's reads (16 key rows per half wave, one column) spread over
+// the LDS banks.
+__device__ __forceinline__ int tab_swz(int row, int upr) {
+  return (2 * ((row & 3) | (((row >> 3) & 1) << 2))) & (upr - 1);
+}
+
+// The same rotation with the cos/sin values read from a swizzled LDS table
+// row (tab_swz), one chunk at a time: cs/sn point at row `row` of the stage.
 template <typename T, int D>
-__device__ __forceinline__ void rotate_from_lds(OpT<T>* x, const float* cs, const float* sn) {
+__device__ __forceinline__ void rotate_from_tab(OpT<T>* x, const float* cs, const float* sn,
+                                                int row, int grp) {
   using C = Cfg<T, D>;
   using M = Mma<T>;
   typedef Run<float, C::KPL> RF;
+  const int f = tab_swz(row, D / 8);
 #pragma unroll
   for (int c = 0; c < C::NH; ++c) {
-    const typename RF::V cv = RF::load(cs + c * C::KCH);
-    const typename RF::V sv = RF::load(sn + c * C::KCH);
+    const int i0 = grp * C::KPL + c * C::KCH;
+    const int off = (((i0 >> 2) ^ f) << 2) | (i0 & 3);
+    const typename RF::V cv = RF::load(cs + off);
+    const typename RF::V sv = RF::load(sn + off);
     float lo[C::KPL], hi[C::KPL];
 #pragma unroll
     for (int e = 0; e < C::KPL; ++e) {
@@ -305,23 +317,55 @@ __device__ __forceinline__ int chunks_of(const AttnArgs& a, int r, int L, int ks
   return num_splits(L, kstep);
 }
 
+// One 16-byte direct load per lane from global memory into LDS: lane i's
+// bytes land at LDS byte address lds_base + 16 i (lds_base: wave-uniform,
+// passed in M0, whose previous value the sequence restores).  Inline
+// assembly on purpose: the compiler neither counts it nor makes later LDS
+// reads wait on it (with the builtin form it may put a wait for every
+// outstanding load in front of the step's first LDS read, which serialises
+// the load pipeline), so callers wait with vm_wait_all() before the barrier
+// that publishes the stage.
+__device__ __forceinline__ void lds_direct_load16(const void* src, unsigned lds_base) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 template <typename T, int D>
 struct DecodeSmem {
   static constexpr int KSTEP = Cfg<T, D>::KSTEP;
-  static constexpr int TLD = D / 2 + 4;
-  float cs[2][KSTEP][TLD];
-  float sn[2][KSTEP][TLD];
+  static constexpr int TROW = D / 2;      // floats per table row (unpadded: direct-load runs)
+  static constexpr int UPR = TROW / 4;    // 16-byte units per row
+  static constexpr int RPC = 256 / TROW;  // rows per 1 KiB run
+  static constexpr int NCK = KSTEP / RPC; // 1 KiB runs per table and step
+  static_assert(KSTEP % RPC == 0, "whole runs per table step");
+  float cs[2][KSTEP][TROW];
+  float sn[2][KSTEP][TROW];
   int pos[kMaxChunk];
   int blk[kMaxChunk / kBlockSize + 2];
 };
 
 // One decode work item: request r, key chunk s, kv heads hg*NW .. hg*NW+NW-1
 // (one per wave of the NW-wave workgroup).  All waves walk the same keys:
-// each step's cos/sin rows are fetched once per workgroup and shared through
-// LDS, while every wave reads
-// its own head's K rows and V runs from the pools into registers.  NB steps
-// of loads are kept in flight (a ring of NB register buffers): the loads of
-// step j+NB are issued as soon as step j has consumed its buffer.  The
+// each step's cos/sin rows are fetched once per workgroup, straight into an
+// LDS table stage by direct loads (no registers), and shared; every wave
+// reads its own head's K rows and V runs from the pools into registers.  NB
+// steps of loads are kept in flight (a ring of NB register buffers): the
+// loads of step j+NB are issued as soon as step j has consumed its buffer.
+// Keeping the table out of registers puts the bf16 kernel at 159 VGPRs, so
+// three workgroups share a compute unit.  The
 // chunk's block ids and key positions are staged in LDS first, so no
 // address lookup ever waits behind the data loads.  With one chunk the wave
 // writes the output row; otherwise it writes a normalised partial and
@@ -399,29 +443,43 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   const int vblk_sel = (grp * 4 * C::NT >= kBlockSize) ? 1 : 0;
   const int vkey_off = (grp * 4 * C::NT) & 15;
 
-  // table staging: thread -> (key of the step, TPT consecutive pairs)
-  constexpr int TPT = C::KSTEP * (D / 2) / NTH;
-  static_assert(TPT >= 1, "at least one table pair per thread");
-  constexpr int TPK = (D / 2) / TPT;
-  typedef Run<float, TPT> RF;
-  const int skey = tid / TPK;
-  const int spart = (tid % TPK) * TPT;
 
   struct Group {
     Op k[C::NT][C::NC];
     Op v[C::NPV][C::ND];
-    typename RF::V c, sn;
   };
+  static_assert(!ROT || NB == 1, "one step of loads in flight: two table stages");
   Group grpbuf[NB];
 
   // Loads of step j (relative to k0) into a register group, in three parts
   // so that each part is issued as soon as the previous step has consumed
   // that part of the group: the table values right after they are copied to
   // LDS, the K rows after the score MFMAs, the V runs after the PV MFMAs.
-  auto issue_tab = [&](int j, Group& gb) {
-    const size_t row = (size_t)sm.pos[j * C::KSTEP + skey] * (D / 2) + spart;
-    gb.c = RF::load(a.cos_tab + row);
-    gb.sn = RF::load(a.sin_tab + row);
+  // The cos/sin rows of step j straight into table stage j & 1 (no
+  // registers): wave w fills 1 KiB runs w, w + NW, ... of each table.  Issued
+  // before that step's K loads: a wave's loads complete in order, so once its
+  // K registers are in, so are its table runs.
+  using SM = DecodeSmem<T, D>;
+  auto dma_tab = [&](int j) {
+    const int buf = j & 1;
+    const unsigned cbase = __builtin_amdgcn_readfirstlane(lds_address(&sm.cs[buf][0][0]));
+    const unsigned sbase = __builtin_amdgcn_readfirstlane(lds_address(&sm.sn[buf][0][0]));
+    const int w = __builtin_amdgcn_readfirstlane(wave);  // uniform: runs per wave
+    for (int ck = w; ck < SM::NCK; ck += NW) {
+      const int row = ck * SM::RPC + lane / SM::UPR;
+      const int unit = (lane % SM::UPR) ^ tab_swz(row, SM::UPR);
+      const size_t at = (size_t)sm.pos[j * C::KSTEP + row] * (D / 2) + unit * 4;
+      lds_direct_load16(a.cos_tab + at, cbase + ck * 1024u);
+      lds_direct_load16(a.sin_tab + at, sbase + ck * 1024u);
+    }
+  };
+  // wait until this wave's K registers of the current step are in (and with
+  // them its earlier table runs)
+  auto wait_k = [&](Group& gb) {
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(gb.k[t][c]));
   };
   auto issue_k = [&](int j, Group& gb) {
     const int kb = j * C::KSTEP;  // offset in the chunk
@@ -447,9 +505,9 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     }
   };
   auto issue = [&](int j, Group& gb) {
+    if constexpr (ROT) dma_tab(j);
     issue_k(j, gb);
     issue_v(j, gb);
-    if constexpr (ROT) issue_tab(j, gb);
   };
 
   f32x4 acc[C::ND];
@@ -466,9 +524,7 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     const int buf = j & 1;
     const int kb = k0 + j * C::KSTEP;  // absolute key index
     if constexpr (ROT) {
-      RF::store(&sm.cs[buf][skey][spart], gb.c);
-      RF::store(&sm.sn[buf][skey][spart], gb.sn);
-      if (j + NB < nsteps) issue_tab(j + NB, gb);
+      wait_k(gb);
       __syncthreads();
     }
     f32x4 sc[C::NT];
@@ -476,13 +532,15 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     for (int t = 0; t < C::NT; ++t) {
       const int krow = key_of<C::NT>(t, row16);
       if constexpr (ROT)
-        rotate_from_lds<T, D>(gb.k[t], &sm.cs[buf][krow][grp * C::KPL],
-                              &sm.sn[buf][krow][grp * C::KPL]);
+        rotate_from_tab<T, D>(gb.k[t], &sm.cs[buf][krow][0], &sm.sn[buf][krow][0], krow, grp);
       sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) sc[t] = M::run(gb.k[t][c], qop[c], sc[t]);
     }
-    if (j + NB < nsteps) issue_k(j + NB, gb);
+    if (j + NB < nsteps) {
+      if constexpr (ROT) dma_tab(j + NB);
+      issue_k(j + NB, gb);
+    }
 #pragma unroll
     for (int t = 0; t < C::NT; ++t)
 #pragma unroll
@@ -878,32 +936,6 @@ __device__ __forceinline__ void sched_interleave() {
 // PV operand reads (32 rows, one unit each, per half wave) and the direct
 // loads (8 rows x 8 units per 64 lanes) hit distinct LDS banks.
 __device__ __forceinline__ int vswz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
-
-// One 16-byte direct load per lane from global memory into LDS: lane i's
-// bytes land at LDS byte address lds_base + 16 i (lds_base: wave-uniform,
-// passed in M0, whose previous value the sequence restores).  Inline
-// assembly on purpose: the compiler neither counts it nor makes later LDS
-// reads wait on it (with the builtin form it may put a wait for every
-// outstanding load in front of the step's first LDS read, which serialises
-// the load pipeline), so callers wait with vm_wait_all() before the barrier
-// that publishes the stage.
-__device__ __forceinline__ void lds_direct_load16(const void* src, unsigned lds_base) {
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds_base)
-      : "memory");
-}
-__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ unsigned lds_address(const void* p) {
-  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 template <int D, int NW, int KS>
 struct Pf {
