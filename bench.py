@@ -46,16 +46,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments and whitespace removed (string literals kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            if not c.isspace():
+                out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def source_hash() -> str:
-    """Hash of the attention kernels' sources (pic_attn.hip and the headers it includes):
-    the traffic counters of the profiled kernels are only valid for this exact device
-    code.  The other kernels' files and host-only C++ do not enter."""
+    """Hash of the attention kernels' code (pic_attn.hip and the headers it includes,
+    comments and whitespace removed): the traffic counters of the profiled kernels are only
+    valid for this device code.  The other kernels' files and host-only C++ do not enter."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "position_independent_kv_amd", "csrc")
     for name in ["pic_attn.hip", "pic_common.hpp", "pic_device.hpp", "pic_host.hpp"]:
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

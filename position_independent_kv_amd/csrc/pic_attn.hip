@@ -27,8 +27,9 @@
 //   waves per (request, key chunk of about 512 keys, four kv heads), one wave
 //   per kv head, the G query heads of the kv head as the columns of a
 //   16x16x32 tile.  The chunk's block ids and positions, and each 32-key
-//   step's cos/sin rows, are staged in LDS once per workgroup; every wave
-//   loads its own head's K rows and V runs into registers.  A request split
+//   step's cos/sin rows (by direct global-to-LDS loads), are staged in LDS
+//   once per workgroup; every wave loads its own head's K rows and V runs
+//   into registers.  A request split
 //   into several chunks writes normalised partials and (max, sum) to the
 //   workspace; combine_kernel merges them.
 // - plan_kernel + mixed_kernel (any mix of q_len): the planner turns
@@ -36,8 +37,8 @@
 //   chunks, and one mixed_kernel launch runs both kinds.  A bf16 prefill tile
 //   is one workgroup of eight waves per (request, kv head, 256 query rows:
 //   (token, group head) pairs, 32 per wave) on 32x32x16 MFMAs; each 64-key
-//   step is gathered from the pool once per workgroup, rotated on its way
-//   into LDS and shared by the eight waves.  Its softmax exponentiates
+//   step is gathered from the pool once per workgroup, K rotated on its way
+//   into LDS and V^T loaded straight into LDS, and shared by the eight waves.  Its softmax exponentiates
 //   against a fixed per-row reference and redoes the tile with the exact row
 //   maximum in the rare case a later score overflows that reference.  A
 //   launch with few tiles splits long tiles into key chunks, merged by
@@ -451,10 +452,10 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   static_assert(!ROT || NB == 1, "one step of loads in flight: two table stages");
   Group grpbuf[NB];
 
-  // Loads of step j (relative to k0) into a register group, in three parts
-  // so that each part is issued as soon as the previous step has consumed
-  // that part of the group: the table values right after they are copied to
-  // LDS, the K rows after the score MFMAs, the V runs after the PV MFMAs.
+  // Loads of step j (relative to k0) into a register group, in two parts so
+  // that each is issued as soon as the previous step has consumed that part
+  // of the group: the K rows after the score MFMAs, the V runs after the PV
+  // MFMAs.
   // The cos/sin rows of step j straight into table stage j & 1 (no
   // registers): wave w fills 1 KiB runs w, w + NW, ... of each table.  Issued
   // before that step's K loads: a wave's loads complete in order, so once its
