@@ -702,6 +702,12 @@ def main():
     main_res = time_config(args.config, args.steps, args.warmup, with_rows=True,
                            only_timed=args.only_main)
     w, counts = main_res["w"], main_res["counts"]
+    if not args.only_main:
+        m = main_res
+        log(f"[bench] {args.config}: timed steps: kernel {m['kernel_ms'] * 1e3:.1f} us (cold); "
+            f"call loop: kernel {m['call_kernel_ms'] * 1e3:.1f} us within call "
+            f"{m['call_ms'] * 1e3:.1f} us, call without events {m['call_unhooked_ms'] * 1e3:.1f} us; "
+            f"warm kernel {m['warm_kernel_ms'] * 1e3:.1f} us")
     decode = w.kind == "decode"
     kernel = "decode_kernel" if decode else "mixed_kernel"
     if decode:
@@ -778,8 +784,10 @@ def main():
             "unique_kv_bytes": c["unique_kv_bytes"], "algorithmic_bytes": c["bytes"],
             "flops": c["flops"],
         }
-        log(f"[bench] {name}: kernel {r['kernel_ms'] * 1e3:.1f} us cold / "
-            f"{r['warm_kernel_ms'] * 1e3:.1f} us warm, call {r['call_unhooked_ms'] * 1e3:.1f} us; "
+        log(f"[bench] {name}: timed steps: kernel {r['kernel_ms'] * 1e3:.1f} us (cold); "
+            f"call loop: kernel {r['call_kernel_ms'] * 1e3:.1f} us within call "
+            f"{r['call_ms'] * 1e3:.1f} us, call without events {r['call_unhooked_ms'] * 1e3:.1f} us; "
+            f"warm kernel {r['warm_kernel_ms'] * 1e3:.1f} us; "
             f"{others[name]['kernel_GBps']:.0f} GB/s, {others[name]['kernel_TFLOPs']:.1f} TFLOP/s")
         if not args.no_cpu_baseline:
             t = time.time()
