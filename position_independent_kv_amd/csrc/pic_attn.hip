@@ -909,7 +909,7 @@ __device__ void prefill_tile(const AttnArgs& a, int r, int g, int tile, unsigned
 // ---------------------------------------------------------------------------
 
 // Scheduling groups (mask bits of __builtin_amdgcn_sched_group_barrier).
-constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgDsWrite = 0x200;
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
 
 // Eight MFMAs, each followed by R LDS reads and V vector instructions.
 template <int R, int V>
