@@ -38,9 +38,10 @@
 //   is one workgroup of eight waves per (request, kv head, 256 query rows:
 //   (token, group head) pairs, 32 per wave) on 32x32x16 MFMAs; each 64-key
 //   step is gathered from the pool once per workgroup, K rotated on its way
-//   into LDS and V^T loaded straight into LDS, and shared by the eight waves.  Its softmax exponentiates
-//   against a fixed per-row reference and redoes the tile with the exact row
-//   maximum in the rare case a later score overflows that reference.  A
+//   into LDS and V^T loaded straight into LDS, and shared by the eight
+//   waves.  Its softmax exponentiates against a fixed per-row reference and
+//   redoes the tile with the exact row maximum in the rare case a later
+//   score overflows that reference.  A
 //   launch with few tiles splits long tiles into key chunks, merged by
 //   combine_kernel.  fp32 tiles use four waves, 128 rows and an online
 //   softmax.
