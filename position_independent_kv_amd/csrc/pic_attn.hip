@@ -654,11 +654,13 @@ __device__ void fill_nan_rows(const AttnArgs& a, int r, int g) {
   }
 }
 
-// Blocks [0, dec_blocks): one per (request, kv head), merging the chunks of
-// q_len == 1 requests (or, after a refused work list, filling the request's
-// rows with NaN); blocks beyond: one per split prefill tile.
+// Blocks [0, dec_blocks): dsplit per (request, kv head), each merging the
+// chunks of a q_len == 1 request for one slice of d (or, after a refused
+// work list, the first filling the request's rows with NaN); blocks beyond:
+// one per split prefill tile.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a, int dec_blocks) {
+__global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a, int dec_blocks,
+                                                           int dsplit) {
   constexpr int EPT = 8;
   __shared__ __attribute__((aligned(16))) float gm[kThreads * EPT];
   __shared__ float2 gml[kThreads];
@@ -667,10 +669,11 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a, int dec_b
     if constexpr (sizeof(T) == 2) merge_prefill_tile<T, D>(a, (int)blockIdx.x - dec_blocks);
     return;
   }
-  const int r = blockIdx.x / a.hkv;
-  const int g = blockIdx.x % a.hkv;
+  const int rg = (int)blockIdx.x / dsplit, ds = (int)blockIdx.x % dsplit;
+  const int r = rg / a.hkv;
+  const int g = rg % a.hkv;
   if (a.cu_q && a.nitems[1]) {  // the planner ran nothing (work list overflow)
-    fill_nan_rows<T, D>(a, r, g);
+    if (ds == 0) fill_nan_rows<T, D>(a, r, g);
     return;
   }
   if (a.cu_q && a.cu_q[r + 1] - a.cu_q[r] != 1) return;
@@ -679,12 +682,13 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a, int dec_b
   const int S = chunks_of(a, r, L, Cfg<T, D>::KSTEP);
   if (L <= 0 || S <= 1) return;
   const int G = a.group;
-  const int pairs = G * (D / EPT);
+  const int DE = D / EPT / dsplit;  // EPT-wide d pieces of this block's slice
+  const int pairs = G * DE;
   const int SG = max(1, kThreads / pairs);
   const int sg = tid / pairs;
   const int pc = tid % pairs;
-  const int col = pc / (D / EPT);
-  const int d0 = (pc % (D / EPT)) * EPT;
+  const int col = pc / DE;
+  const int d0 = (ds * DE + pc % DE) * EPT;
   const size_t pbase = ((size_t)r * a.hkv + g) * a.s_max;
   float pm = -INFINITY, pl = 0.0f;
   float po[EPT];
@@ -2117,16 +2121,21 @@ static AttnArgs make_args(const AttnHostArgs& h, const WorkspaceLayout& w) {
   return a;
 }
 
-// all_reqs: one block per (request, kv head) even when no request can have
+// all_reqs: blocks for every (request, kv head) even when no request can have
 // several chunks (the mixed launch: those blocks also report a refused work
-// list).
+// list).  A batch of few (request, kv head) pairs splits each merge over
+// slices of d so that about 256 blocks share the work (4 x 131k-key decodes:
+// 32 pairs of 256 chunks each: the merge 16.4 -> 11.6 us).
 template <typename T, int D>
 static void launch_combine(const AttnArgs& a, hipStream_t s, bool all_reqs,
                            int split_blocks = 0) {
-  const int dec_blocks = all_reqs || a.s_max > 1 ? a.num_reqs * a.hkv : 0;
+  const int rh = all_reqs || a.s_max > 1 ? a.num_reqs * a.hkv : 0;
+  int dsplit = 1;
+  while (a.s_max > 1 && dsplit < D / 8 && (long long)rh * dsplit < 256) dsplit *= 2;
+  const int dec_blocks = rh * dsplit;
   if (dec_blocks + split_blocks > 0)
     hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)(dec_blocks + split_blocks)),
-                       dim3(kThreads), 0, s, a, dec_blocks);
+                       dim3(kThreads), 0, s, a, dec_blocks, dsplit);
 }
 
 template <typename T, int D, bool ROT>
