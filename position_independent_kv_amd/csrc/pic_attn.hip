@@ -1464,6 +1464,31 @@ __device__ __forceinline__ unsigned xcd_position(unsigned l, unsigned n) {
   }
   return k * 8 + x;
 }
+// xcd_position for one list length n, its two divisions by the per-XCD
+// quotient done by multiplication: for a divisor d >= 1 and
+// m = floor((2^32 - 1) / d), umulhi(l, m) is floor(l / d) or one less for
+// every l < 2^32, and one compare fixes it.
+struct XcdMap {
+  unsigned q, rem, m1, m0;  // n / 8, n % 8, multipliers for q + 1 and q
+  __device__ explicit XcdMap(unsigned n)
+      : q(n / 8), rem(n % 8), m1(0xffffffffu / (n / 8 + 1)), m0(n >= 8 ? 0xffffffffu / (n / 8) : 0u) {}
+  __device__ static unsigned div(unsigned l, unsigned d, unsigned m, unsigned& r) {
+    unsigned x = __umulhi(l, m);
+    r = l - x * d;
+    if (r >= d) {
+      ++x;
+      r -= d;
+    }
+    return x;
+  }
+  __device__ unsigned position(unsigned l) const {
+    const unsigned head = rem * (q + 1);
+    unsigned x, k;
+    if (l < head) x = div(l, q + 1, m1, k);
+    else x = rem + div(l - head, q, m0, k);  // q >= 1 here: l < n
+    return k * 8 + x;
+  }
+};
 
 // Keys of a prefill tile that takes about as long as one decode chunk of the
 // mixed launch (8 kv heads, about kSplitTarget keys): measured 61 us per
@@ -1476,9 +1501,11 @@ constexpr int kDecodeTileKeys = 4 * kSplitTarget;
 __device__ __forceinline__ int len_bucket(int L) { return min(max(L, 0) >> 6, 1023); }
 // Keys tile k of a request (q_len ql, seq_len L) sees: the slots up to the
 // causal limit of its last query row (rows query rows per tile, group heads
-// per token), as the tile kernels bound their key loop.
+// per token), as the tile kernels bound their key loop.  k * rows is below
+// ql * group < 2^31, so the row index fits 32 unsigned bits.
 __device__ __forceinline__ int tile_keys(int L, int ql, int k, int rows, int group) {
-  const int last_tok = min((int)(((long long)k * rows + rows - 1) / group), ql - 1);
+  const int last_tok =
+      min((int)(((unsigned)k * (unsigned)rows + (unsigned)rows - 1u) / (unsigned)group), ql - 1);
   return min(L, L - ql + last_tok + 1);
 }
 
@@ -1844,44 +1871,73 @@ __global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
 // a few chunk levels' table rows in its L2.  (Ranks inside a group are taken
 // with LDS atomics, so the dispatch order of equal-length requests may vary
 // between calls; no result depends on it.)
+// One step of a 64-bit inclusive scan across a wave by DPP: each lane adds
+// the value of the lane CTRL selects (nothing where CTRL selects no lane, or
+// where the lane's row of 16 is outside ROW_MASK).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ long long dpp_scan_step(long long x) {
+  const unsigned long long u = (unsigned long long)x;
+  const unsigned lo =
+      (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROW_MASK, 0xf, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL,
+                                                            ROW_MASK, 0xf, false);
+  return (long long)(u + (((unsigned long long)hi << 32) | lo));
+}
+// Inclusive scan across the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// lanes inside each row of 16, then the last lane of rows 0 and 2 added to
+// rows 1 and 3, then lane 31 added to rows 2 and 3.  (Shuffles through
+// ds_bpermute made the planner's scans half of its time.)
+__device__ __forceinline__ long long wave_scan(long long x) {
+  x = dpp_scan_step<0x111, 0xf>(x);  // row_shr:1
+  x = dpp_scan_step<0x112, 0xf>(x);  // row_shr:2
+  x = dpp_scan_step<0x114, 0xf>(x);  // row_shr:4
+  x = dpp_scan_step<0x118, 0xf>(x);  // row_shr:8
+  x = dpp_scan_step<0x142, 0xa>(x);  // row_bcast:15, rows 1 and 3
+  x = dpp_scan_step<0x143, 0xc>(x);  // row_bcast:31, rows 2 and 3
+  return x;
+}
+// Lane l's 64-bit value, l uniform across the wave.
+__device__ __forceinline__ long long read_lane64(long long x, int l) {
+  const unsigned long long u = (unsigned long long)x;
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), l);
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 // Inclusive scans of NV values per thread across the 1024-thread planner
-// workgroup: a shuffle scan inside each wave, then one over the 16 wave
-// totals; two barriers.  s_w: [16][NV] scratch.  Returns each thread's
-// inclusive prefix; tot gets the workgroup totals.
+// workgroup: a DPP scan inside each wave; then in every wave lane l reads
+// wave l's total (l < 16, repeated in each row of 16 lanes), a DPP scan
+// inside the row sums them, and the wave takes the sum before it and the
+// grand total from two lanes.  One barrier.  (Every lane reading all 16
+// totals instead cost 1.7 us of LDS return bandwidth.)  s_w: [16][NV]
+// scratch, which the caller may write again only after its next barrier.
+// Returns each thread's inclusive prefix; tot gets the workgroup totals.
+// Called by every thread of the workgroup.
 template <int NV>
 __device__ __forceinline__ void plan_scan(long long (&x)[NV], long long (*s_w)[NV],
                                           long long (&tot)[NV]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int v = 0; v < NV; ++v)
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const long long y = __shfl_up(x[v], o);
-      if (lane >= o) x[v] += y;
-    }
+  for (int v = 0; v < NV; ++v) x[v] = wave_scan(x[v]);
   if (lane == 63)
 #pragma unroll
     for (int v = 0; v < NV; ++v) s_w[wave][v] = x[v];
   __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      long long w = lane < 16 ? s_w[lane][v] : 0;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const long long y = __shfl_up(w, o);
-        if (lane >= o) w += y;
-      }
-      if (lane < 16) s_w[lane][v] = w;
-    }
-  }
-  __syncthreads();
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    if (wave > 0) x[v] += s_w[wave - 1][v];
-    tot[v] = s_w[15][v];
+    long long t = s_w[lane & 15][v];
+    t = dpp_scan_step<0x111, 0xf>(t);
+    t = dpp_scan_step<0x112, 0xf>(t);
+    t = dpp_scan_step<0x114, 0xf>(t);
+    t = dpp_scan_step<0x118, 0xf>(t);
+    if (wv > 0) x[v] += read_lane64(t, wv - 1);
+    tot[v] = read_lane64(t, 15);
   }
 }
+
+// Request kinds in the planner's per-request record.
+constexpr int kPlanNone = 0, kPlanPrefill = 1, kPlanDecode = 2;
 
 __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ cu_q,
                                                     const int32_t* __restrict__ seq_lens,
@@ -1892,22 +1948,23 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
                                                     int* __restrict__ count,
                                                     int4* __restrict__ pf_tiles,
                                                     int* __restrict__ pf_count) {
-  __shared__ long long s_w4[16][4];
+  __shared__ long long s_w2[16][2];
   __shared__ long long s_wt[16][1];
-  __shared__ int s_nsp[1024];          // key chunks per tile of each request (1: not split)
+  __shared__ long long s_w1[16][1];
+  // per request of the current chunk of 1024: {kind, then for a prefill
+  // request its tiles, seq_len and q_len; for a decode request its chunks,
+  // the logical decode index of its chunk 0 (head group 0), and the index
+  // step from one chunk to the next}
+  __shared__ int4 s_meta[1024];
   __shared__ int s_pfn;                // split tiles listed so far
-  __shared__ long long s_w1[2][16][1];
-  __shared__ long long s_off[1024];
-  __shared__ int s_cnt[1024];
-  __shared__ unsigned char s_kind[1024];
   __shared__ int s_bcnt[1024];         // decode requests per chunk count S
   __shared__ int s_brank[1024];        // ranks handed out so far per S
   __shared__ long long s_bbase[1024];  // first decode-list index of group S
   __shared__ int s_bover;              // some request has 1024 or more chunks
-  __shared__ int s_ptot[1024];         // prefill tiles per context-length bucket
+  __shared__ unsigned long long s_dcover;  // decode items of those requests
+  __shared__ unsigned long long s_ptot[1024];  // prefill items per context-length bucket
   __shared__ int s_prank[1024];        // prefill tiles placed so far per bucket
   __shared__ long long s_pbase[1024];  // first prefill-list index of each bucket
-  __shared__ int s_ql[1024], s_len[1024];  // q_len, seq_len of the chunk's requests
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   s_bcnt[tid] = 0;
@@ -1916,11 +1973,25 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   s_prank[tid] = 0;
   if (tid == 0) {
     s_bover = 0;
+    s_dcover = 0;
     s_pfn = 0;
   }
+  // q_len and (capped) seq_len of request base + tid; the first chunk's stay
+  // in registers for the later passes
+  auto load = [&](int base, int& ql, int& L) {
+    const int r = base + tid;
+    ql = 0;
+    L = 0;
+    if (r < num_reqs) {
+      ql = cu_q[r + 1] - cu_q[r];
+      L = min(seq_lens[r], len_cap);
+    }
+  };
+  int ql0, L0;
+  load(0, ql0, L0);
   // pass 1a: prefill tiles before splitting; they decide the split
-  long long tl[1] = {0};
-  for (int r = tid; r < num_reqs; r += 1024) {
+  long long tl[1] = {ql0 > 1 ? (long long)hkv * cdiv(ql0 * group, rows) : 0};
+  for (int r = tid + 1024; r < num_reqs; r += 1024) {
     const int ql = cu_q[r + 1] - cu_q[r];
     if (ql > 1) tl[0] += (long long)hkv * cdiv(ql * group, rows);
   }
@@ -1932,57 +2003,54 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
   auto nsplit_of = [&](int L) {
     return split_max > 1 ? max(1, min(split_max, L / kPrefillChunkMin)) : 1;
   };
-  // pass 1b, per chunk of 1024 requests: item totals, decode requests per
-  // chunk count; then prefill items per key-count bucket, the waves taking
-  // the chunk's requests in turn and their lanes the request's tiles
-  long long pf = 0, dc = 0;
+  // pass 1b, per chunk of 1024 requests: decode requests per chunk count;
+  // then prefill items per key-count bucket, the waves taking the chunk's
+  // requests in turn and their lanes the request's tiles
   for (int base = 0; base < num_reqs; base += 1024) {
-    const int r = base + tid;
-    int ql = 0, L = 0;
-    if (r < num_reqs) {
-      ql = cu_q[r + 1] - cu_q[r];
-      L = min(seq_lens[r], len_cap);
-      if (ql > 1) {
-        pf += (long long)hkv * cdiv(ql * group, rows) * nsplit_of(L);
-      } else if (ql == 1) {
-        const int S = num_splits(L, kstep);
-        dc += (long long)nhg * S;
-        if (S < 1024) atomicAdd(&s_bcnt[S], 1);
-        else s_bover = 1;
+    int ql = ql0, L = L0;
+    if (base > 0) load(base, ql, L);
+    if (ql == 1) {
+      const int S = num_splits(L, kstep);
+      if (S < 1024) {
+        atomicAdd(&s_bcnt[S], 1);
+      } else {
+        s_bover = 1;
+        atomicAdd(&s_dcover, (unsigned long long)nhg * S);
       }
     }
-    s_ql[tid] = ql;
-    s_len[tid] = L;
+    s_meta[tid] = make_int4(ql > 1 ? kPlanPrefill : kPlanNone, cdiv(max(ql, 0) * group, rows), L,
+                            ql);
     __syncthreads();
     const int nr = min(1024, num_reqs - base);
     for (int rr = wave; rr < nr; rr += 16) {
-      const int qr = s_ql[rr], Lr = s_len[rr];
-      if (qr <= 1) continue;
-      const int n = hkv * nsplit_of(Lr);
-      for (int k = lane; k < cdiv(qr * group, rows); k += 64)
-        atomicAdd(&s_ptot[len_bucket(tile_keys(Lr, qr, k, rows, group))], n);
+      const int4 m = s_meta[rr];
+      if (m.x != kPlanPrefill) continue;
+      const unsigned long long n = (unsigned long long)(hkv * nsplit_of(m.z));
+      for (int k = lane; k < m.y; k += 64)
+        atomicAdd(&s_ptot[len_bucket(tile_keys(m.z, m.w, k, rows, group))], n);
     }
     __syncthreads();
   }
-  // totals, and the group / bucket bases (longest first: exclusive suffix
-  // sums, total minus the inclusive prefix): thread b holds bucket b
-  long long x[4] = {pf, dc, (long long)s_bcnt[tid] * tid * nhg, (long long)s_ptot[tid]};
-  long long tot[4];
-  plan_scan<4>(x, s_w4, tot);
-  const long long total_pf = tot[0];
-  const long long total_dc = tot[1];
+  // the group / bucket bases (longest first: exclusive suffix sums, total
+  // minus the inclusive prefix; thread b holds group or bucket b) and the
+  // item totals
+  long long x[2] = {(long long)s_bcnt[tid] * tid * nhg, (long long)s_ptot[tid]};
+  long long tot[2];
+  plan_scan<2>(x, s_w2, tot);
+  const long long total_pf = tot[1];
+  const long long total_dc = tot[0] + (long long)s_dcover;
   const long long total = total_pf + total_dc;
-  s_bbase[tid] = tot[2] - x[2];
-  s_pbase[tid] = tot[3] - x[3];
+  s_bbase[tid] = tot[0] - x[0];
+  s_pbase[tid] = tot[1] - x[1];
   const bool chunk_major = s_bover == 0;
   // the decode items start after the prefill items of buckets bd and above
-  // (s_pbase[bd - 1] of them); the buckets below move behind the decode items
+  // (s_pbase[bd - 1] of them); the buckets below sit behind the decode items
+  // (their bases move by low_shift at use)
   constexpr int bd = kDecodeTileKeys / 64;
   static_assert(bd >= 1 && bd < 1024, "decode items sit between two buckets");
   __syncthreads();
   const long long dec_base = split_max > 1 ? total_pf : s_pbase[bd - 1];
-  __syncthreads();
-  if (split_max == 1 && tid < bd) s_pbase[tid] += total_dc;
+  const long long low_shift = split_max > 1 ? 0 : total_dc;
   // More items than the workspace was sized for means the metadata broke a
   // precondition (cu_seqlens_q not ascending, or total_q / max_seq_len too
   // small): run nothing, and raise the flag that makes the merge launch fill
@@ -1999,65 +2067,61 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
     count[0] = (int)total;
     count[1] = 0;
   }
-  // pass 2, per chunk of 1024 requests: decode offsets (request order, when
-  // not chunk-major) by a scan, prefill and chunk-major ranks by LDS
-  // atomics; then the waves take the chunk's requests in turn and their
-  // lanes split each request's items
+  // (From here on every decode index is below total_dc <= max_items < 2^31.)
+  const XcdMap dec_map((unsigned)total_dc);
+  // pass 2, per chunk of 1024 requests: decode offsets (chunk-major: rank in
+  // the request's group by LDS atomics; else request order, by a scan),
+  // prefill ranks by LDS atomics; then the waves take the chunk's requests
+  // in turn and their lanes split each request's items
   long long dc_base = 0;
   for (int base = 0; base < num_reqs; base += 1024) {
-    const int r = base + tid;
-    int ql = 0, L = 0;
-    long long ndc = 0;
-    if (r < num_reqs) {
-      ql = cu_q[r + 1] - cu_q[r];
-      L = min(seq_lens[r], len_cap);
-      if (ql == 1) ndc = (long long)nhg * num_splits(L, kstep);
-    }
-    long long y[1] = {ndc};
-    long long ytot[1];
-    plan_scan<1>(y, s_w1[(base >> 10) & 1], ytot);
-    s_kind[tid] = ql > 1 ? 1 : (ql == 1 ? 2 : 0);
-    s_cnt[tid] = ql > 1 ? cdiv(ql * group, rows) : (ql == 1 ? num_splits(L, kstep) : 0);
-    s_nsp[tid] = ql > 1 ? nsplit_of(L) : 1;
-    s_ql[tid] = ql;
-    s_len[tid] = L;
-    if (ql == 1) {
-      s_off[tid] = chunk_major ? (long long)atomicAdd(&s_brank[s_cnt[tid]], 1)
-                               : dc_base + y[0] - ndc;
+    int ql = ql0, L = L0;
+    if (base > 0) load(base, ql, L);
+    const int S = ql == 1 ? num_splits(L, kstep) : 0;
+    int4 m = make_int4(kPlanNone, 0, 0, 0);
+    if (chunk_major) {
+      // item of chunk sc, head group hg: s_bbase[S] + (sc * s_bcnt[S] + rank) * nhg + hg
+      if (ql == 1) {
+        const int rank = atomicAdd(&s_brank[S], 1);
+        m = make_int4(kPlanDecode, S, (int)(s_bbase[S] + (long long)rank * nhg), s_bcnt[S] * nhg);
+      }
     } else {
-      s_off[tid] = 0;
+      // request order: the request's items follow those of the requests before it
+      long long y[1] = {ql == 1 ? (long long)nhg * S : 0};
+      long long ytot[1];
+      plan_scan<1>(y, s_w1, ytot);
+      if (ql == 1) m = make_int4(kPlanDecode, S, (int)(dc_base + y[0] - (long long)nhg * S), nhg);
+      dc_base += ytot[0];
     }
-    dc_base += ytot[0];
+    if (ql > 1) m = make_int4(kPlanPrefill, cdiv(ql * group, rows), L, ql);
+    s_meta[tid] = m;
     __syncthreads();
     const int nr = min(1024, num_reqs - base);
     for (int rr = wave; rr < nr; rr += 16) {
-      const int kind = s_kind[rr];
-      const int cnt = s_cnt[rr];
-      const long long off = s_off[rr];
-      if (kind == 1) {  // prefill tiles: each at a place in its bucket, kv heads, then chunks
-        const int S = s_nsp[rr];
-        const int n = hkv * S;
-        for (int k = lane; k < cnt; k += 64) {
-          const int b = len_bucket(tile_keys(s_len[rr], s_ql[rr], k, rows, group));
-          const long long o = s_pbase[b] + atomicAdd(&s_prank[b], n);
-          for (int j = 0; j < n; ++j) {
-            const int sp = j % S, g = j / S;
-            items[o + j] = make_int4(item_code(kItemPrefill, S > 1 ? sp : 0, S > 1 ? S : 0),
-                                     base + rr, g, k);
-            if (S > 1 && sp == 0) {
+      m = s_meta[rr];
+      if (m.x == kPlanPrefill) {  // tiles: each at a place in its bucket, kv heads, then chunks
+        const int ns = nsplit_of(m.z);
+        const int n = hkv * ns;
+        const int code0 = item_code(kItemPrefill, 0, ns > 1 ? ns : 0);
+        for (int k = lane; k < m.y; k += 64) {
+          const int b = len_bucket(tile_keys(m.z, m.w, k, rows, group));
+          long long o = s_pbase[b] + (b < bd ? low_shift : 0) + atomicAdd(&s_prank[b], n);
+          for (int g = 0; g < hkv; ++g) {
+            if (ns > 1) {
               const int slot = atomicAdd(&s_pfn, 1);
-              if (slot < kSplitCUs / 2) pf_tiles[slot] = make_int4(base + rr, g, k, (int)(o + j));
+              if (slot < kSplitCUs / 2) pf_tiles[slot] = make_int4(base + rr, g, k, (int)o);
             }
+            for (int sp = 0; sp < ns; ++sp, ++o)
+              items[o] = make_int4(ns > 1 ? item_code(kItemPrefill, sp, ns) : code0, base + rr,
+                                   g, k);
           }
         }
-      } else if (kind == 2) {  // decode chunks, per chunk the kv-head groups
-        for (int it = lane; it < cnt * nhg; it += 64) {
-          const int sc = it / nhg, hg = it % nhg;
-          const long long di = chunk_major
-                                   ? s_bbase[cnt] + ((long long)sc * s_bcnt[cnt] + off) * nhg + hg
-                                   : off + it;
-          items[dec_base + xcd_position((unsigned)di, (unsigned)total_dc)] =
-              make_int4(kItemDecode, base + rr, hg, sc);
+      } else if (m.x == kPlanDecode) {  // chunks, per chunk the kv-head groups
+        for (int sc = lane; sc < m.y; sc += 64) {
+          const unsigned di0 = (unsigned)m.z + (unsigned)sc * (unsigned)m.w;
+          for (int hg = 0; hg < nhg; ++hg)
+            items[dec_base + dec_map.position(di0 + hg)] =
+                make_int4(kItemDecode, base + rr, hg, sc);
         }
       }
     }

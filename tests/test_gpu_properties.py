@@ -443,7 +443,7 @@ def _tile_keys(L, ql, k, G, rows=256):
     return min(L, L - ql + min((k * rows + rows - 1) // G, ql - 1) + 1)
 
 
-@pytest.mark.parametrize("case", ["mixed", "c3", "split"])
+@pytest.mark.parametrize("case", ["mixed", "c3", "split", "many"])
 def test_work_list_holds_every_item_once_longest_first(case):
     """The mixed launch's work list, read back from the workspace (int[2] at byte 0, the
     item count first; int4 items from byte 256: kind | split << 4 | nsplit << 16, request,
@@ -457,7 +457,13 @@ def test_work_list_holds_every_item_once_longest_first(case):
     is its list position).  'mixed': 4 causal 4096-token span prefills (tiles of 64 to
     4,096 keys) and 24 decodes over two of those spans; 'c3': 8 chunked prefills of 512
     queries over 4,096 cached keys; 'split': one causal 2048-token span prefill with 2 kv
-    heads (64 tiles, so 2 key chunks per tile) and 6 decodes over that span."""
+    heads (64 tiles, so 2 key chunks per tile) and 6 decodes over that span; 'many': 4
+    causal 2048-token span prefills and 1,100 decodes cut to seeded lengths of 1 to 4,097
+    keys (1 to 8 chunks), so the planner takes its requests in two passes of 1024 and
+    every wave holds requests of both kinds.  The decode run, its interleave over the
+    XCDs undone (dispatch position p holds logical item x * q + min(x, rem) + k for
+    x = p % 8, k = p // 8, where q, rem = divmod(chunks, 8)), lists the requests with more
+    chunks first, and inside one chunk count all requests' chunk 0, then chunk 1, ..."""
     torch = _torch()
     if case == "mixed":
         w = make_workload("x", values=False, builder="mixed", seed=63, n_chunks=4, chunk=4096,
@@ -465,6 +471,12 @@ def test_work_list_holds_every_item_once_longest_first(case):
     elif case == "split":
         w = make_workload("x", values=False, builder="mixed", seed=64, n_chunks=1, chunk=2048,
                           n_dec=6, per_dec=1, hq=8, hkv=2)
+    elif case == "many":
+        w = make_workload("x", values=False, builder="mixed", seed=65, n_chunks=4, chunk=2048,
+                          n_dec=1100, per_dec=2)
+        dec = w.q_lens() == 1
+        w.seq_lens[dec] = np.random.default_rng(65).integers(1, int(w.seq_lens.max()) + 1,
+                                                             int(dec.sum()))
     else:
         w = make_workload(case, values=False)
     dw = DeviceWorkload(w, write_context=False)
@@ -519,8 +531,21 @@ def test_work_list_holds_every_item_once_longest_first(case):
         grp = part.reshape(-1, w.hkv, 4)
         assert (grp[:, :, 1] == grp[:, :1, 1]).all() and (grp[:, :, 3] == grp[:, :1, 3]).all()
         assert (grp[:, :, 2] == np.arange(w.hkv)[None, :]).all()
+    # decode run in logical order: chunk count non-increasing; inside one count, chunk
+    # index non-decreasing
+    nd = d1 - d0
+    q8, rem = divmod(nd, 8)
+    p = np.arange(nd)
+    logical = (p % 8) * q8 + np.minimum(p % 8, rem) + p // 8
+    assert (np.sort(logical) == p).all()
+    run = np.empty((nd, 2), np.int64)
+    run[logical, 0] = [pic.pic_decode_num_splits(int(L[r])) for r in items[d0:d1, 1]]
+    run[logical, 1] = items[d0:d1, 3]
+    assert (np.diff(run[:, 0]) <= 0).all(), "requests with more chunks first"
+    same = np.diff(run[:, 0]) == 0
+    assert (np.diff(run[:, 1])[same] >= 0).all(), "chunk-major inside one chunk count"
     print(f"{case}: {len(pf)} prefill items ({len(before)} before the {len(dc)} decode "
-          f"chunks, {len(after)} after)")
+          f"chunks in {len(set(run[:, 0].tolist()))} chunk counts, {len(after)} after)")
 
 
 def test_refused_work_list_fills_nan():
