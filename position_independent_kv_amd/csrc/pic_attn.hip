@@ -345,16 +345,17 @@ __device__ __forceinline__ unsigned lds_address(const void* p) {
   return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <typename T, int D>
+template <typename T, int D, int NTAB = 2>
 struct DecodeSmem {
+  static constexpr int NTS = NTAB;        // table stages: steps in flight + 1
   static constexpr int KSTEP = Cfg<T, D>::KSTEP;
   static constexpr int TROW = D / 2;      // floats per table row (unpadded: direct-load runs)
   static constexpr int UPR = TROW / 4;    // 16-byte units per row
   static constexpr int RPC = 256 / TROW;  // rows per 1 KiB run
   static constexpr int NCK = KSTEP / RPC; // 1 KiB runs per table and step
   static_assert(KSTEP % RPC == 0, "whole runs per table step");
-  float cs[2][KSTEP][TROW];
-  float sn[2][KSTEP][TROW];
+  float cs[NTS][KSTEP][TROW];
+  float sn[NTS][KSTEP][TROW];
   int pos[kMaxChunk];
   int blk[kMaxChunk / kBlockSize + 2];
 };
@@ -364,8 +365,9 @@ struct DecodeSmem {
 // each step's cos/sin rows are fetched once per workgroup, straight into an
 // LDS table stage by direct loads (no registers), and shared; every wave
 // reads its own head's K rows and V runs from the pools into registers.  NB
-// steps of loads are kept in flight (a ring of NB register buffers): the
-// loads of step j+NB are issued as soon as step j has consumed its buffer.
+// steps of loads are kept in flight (a ring of NB register buffers and
+// NB + 1 table stages): the loads of step j+NB are issued as soon as step j
+// has consumed its buffer.
 // Keeping the table out of registers puts the bf16 kernel at 159 VGPRs, so
 // three workgroups share a compute unit.  The
 // chunk's block ids and key positions are staged in LDS first, so no
@@ -381,7 +383,8 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   using C = Cfg<T, D>;
   using M = Mma<T>;
   typedef typename M::Op Op;
-  DecodeSmem<T, D>& sm = *reinterpret_cast<DecodeSmem<T, D>*>(smem_raw);
+  using SM = DecodeSmem<T, D, NB + 1>;
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -450,20 +453,20 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     Op k[C::NT][C::NC];
     Op v[C::NPV][C::ND];
   };
-  static_assert(!ROT || NB == 1, "one step of loads in flight: two table stages");
   Group grpbuf[NB];
 
   // Loads of step j (relative to k0) into a register group, in two parts so
   // that each is issued as soon as the previous step has consumed that part
   // of the group: the K rows after the score MFMAs, the V runs after the PV
   // MFMAs.
-  // The cos/sin rows of step j straight into table stage j & 1 (no
+  // The cos/sin rows of step j straight into table stage j % (NB + 1) (no
   // registers): wave w fills 1 KiB runs w, w + NW, ... of each table.  Issued
   // before that step's K loads: a wave's loads complete in order, so once its
-  // K registers are in, so are its table runs.
-  using SM = DecodeSmem<T, D>;
+  // K registers are in, so are its table runs.  The stage was last read in
+  // step j - NB - 1, which every wave has left: the stage is refilled during
+  // step j - NB, after that step's barrier.
   auto dma_tab = [&](int j) {
-    const int buf = j & 1;
+    const int buf = j % SM::NTS;
     const unsigned cbase = __builtin_amdgcn_readfirstlane(lds_address(&sm.cs[buf][0][0]));
     const unsigned sbase = __builtin_amdgcn_readfirstlane(lds_address(&sm.sn[buf][0][0]));
     const int w = __builtin_amdgcn_readfirstlane(wave);  // uniform: runs per wave
@@ -521,9 +524,9 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   for (int b = 0; b < NB; ++b)
     if (b < nsteps) issue(b, grpbuf[b]);
 
-  // step j with its loads in group gb; buf: LDS table slot
+  // step j with its loads in group gb; buf: LDS table stage
   auto step = [&](int j, Group& gb) {
-    const int buf = j & 1;
+    const int buf = j % SM::NTS;
     const int kb = k0 + j * C::KSTEP;  // absolute key index
     if constexpr (ROT) {
       wait_k(gb);
@@ -1810,6 +1813,16 @@ constexpr int mixed_waves() {
   return sizeof(T) == 2 ? kMixedWavesBf16 : kWaves;
 }
 
+// Steps of K/V loads each decode wave of the bf16 mixed launch keeps in
+// flight.  That launch holds one workgroup of 8 waves per compute unit (the
+// prefill tile's LDS and registers), so a decode item there has 8 waves'
+// loads in flight where the decode launch's three 4-wave workgroups have 12;
+// a second step per wave restores the bytes in flight per unit.
+template <typename T>
+constexpr int mixed_decode_depth() {
+  return sizeof(T) == 2 ? 2 : 1;
+}
+
 template <typename T, int D>
 constexpr int prefill_rows() {
   return sizeof(T) == 2 ? Pf<D, mixed_waves<T>(), kPrefillStep>::ROWS : kPrefillRows;
@@ -1819,7 +1832,8 @@ template <typename T, int D>
 struct MixedSmem {
   static constexpr int PB =
       sizeof(T) == 2 ? Pf<D, mixed_waves<T>(), kPrefillStep>::BYTES : PrefillSmem<T, D>::BYTES;
-  static constexpr int BYTES = PB > (int)sizeof(DecodeSmem<T, D>) ? PB : (int)sizeof(DecodeSmem<T, D>);
+  static constexpr int DB = (int)sizeof(DecodeSmem<T, D, mixed_decode_depth<T>() + 1>);
+  static constexpr int BYTES = PB > DB ? PB : DB;
 };
 
 // Mixed launch over the planner's work list.
@@ -1839,7 +1853,8 @@ __global__ void __launch_bounds__(64 * mixed_waves<T>(), 8 / mixed_waves<T>())
       prefill_tile<T, D>(a, it.y, it.z, it.w, smem);
     }
   } else {
-    decode_item<T, D, 1, NW, ROT>(a, it.y, it.z, it.w, (long long)a.cu_q[it.y], smem);
+    decode_item<T, D, mixed_decode_depth<T>(), NW, ROT>(a, it.y, it.z, it.w,
+                                                       (long long)a.cu_q[it.y], smem);
   }
 }
 
