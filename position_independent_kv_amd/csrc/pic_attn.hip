@@ -603,12 +603,21 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
 // o = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m).  One
 // workgroup per (request, kv head); threads take (column, 8 consecutive d)
 // pairs, and threads beyond those pairs take every SG-th chunk in parallel.
-// Merge of one split prefill tile (kPrefillTileRows threads, one query row
-// each): o = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m), over
-// the tile's chunks that saw a key.
+// Merge of one quarter of d of one split prefill tile (kPrefillTileRows
+// threads, one query row each): o = sum_s w_s o_s / sum_s w_s with
+// w_s = l_s 2^(m_s - max m), over the tile's chunks that saw a key of the
+// row (every row sees key 0, so at least the first chunk).  All chunks'
+// (m, l) are read first, then the partial rows, so no load waits on another
+// (a running rescale chained every chunk's loads behind the previous
+// chunk's, and the merge of a few long-context tiles took 20-30 us).  A
+// chunk that saw no key of the row may hold stale values: a select skips
+// it, nothing multiplies them.
+constexpr int kMergeParts = 4;
 template <typename T, int D>
-__device__ void merge_prefill_tile(const AttnArgs& a, int idx) {
+__device__ void merge_prefill_tile(const AttnArgs& a, int idx, int part) {
   static_assert(kThreads == kPrefillTileRows, "one thread per tile row");
+  static_assert(D % (4 * kMergeParts) == 0, "whole f32x4 pieces per part");
+  constexpr int NQ = D / kMergeParts / 4;  // f32x4 pieces of this part
   if (!a.pf_tiles || idx >= *a.pf_count) return;
   const int4 t = a.pf_tiles[idx];  // request, kv head, tile, first item
   const int r = t.x, g = t.y, p0 = t.w;
@@ -619,26 +628,35 @@ __device__ void merge_prefill_tile(const AttnArgs& a, int idx) {
   const int G = a.group;
   const int n = t.z * kPrefillTileRows + (int)threadIdx.x;
   if (n >= ql * G) return;
-  float m = -INFINITY, l = 0.0f;
-  f32x4 o[D / 4];
-#pragma unroll
-  for (int e = 0; e < D / 4; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const size_t row0 = (size_t)p0 * kPrefillTileRows + threadIdx.x;
+  float m = -INFINITY;
+#pragma unroll 4
   for (int s = 0; s < S; ++s) {
-    const size_t prow = (size_t)(p0 + s) * kPrefillTileRows + threadIdx.x;
-    const float2 ml = a.pf_ml[prow];
-    if (!(ml.y > 0.0f)) continue;  // the chunk holds no key of this row
-    const float mn = fmaxf(m, ml.x);
-    const float a0 = fast_exp2(m - mn), a1 = ml.y * fast_exp2(ml.x - mn);
-    l = l * a0 + a1;
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.pf_o + prow * D);
+    const float2 ml = a.pf_ml[row0 + (size_t)s * kPrefillTileRows];
+    if (ml.y > 0.0f) m = fmaxf(m, ml.x);
+  }
+  float l = 0.0f;
+  f32x4 o[NQ];
 #pragma unroll
-    for (int e = 0; e < D / 4; ++e) o[e] = o[e] * a0 + src[e] * a1;
-    m = mn;
+  for (int e = 0; e < NQ; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = 0; s < S; ++s) {
+    const size_t prow = row0 + (size_t)s * kPrefillTileRows;
+    const float2 ml = a.pf_ml[prow];
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.pf_o + prow * D) + part * NQ;
+    f32x4 x[NQ];
+#pragma unroll
+    for (int e = 0; e < NQ; ++e) x[e] = src[e];
+    const bool seen = ml.y > 0.0f;
+    const float w = seen ? ml.y * fast_exp2(ml.x - m) : 0.0f;
+    l += w;
+#pragma unroll
+    for (int e = 0; e < NQ; ++e) o[e] = seen ? o[e] + x[e] * w : o[e];
   }
   const float inv = 1.0f / l;
-  T* dst = (T*)a.out + (((size_t)q0 + n / G) * a.hq + g * G + n % G) * D;
+  T* dst = (T*)a.out + (((size_t)q0 + n / G) * a.hq + g * G + n % G) * D + part * NQ * 4;
 #pragma unroll
-  for (int e = 0; e < D / 4; ++e) store4<T>(dst + 4 * e, o[e], inv);
+  for (int e = 0; e < NQ; ++e) store4<T>(dst + 4 * e, o[e], inv);
 }
 
 // NaN into the output rows of request r for the q heads of kv head g (rows
@@ -660,7 +678,7 @@ __device__ void fill_nan_rows(const AttnArgs& a, int r, int g) {
 // Blocks [0, dec_blocks): dsplit per (request, kv head), each merging the
 // chunks of a q_len == 1 request for one slice of d (or, after a refused
 // work list, the first filling the request's rows with NaN); blocks beyond:
-// one per split prefill tile.
+// kMergeParts per split prefill tile, one per quarter of d.
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a, int dec_blocks,
                                                            int dsplit) {
@@ -669,7 +687,10 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a, int dec_b
   __shared__ float2 gml[kThreads];
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= dec_blocks) {
-    if constexpr (sizeof(T) == 2) merge_prefill_tile<T, D>(a, (int)blockIdx.x - dec_blocks);
+    if constexpr (sizeof(T) == 2) {
+      const int b = (int)blockIdx.x - dec_blocks;
+      merge_prefill_tile<T, D>(a, b / kMergeParts, b % kMergeParts);
+    }
     return;
   }
   const int rg = (int)blockIdx.x / dsplit, ds = (int)blockIdx.x % dsplit;
@@ -2248,7 +2269,7 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
   ok = record_after(s) && ok;
   // Always launched: whether a request has q_len == 1 is device data, and its
   // blocks exit at once where there is nothing to merge.
-  launch_combine<T, D>(a, s, true, split ? kSplitCUs / 2 : 0);
+  launch_combine<T, D>(a, s, true, split ? kSplitCUs / 2 * kMergeParts : 0);
   return hipGetLastError() == hipSuccess && ok ? PIC_OK : PIC_EHIP;
 }
 
