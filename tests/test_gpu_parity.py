@@ -85,13 +85,16 @@ def test_cache_write_readback_bit_exact(name):
                 assert np.all(np.isnan(dw.v_pool[b, :, :, o].float().cpu().numpy()))
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128)])
-def test_cache_write_slot_patterns(dtype, d):
+@pytest.mark.parametrize("dtype,d,hkv", [("bf16", 128, 3), ("bf16", 64, 3), ("f32", 128, 3),
+                                         ("f32", 128, 8), ("bf16", 64, 20)])
+def test_cache_write_slot_patterns(dtype, d, hkv):
     """Whole blocks filled in order (the transposing fast path), a run of 16 that is not
     block aligned, a reversed block, skipped and out-of-range slots and a ragged tail:
-    the pools hold exactly the oracle placement, everything else keeps its NaN fill."""
+    the pools hold exactly the oracle placement, everything else keeps its NaN fill.
+    With 8 fp32 heads of 128 or 20 bf16 heads of 64, the fast path takes the heads in two
+    passes of its 32 KB transpose stage."""
     torch = _torch()
-    hkv, nb, B = 3, 12, 16
+    nb, B = 12, 16
     slots = np.concatenate([
         np.arange(2 * B, 4 * B),                 # blocks 2, 3 in order
         np.arange(5 * B + 3, 6 * B + 3),         # 16 consecutive slots across blocks 5/6
