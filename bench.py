@@ -117,11 +117,13 @@ def time_config(name, steps, warmup, with_rows=False, only_timed=False):
     """Time one config.  Timed region (the benchmark's K steps, after W warm-up steps):
     step k writes the new tokens into layer k's pools and runs the attention call on them,
     cycling over pool_layers(w) copies, so every call is cold (the Infinity Cache holds
-    other layers' data); the library records HIP events right around the call's main
-    kernel on the launch stream (kernel_*: mean and median over the K steps).  Unless
-    only_timed, with >= 10 warm-ups and >= 20 samples each, cold: events around the whole
-    call and around its main kernel in the same steps (call_ms with call_kernel_ms, the
-    pair to compare), the call with no kernel events (what recording them costs); warm
+    other layers' data).  A decode batch whose new tokens sit at each request's last key
+    slot does both in one call (pic_attn_decode_append); other batches call
+    pic_cache_write, then the attention.  The call's main kernel records HIP events at its
+    start and end (pic_set_kernel_events; kernel_*: mean and median over the K steps).
+    Unless only_timed, with >= 10 warm-ups and >= 20 samples each, cold: events around the
+    whole call and around its main kernel in the same steps (call_ms with call_kernel_ms,
+    the pair to compare), the call with no kernel events (what recording them costs); warm
     (one layer back to back): the main kernel and the call."""
     import torch
 
@@ -139,17 +141,28 @@ def time_config(name, steps, warmup, with_rows=False, only_timed=False):
         f"{counts['bytes'] / 1e9:.3f} GB, {counts['flops'] / 1e12:.3f} TFLOP per attention call; "
         f"{nl} layer copies of the pools")
     stream = torch.cuda.current_stream()
+    # A decode step writes its new tokens inside the decode launch (pic_attn_decode_append:
+    # one launch fewer per step, same pool bytes and outputs); other steps write them with
+    # pic_cache_write before the attention call.
+    append = dw.appends_new_tokens()
+
+    def pre():
+        if not append:
+            dw.write_new_tokens()
+
+    def call():
+        return dw.attention_append() if append else dw.attention()
 
     def loop(n, layer_of, hooked, first=0):
         """n steps; returns (kernel ms, call ms) per step (kernel None when not hooked)."""
         kev, cev = _events(n), _events(n)
         for k in range(n):
             dw.use_layer(layer_of(first + k))
-            dw.write_new_tokens()
+            pre()
             if hooked:
                 pic.pic_set_kernel_events(*kev[k])
             cev[k][0].record(stream)
-            dw.attention()
+            call()
             cev[k][1].record(stream)
         pic.pic_set_kernel_events(None, None)
         torch.cuda.synchronize()
@@ -158,7 +171,8 @@ def time_config(name, steps, warmup, with_rows=False, only_timed=False):
     def warm_up(n, layer_of):
         for k in range(n):
             dw.use_layer(layer_of(k))
-            dw.step()
+            pre()
+            call()
 
     warm_up(warmup, lambda k: k)
     kev = _events(steps)
@@ -166,14 +180,15 @@ def time_config(name, steps, warmup, with_rows=False, only_timed=False):
     t0 = time.perf_counter()
     for k in range(steps):
         dw.use_layer(warmup + k)
-        dw.write_new_tokens()
+        pre()
         pic.pic_set_kernel_events(*kev[k])
-        dw.attention()
+        call()
     pic.pic_set_kernel_events(None, None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern = _ms(kev)
-    res = dict(name=name, w=w, counts=counts, layers=nl, step_ms=(t1 - t0) * 1e3 / steps,
+    res = dict(name=name, w=w, counts=counts, layers=nl, appends=append,
+               step_ms=(t1 - t0) * 1e3 / steps,
                kernel_ms=float(kern.mean()), kernel_median_ms=float(np.median(kern)),
                step_bytes=step_counts(w, counts))
     if not only_timed:
@@ -730,7 +745,13 @@ def main():
                 traffic=load_traffic(kernel, args.config), kernel=kernel,
                 timing="cold: the timed steps cycle over %d copies of the KV pools (layers), so "
                        "no call finds its data in the caches; achieved = algorithmic work / mean "
-                       "main-kernel time over the timed steps" % main_res["layers"],
+                       "main-kernel time over the timed steps (events recorded by the kernel's "
+                       "dispatch)%s" % (main_res["layers"],
+                                        "; each step's new tokens are written by the decode "
+                                        "launch itself (pic_attn_decode_append)"
+                                        if main_res["appends"] else
+                                        "; each step writes its new tokens with "
+                                        "pic_cache_write, then runs the attention call"),
                 kernel_ms=main_res["kernel_ms"], kernel_median_ms=main_res["kernel_median_ms"],
                 algorithmic_bytes=counts["bytes"], algorithmic_flops=counts["flops"],
                 unique_kv_bytes=counts["unique_kv_bytes"])

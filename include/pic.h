@@ -151,6 +151,35 @@ int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool, con
                     int max_seq_len, int dtype, void* out, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+
+/*
+ * pic_attn_decode_append -- pic_attn_decode that also writes the step's new
+ * tokens (MiniPIC §2.1: the cache holds keys unrotated; the write itself is
+ * pic_cache_write's).  Request r's new token is its key slot
+ * seq_lens[r] - 1: new_k and new_v [num_reqs][Hkv][head_dim] (dtype; row r =
+ * request r) are stored, unrotated, at offset (seq_lens[r] - 1) % block_size
+ * of block block_table[r * block_table_stride + (seq_lens[r] - 1) /
+ * block_size], and the same call attends to them there.  The pools then hold
+ * the same bytes, and out the same values bit for bit, as pic_cache_write of
+ * those rows followed by pic_attn_decode.  The work of the write is done by
+ * the decode launch itself (each request's last key chunk stores its token
+ * and uses it for its own key slot), which saves the separate write launch
+ * of a decode step.  Preconditions beyond pic_attn_decode's: seq_lens[r] >= 1,
+ * and no other request of the call reads the slot being written (a decode
+ * appends to its own tail block).  A request with seq_len == 0 writes
+ * nothing.  A block id out of range is not written (the attention reads it
+ * clamped, as everywhere).  Errors as pic_attn_decode; PIC_EINVAL when
+ * new_k or new_v is NULL.  The pools are written; the rest is only read.
+ */
+int pic_attn_decode_append(const void* q, const void* new_k, const void* new_v,
+                           const int32_t* q_pos, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, int block_table_stride,
+                           const int32_t* seq_lens, const int32_t* cu_seqlens_k,
+                           const int32_t* k_pos, const float* cos_tab, const float* sin_tab,
+                           int max_pos, int num_reqs, int num_q_heads, int num_kv_heads,
+                           int head_dim, int block_size, int num_blocks, int max_seq_len,
+                           int dtype, void* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
 /*
  * pic_attn_decode_noalloc -- pic_attn_decode for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
@@ -408,16 +437,18 @@ int pic_decode_split_len(int seq_len, int dtype);
 
 /*
  * pic_set_kernel_events -- measurement hook.  While set (both non-null
- * hipEvent_t handles, passed as void*), every attention call made from the
- * calling host thread records `before` on its stream immediately before it
- * launches its main kernel (decode_kernel for pic_attn_decode and
+ * hipEvent_t handles, passed as void*, created with timing enabled), every
+ * attention call made from the calling host thread hands them to the
+ * dispatch of its main kernel (decode_kernel for pic_attn_decode and
  * pic_attn_decode_rotated, decode_shared_kernel for pic_attn_decode_shared,
- * mixed_kernel for pic_attn_prefill*) and `after` immediately after it, so
+ * mixed_kernel for pic_attn_prefill*), which records `before` at the
+ * kernel's start and `after` at its end (hipExtLaunchKernel's start and
+ * stop events: no extra packets on the stream).  So
  * hipEventElapsedTime(before, after) is that kernel's duration alone,
  * without the planning and merge launches of the call.  The setting is per
  * host thread; both null turns it off.  The events stay owned by the
  * caller.  Errors: PIC_EINVAL when exactly one handle is null; an attention
- * call returns PIC_EHIP when recording fails.
+ * call returns PIC_EHIP when the launch fails.
  */
 int pic_set_kernel_events(void* before, void* after);
 

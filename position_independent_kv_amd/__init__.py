@@ -36,7 +36,7 @@ EXPORTS = [
     "pic_build_block_tables", "pic_blocks_copy", "pic_sched_create", "pic_sched_destroy",
     "pic_sched_add_span", "pic_sched_add_request", "pic_sched_step", "pic_set_kernel_events",
     "pic_attn_decode_shared", "pic_attn_decode_shared_workspace_size", "pic_attn_decode_noalloc",
-    "pic_stream_read",
+    "pic_stream_read", "pic_attn_decode_append",
 ]
 PIC_SCHED_ISPS, PIC_SCHED_BARRIER = 0, 1
 PIC_SEQ_SPAN, PIC_SEQ_PROMPT, PIC_SEQ_DECODE = 0, 1, 2
@@ -114,6 +114,8 @@ def _load():
     lib.pic_sched_step.argtypes = [c_void, ctypes.POINTER(_SchedBatch)]
     lib.pic_set_kernel_events.argtypes = [c_void, c_void]
     lib.pic_attn_decode_shared.argtypes = lib.pic_attn_decode.argtypes
+    lib.pic_attn_decode_append.argtypes = ([c_void] * 7 + [c_int] + [c_void] * 5 + [c_int] * 9
+                                           + [c_void, c_void, c_size, c_void])
     lib.pic_attn_decode_noalloc.argtypes = ([c_void] * 5 + [c_int] + [c_void] * 5 + [c_int] * 9
                                             + [c_void, c_void])
     lib.pic_attn_decode_shared_workspace_size.restype = c_size
@@ -270,6 +272,39 @@ def pic_attn_decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens_
     """One query row per request: q, out [R][Hq][d]; metadata int32 device tensors."""
     _decode_call("pic_attn_decode", q, q_pos, k_pool, v_pool, block_table, seq_lens,
                  cu_seqlens_k, k_pos, cos_tab, sin_tab, max_seq_len, out, workspace, stream)
+
+
+def pic_attn_decode_append(q, new_k, new_v, q_pos, k_pool, v_pool, block_table, seq_lens,
+                           cu_seqlens_k, k_pos, cos_tab, sin_tab, max_seq_len, out, workspace,
+                           stream=None):
+    """pic_attn_decode that also writes each request's new token: new_k, new_v [R][Hkv][d]
+    (q's dtype) are request r's key (unrotated) and value, stored as its key slot
+    seq_lens[r] - 1, which the same call attends to.  The pools hold the same bytes and out
+    the same values as pic_cache_write followed by pic_attn_decode."""
+    torch = _torch()
+    i32 = torch.int32
+    fn = "pic_attn_decode_append"
+    R, hq, d = q.shape
+    nb, hkv, bs, pd = _pool_dims(k_pool, v_pool)
+    if pd != d or tuple(out.shape) != (R, hq, d) or out.dtype != q.dtype:
+        raise ValueError("q / out / pool head sizes disagree")
+    for t in (new_k, new_v):
+        if tuple(t.shape) != (R, hkv, d):
+            raise ValueError(f"{fn}: new_k / new_v must be [{R}][{hkv}][{d}]")
+    _check_meta(fn, R, R, d, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab)
+    if validation_enabled():
+        _validate(fn, None, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos, 1, max_seq_len,
+                  cos_tab.shape[0], nb)
+    _check(_load().pic_attn_decode_append(
+        _ptr(q, "q"), _ptr(new_k, "new_k", q.dtype), _ptr(new_v, "new_v", q.dtype),
+        _ptr(q_pos, "q_pos", i32), _ptr(k_pool, "k_pool", q.dtype),
+        _ptr(v_pool, "v_pool", q.dtype), _ptr(block_table, "block_table", i32),
+        block_table.shape[1], _ptr(seq_lens, "seq_lens", i32),
+        _ptr(cu_seqlens_k, "cu_seqlens_k", i32), _ptr(k_pos, "k_pos", i32),
+        _ptr(cos_tab, "cos_tab", torch.float32), _ptr(sin_tab, "sin_tab", torch.float32),
+        cos_tab.shape[0], R, hq, hkv, d, bs, nb, int(max_seq_len), _dtype_code(q),
+        _ptr(out, "out"), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), fn)
 
 
 def pic_attn_decode_shared(q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens_k,

@@ -45,6 +45,7 @@
 //   launch with few tiles splits long tiles into key chunks, merged by
 //   combine_kernel.  fp32 tiles use four waves, 128 rows and an online
 //   softmax.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -98,6 +99,10 @@ struct AttnArgs {
   // request, and per request s_max + 1 chunk start blocks
   const int* cdc_count;
   const int* cdc_start;
+  // decode with append (null elsewhere): row r ([hkv][D]) is request r's new
+  // token, its key slot seq_lens[r] - 1
+  const void* new_k;
+  const void* new_v;
 };
 
 // Work item x field: kind in bits 0-3; for a split prefill tile the split
@@ -376,10 +381,15 @@ struct DecodeSmem {
 // (max, sum) that combine_kernel merges.  Uniform across the workgroup.
 // ROT = false compiles the key rotation out (the pool then holds keys
 // already rotated to this request's positions): no positions, no table rows,
-// no per-step barrier.
-template <typename T, int D, int NB, int NW, bool ROT>
+// no per-step barrier.  APPEND: the request's new token (a.new_k / a.new_v
+// row r) is its key slot L - 1, in the last chunk.  That chunk's workgroup
+// stores the token's rows of its heads into the pools (for later calls) and
+// keeps them in LDS (s_new: [2][NW][D], K then V), and its last step takes
+// key L - 1 from there instead of from the pools, so no workgroup reads
+// what another one writes in the same launch.
+template <typename T, int D, int NB, int NW, bool ROT, bool APPEND = false>
 __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long qrow,
-                            unsigned char* smem_raw) {
+                            unsigned char* smem_raw, T* s_new = nullptr) {
   using C = Cfg<T, D>;
   using M = Mma<T>;
   typedef typename M::Op Op;
@@ -418,6 +428,24 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   }
   const int nsteps = cdiv(k1 - k0, C::KSTEP);
 
+  // append: the new token's K and V elements this thread stores (below)
+  const bool append = APPEND && s == S - 1;
+  constexpr int kNewPerThread = APPEND ? (NW * D + NTH - 1) / NTH : 1;
+  T new_kx[kNewPerThread], new_vx[kNewPerThread];
+  if (append) {
+    const T* nk = (const T*)a.new_k + (size_t)r * a.hkv * D;
+    const T* nv = (const T*)a.new_v + (size_t)r * a.hkv * D;
+#pragma unroll
+    for (int i = 0; i < kNewPerThread; ++i) {
+      const int e = tid + i * NTH;
+      const int gw = hg * NW + e / D;
+      if (e < NW * D && gw < a.hkv) {
+        new_kx[i] = nk[(size_t)gw * D + e % D];
+        new_vx[i] = nv[(size_t)gw * D + e % D];
+      }
+    }
+  }
+
   // chunk metadata -> LDS: positions of keys k0.., block ids of blocks k0/16..
   {
     const int32_t* bt = a.block_table + (size_t)r * a.bt_stride;
@@ -435,6 +463,19 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   Op qop[C::NC];
   const bool qvalid = row16 < G;
   load_query<T, D>(a, qrow, ga * G + (qvalid ? row16 : 0), a.q_pos[qrow], qvalid, grp, qop);
+  // append: the new token's rows of this workgroup's heads into LDS (their
+  // loads were issued before the chunk's metadata, so their latency overlaps
+  // it); they go to the pools once the item is done
+  if (append) {
+#pragma unroll
+    for (int i = 0; i < kNewPerThread; ++i) {
+      const int e = tid + i * NTH;
+      if (e < NW * D && hg * NW + e / D < a.hkv) {
+        s_new[e] = new_kx[i];
+        s_new[NW * D + e] = new_vx[i];
+      }
+    }
+  }
   __syncthreads();
 
   const T* kpool = (const T*)a.k_pool;
@@ -532,6 +573,14 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
       wait_k(gb);
       __syncthreads();
     }
+    if (append && j == nsteps - 1) {  // key L - 1: the new token's K, before its rotation
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+        if (kb + key_of<C::NT>(t, row16) == L - 1)
+#pragma unroll
+          for (int c = 0; c < C::NC; ++c)
+            gb.k[t][c] = M::load(s_new + wave * D + grp * C::KPL + c * C::KCH);
+    }
     f32x4 sc[C::NT];
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
@@ -567,6 +616,11 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
           for (int e = 0; e < C::KPL; ++e)
             if (e >= nvalid) M::set(gb.v[mi][dt], e, 0.0f);
       }
+      if (append && nvalid >= 1 && nvalid <= C::KPL) {  // this run holds key L - 1
+#pragma unroll
+        for (int dt = 0; dt < C::ND; ++dt)
+          M::set(gb.v[mi][dt], nvalid - 1, (float)s_new[(NW + wave) * D + row16 + 16 * dt]);
+      }
     }
 #pragma unroll
     for (int mi = 0; mi < C::NPV; ++mi) {
@@ -583,6 +637,23 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
       if (j0 + b < nsteps) step(j0 + b, grpbuf[b]);
   }
 
+  // append: the new token into the pools, for later calls (nothing in this
+  // launch reads it there; a block id out of range is not written)
+  if (append) {
+    const int blk = a.block_table[(size_t)r * a.bt_stride + ((L - 1) >> 4)];
+    const int off = (L - 1) & 15;
+    if (blk >= 0 && blk < a.num_blocks) {
+      T* kpw = (T*)a.k_pool;
+      T* vpw = (T*)a.v_pool;
+      for (int e = tid; e < NW * D; e += NTH) {
+        const int gw = hg * NW + e / D, d = e % D;
+        if (gw < a.hkv) {
+          kpw[(((size_t)blk * a.hkv + gw) * kBlockSize + off) * D + d] = s_new[e];
+          vpw[(((size_t)blk * a.hkv + gw) * D + d) * kBlockSize + off] = s_new[NW * D + e];
+        }
+      }
+    }
+  }
   const float l_tot = col_sum(l_run);
   if (!active || row16 >= G) return;
   const float inv = 1.0f / l_tot;
@@ -1540,16 +1611,19 @@ constexpr int kDecodeDepth = 1;
 // Decode-only launch: logical item = (chunk s, request r, head group hg),
 // head group fastest, then request: the workgroups that read the same table
 // rows (the same key positions) run on one XCD and share its L2.
-template <typename T, int D, bool ROT>
+// APPEND: each request's new token is written by the workgroups of its last
+// chunk (decode_item).
+template <typename T, int D, bool ROT, bool APPEND = false>
 __global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(DecodeSmem<T, D>)];
+  __shared__ __attribute__((aligned(16))) T s_new[APPEND ? 2 * kWaves * D : 1];
   const long long n = (long long)gridDim.x;
   const long long l = xcd_logical(blockIdx.x, n);
   const int hg = (int)(l % a.nhg);
   const long long rs = l / a.nhg;
   const int r = (int)(rs % a.num_reqs);
   const int s = (int)(rs / a.num_reqs);
-  decode_item<T, D, kDecodeDepth, kWaves, ROT>(a, r, hg, s, r, smem);
+  decode_item<T, D, kDecodeDepth, kWaves, ROT, APPEND>(a, r, hg, s, r, smem, s_new);
 }
 
 // ---------------------------------------------------------------------------
@@ -2170,16 +2244,13 @@ __global__ void __launch_bounds__(1024) plan_kernel(const int32_t* __restrict__ 
 // host side
 // ---------------------------------------------------------------------------
 
-// Measurement hook (pic_set_kernel_events): events recorded around the main
-// kernel of each attention call made from this host thread.
+// Measurement hook (pic_set_kernel_events): events that the main kernel of
+// each attention call made from this host thread records at its start and
+// end.  They are handed to the kernel's dispatch (hipExtLaunchKernelGGL),
+// which records them from the dispatch's own timestamps, so the stream gets
+// no extra packets.  (Separate event records before and after the kernel
+// added about 10 us to every decode step.)  Null when unset: a plain launch.
 static thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
-
-static bool record_before(hipStream_t s) {
-  return !g_ev_before || hipEventRecord(g_ev_before, s) == hipSuccess;
-}
-static bool record_after(hipStream_t s) {
-  return !g_ev_after || hipEventRecord(g_ev_after, s) == hipSuccess;
-}
 
 static AttnArgs make_args(const AttnHostArgs& h, const WorkspaceLayout& w) {
   AttnArgs a{};
@@ -2212,6 +2283,8 @@ static AttnArgs make_args(const AttnHostArgs& h, const WorkspaceLayout& w) {
   a.ws_o = (float*)(ws + w.o_off);
   a.items = (const int4*)(ws + w.items_off);
   a.nitems = (const int*)(ws + w.count_off);
+  a.new_k = h.new_k;
+  a.new_v = h.new_v;
   if (w.pf_split && h.dtype == PIC_BF16) {
     a.pf_ml = (float2*)(ws + w.pf_ml_off);
     a.pf_o = (float*)(ws + w.pf_o_off);
@@ -2242,11 +2315,18 @@ template <typename T, int D, bool ROT>
 static int launch_decode(const AttnArgs& a, hipStream_t s) {
   const long long n = (long long)a.num_reqs * a.s_max * a.nhg;
   if (n > 0x7fffffffLL || (long long)a.num_reqs * a.hkv > 0x7fffffffLL) return PIC_EUNSUPPORTED;
-  bool ok = record_before(s);
-  hipLaunchKernelGGL((decode_kernel<T, D, ROT>), dim3((unsigned)n), dim3(kThreads), 0, s, a);
-  ok = record_after(s) && ok;
+  if constexpr (ROT) {
+    if (a.new_k) {
+      hipExtLaunchKernelGGL((decode_kernel<T, D, true, true>), dim3((unsigned)n),
+                            dim3(kThreads), 0, s, g_ev_before, g_ev_after, 0, a);
+      launch_combine<T, D>(a, s, false);
+      return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
+    }
+  }
+  hipExtLaunchKernelGGL((decode_kernel<T, D, ROT>), dim3((unsigned)n), dim3(kThreads), 0, s,
+                        g_ev_before, g_ev_after, 0, a);
   launch_combine<T, D>(a, s, false);
-  return hipGetLastError() == hipSuccess && ok ? PIC_OK : PIC_EHIP;
+  return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }
 
 template <typename T, int D, bool ROT>
@@ -2263,14 +2343,12 @@ static int launch_mixed(const AttnArgs& a, const WorkspaceLayout& w, const AttnH
                      Cfg<T, D>::KSTEP, prefill_rows<T, D>(), len_cap,
                      w.max_items, (int4*)(ws + w.items_off), (int*)(ws + w.count_off),
                      a.pf_tiles, a.pf_count);
-  bool ok = record_before(s);
-  hipLaunchKernelGGL((mixed_kernel<T, D, ROT>), dim3((unsigned)w.max_items),
-                     dim3(64 * mixed_waves<T>()), 0, s, a);
-  ok = record_after(s) && ok;
+  hipExtLaunchKernelGGL((mixed_kernel<T, D, ROT>), dim3((unsigned)w.max_items),
+                        dim3(64 * mixed_waves<T>()), 0, s, g_ev_before, g_ev_after, 0, a);
   // Always launched: whether a request has q_len == 1 is device data, and its
   // blocks exit at once where there is nothing to merge.
   launch_combine<T, D>(a, s, true, split ? kSplitCUs / 2 * kMergeParts : 0);
-  return hipGetLastError() == hipSuccess && ok ? PIC_OK : PIC_EHIP;
+  return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }
 
 // One decode call: position-free (ROT) or over an already rotated cache.
@@ -2304,12 +2382,10 @@ static int launch_decode_shared(const AttnArgs& a, const SharedDecodeLayout& w,
   hipLaunchKernelGGL(cdc_order_kernel, dim3(1), dim3(1024), 0, s, a, cnt, start,
                      (int*)(ws + w.coff_off), (int4*)(ws + w.items_off),
                      (int*)(ws + w.count_off));
-  bool ok = record_before(s);
-  hipLaunchKernelGGL((decode_shared_kernel<T, D>), dim3((unsigned)w.max_items), dim3(kThreads), 0,
-                     s, a);
-  ok = record_after(s) && ok;
+  hipExtLaunchKernelGGL((decode_shared_kernel<T, D>), dim3((unsigned)w.max_items),
+                        dim3(kThreads), 0, s, g_ev_before, g_ev_after, 0, a);
   launch_combine<T, D>(a, s, false);
-  return hipGetLastError() == hipSuccess && ok ? PIC_OK : PIC_EHIP;
+  return hipGetLastError() == hipSuccess ? PIC_OK : PIC_EHIP;
 }
 
 static int attn_decode_shared(const AttnHostArgs& h, hipStream_t s) {
@@ -2403,6 +2479,26 @@ extern "C" int pic_attn_decode(const void* q, const int32_t* q_pos, const void* 
                        seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab, max_pos, num_reqs,
                        num_reqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, max_seq_len, dtype, out, workspace, workspace_bytes};
+  return pic::attn_decode<true>(h, (hipStream_t)stream);
+}
+
+extern "C" int pic_attn_decode_append(const void* q, const void* new_k, const void* new_v,
+                                      const int32_t* q_pos, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, int block_table_stride,
+                                      const int32_t* seq_lens, const int32_t* cu_seqlens_k,
+                                      const int32_t* k_pos, const float* cos_tab,
+                                      const float* sin_tab, int max_pos, int num_reqs,
+                                      int num_q_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int num_blocks, int max_seq_len, int dtype,
+                                      void* out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  AttnHostArgs h{q, nullptr, q_pos, k_pool, v_pool, block_table, block_table_stride,
+                 seq_lens, cu_seqlens_k, k_pos, cos_tab, sin_tab, max_pos, num_reqs,
+                 num_reqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
+                 num_blocks, max_seq_len, dtype, out, workspace, workspace_bytes};
+  if (num_reqs > 0 && (!new_k || !new_v)) return PIC_EINVAL;
+  h.new_k = new_k;
+  h.new_v = new_v;
   return pic::attn_decode<true>(h, (hipStream_t)stream);
 }
 

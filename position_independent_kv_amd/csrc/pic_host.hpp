@@ -33,6 +33,9 @@ struct AttnHostArgs {
   void* out;
   void* workspace;
   size_t workspace_bytes;
+  // decode with append: request r's new token, [num_reqs][hkv][head_dim]
+  const void* new_k = nullptr;
+  const void* new_v = nullptr;
 };
 
 int check_dtype_dims(int dtype, int head_dim, int block_size);

@@ -182,6 +182,31 @@ class DeviceWorkload:
         self.write_new_tokens()
         return self.attention(decode)
 
+    def appends_new_tokens(self) -> bool:
+        """Whether the batch's new tokens are one per request, in request order, each at its
+        request's last key slot (what pic_attn_decode_append writes)."""
+        w = self.w
+        if w.kind != "decode" or w.new_slots.shape[0] != w.num_reqs:
+            return False
+        L = np.asarray(w.seq_lens, np.int64)
+        if (L < 1).any():
+            return False
+        bt = np.asarray(w.block_table, np.int64)
+        last = bt[np.arange(w.num_reqs), (L - 1) // w.block_size] * w.block_size \
+            + (L - 1) % w.block_size
+        return bool(np.array_equal(last, np.asarray(w.new_slots, np.int64)))
+
+    def attention_append(self, out=None):
+        """A decode step in one call: the decode launch writes request r's new token (row r
+        of new_k / new_v, its key slot seq_lens[r] - 1) itself (pic_attn_decode_append)."""
+        w = self.w
+        out = self.out if out is None else out
+        pic.pic_attn_decode_append(self.q, self.new_k, self.new_v, self.q_pos, self.k_pool,
+                                   self.v_pool, self.block_table, self.seq_lens, self.cu_k,
+                                   self.k_pos, self.cos, self.sin, w.max_seq_len, out,
+                                   self.workspace)
+        return out
+
 
 def run_workload(w: Workload, decode=None) -> np.ndarray:
     torch = _torch()

@@ -28,7 +28,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = pic.library()
     names = _declared()
-    assert len(names) == 27
+    assert len(names) == 28
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(pic.EXPORTS)
@@ -132,6 +132,19 @@ def test_entry_points_reject_bad_arguments_before_launch():
     args6 = list(args)
     args6[12] = 0
     assert lib.pic_attn_decode(*args6) == pic.PIC_OK
+    # decode with append: the same checks, and both new-token rows required
+    aargs = args[:1] + [buf, buf] + args[1:]
+    assert lib.pic_attn_decode_append(*aargs) == pic.PIC_EWORKSPACE
+    for i in (1, 2):
+        bad = list(aargs)
+        bad[i] = None
+        assert lib.pic_attn_decode_append(*bad) == pic.PIC_EINVAL
+    bad = list(aargs)
+    bad[15] = 30  # Hq not a multiple of Hkv
+    assert lib.pic_attn_decode_append(*bad) == pic.PIC_EUNSUPPORTED
+    empty = [None, None, None] + list(args6[1:])
+    empty[14] = 0
+    assert lib.pic_attn_decode_append(*empty) == pic.PIC_OK
     # prefill
     pargs = [buf] * 6 + [300] + [buf] * 5 + [4097, 4, 40, 16, 32, 8, 128, 16, 100, 4097, 1] + [
         buf, None, 0, None]
