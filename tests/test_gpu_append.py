@@ -65,6 +65,9 @@ CASES = {
                         n_spans=5, hq=8, hkv=4, dtype="f32"),
     "bf16-g1": dict(builder="decode", seed=74, R=4, seg_len=512, n_seg=2, n_shared=0, n_spans=0,
                     hq=8, hkv=8),
+    # 6 kv heads: the second head group's workgroup has two idle waves
+    "bf16-hkv6": dict(builder="decode", seed=77, R=5, seg_len=320, n_seg=2, n_shared=1,
+                      n_spans=5, hq=24, hkv=6),
 }
 
 
