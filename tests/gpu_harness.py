@@ -292,13 +292,19 @@ class TraceRun:
             if st["num_seqs"] == 0:
                 continue
             src = torch.from_numpy(st["src"]).to(dev)
+            decode_only = bool(st["max_q_len"] == 1)
+            if decode_only:  # one token per sequence, each at its sequence's last key slot
+                L = np.asarray(st["seq_lens"], np.int64)
+                bt = np.asarray(st["block_table"], np.int64)
+                last = bt[np.arange(L.shape[0]), (L - 1) // B] * B + (L - 1) % B
+                assert np.array_equal(last, np.asarray(st["slot_mapping"], np.int64))
             d = dict(q=q_all[src].contiguous(), k=k_all[src].contiguous(),
                      v=v_all[src].contiguous(), slots=i32(st["slot_mapping"], dev),
                      cu_q=i32(st["cu_seqlens_q"], dev), q_pos=i32(st["q_pos"], dev),
                      bt=i32(st["block_table"], dev), seq_lens=i32(st["seq_lens"], dev),
                      cu_k=i32(st["cu_seqlens_k"], dev), k_pos=i32(st["k_pos"], dev),
                      max_q_len=st["max_q_len"], max_seq_len=st["max_seq_len"], src=src,
-                     decode_only=bool(st["max_q_len"] == 1))
+                     decode_only=decode_only)
             d["out"] = torch.empty_like(d["q"])
             ws = max(ws, pic.pic_attn_workspace_size(st["num_seqs"], st["total_q"],
                                                      st["max_seq_len"], trace.hq, trace.hkv,
@@ -308,15 +314,17 @@ class TraceRun:
         self.rows = int(sum(st["total_q"] for st in self.steps))
 
     def run(self):
-        """Every step: cache write, then one attention call (the decode launch when every
-        sequence of the step is a single row, else the mixed launch)."""
+        """Every step: the new tokens' cache write and one attention call.  A step whose
+        sequences are all single rows is one decode launch that writes its tokens itself
+        (pic_attn_decode_append); any other step is pic_cache_write, then the mixed launch."""
         for d in self.dev_steps:
-            pic.pic_cache_write(d["k"], d["v"], d["slots"], self.k_pool, self.v_pool)
             if d["decode_only"]:
-                pic.pic_attn_decode(d["q"], d["q_pos"], self.k_pool, self.v_pool, d["bt"],
-                                    d["seq_lens"], d["cu_k"], d["k_pos"], self.cos, self.sin,
-                                    d["max_seq_len"], d["out"], self.workspace)
+                pic.pic_attn_decode_append(d["q"], d["k"], d["v"], d["q_pos"], self.k_pool,
+                                           self.v_pool, d["bt"], d["seq_lens"], d["cu_k"],
+                                           d["k_pos"], self.cos, self.sin, d["max_seq_len"],
+                                           d["out"], self.workspace)
             else:
+                pic.pic_cache_write(d["k"], d["v"], d["slots"], self.k_pool, self.v_pool)
                 pic.pic_attn_prefill(d["q"], d["cu_q"], d["q_pos"], self.k_pool, self.v_pool,
                                      d["bt"], d["seq_lens"], d["cu_k"], d["k_pos"], self.cos,
                                      self.sin, d["max_q_len"], d["max_seq_len"], d["out"],
