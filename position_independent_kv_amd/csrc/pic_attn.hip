@@ -373,8 +373,9 @@ struct DecodeSmem {
 // steps of loads are kept in flight (a ring of NB register buffers and
 // NB + 1 table stages): the loads of step j+NB are issued as soon as step j
 // has consumed its buffer.
-// Keeping the table out of registers puts the bf16 kernel at 159 VGPRs, so
-// three workgroups share a compute unit.  The
+// Keeping the table out of registers puts the bf16 kernel of the decode
+// launch (two steps in flight) at 230 VGPRs without spills: two workgroups
+// share a compute unit.  The
 // chunk's block ids and key positions are staged in LDS first, so no
 // address lookup ever waits behind the data loads.  With one chunk the wave
 // writes the output row; otherwise it writes a normalised partial and
@@ -1605,8 +1606,10 @@ __device__ __forceinline__ int tile_keys(int L, int ql, int k, int rows, int gro
 }
 
 // Steps of K/V loads each decode wave keeps in flight.  Measured on MI355X:
-// one step at two waves per SIMD beats deeper rings at one wave per SIMD.
-constexpr int kDecodeDepth = 1;
+// two steps at two workgroups per compute unit (8 waves, 230 VGPRs) beat one
+// step at three (12 waves, 159 VGPRs) by about 2% on the 64 x 4097-key
+// batches; deeper rings at one workgroup per unit were slower.
+constexpr int kDecodeDepth = 2;
 
 // Decode-only launch: logical item = (chunk s, request r, head group hg),
 // head group fastest, then request: the workgroups that read the same table
@@ -1615,7 +1618,8 @@ constexpr int kDecodeDepth = 1;
 // chunk (decode_item).
 template <typename T, int D, bool ROT, bool APPEND = false>
 __global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(DecodeSmem<T, D>)];
+  __shared__ __attribute__((aligned(16)))
+  unsigned char smem[sizeof(DecodeSmem<T, D, kDecodeDepth + 1>)];
   __shared__ __attribute__((aligned(16))) T s_new[APPEND ? 2 * kWaves * D : 1];
   const long long n = (long long)gridDim.x;
   const long long l = xcd_logical(blockIdx.x, n);
@@ -1885,7 +1889,8 @@ __global__ void __launch_bounds__(1024) cdc_order_kernel(AttnArgs a, const int* 
 // The shared-span decode's main kernel: one work-list item per workgroup.
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads, 2) decode_shared_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(DecodeSmem<T, D>)];
+  __shared__ __attribute__((aligned(16)))
+  unsigned char smem[sizeof(DecodeSmem<T, D, kDecodeDepth + 1>)];
   if ((int)blockIdx.x >= *a.nitems) return;
   const int4 it = a.items[blockIdx.x];
   decode_item<T, D, kDecodeDepth, kWaves, true>(a, it.y, it.z, it.w, it.y, smem);
@@ -1910,9 +1915,8 @@ constexpr int mixed_waves() {
 
 // Steps of K/V loads each decode wave of the bf16 mixed launch keeps in
 // flight.  That launch holds one workgroup of 8 waves per compute unit (the
-// prefill tile's LDS and registers), so a decode item there has 8 waves'
-// loads in flight where the decode launch's three 4-wave workgroups have 12;
-// a second step per wave restores the bytes in flight per unit.
+// prefill tile's LDS and registers); like the decode launch's two 4-wave
+// workgroups, its waves keep two steps each in flight.
 template <typename T>
 constexpr int mixed_decode_depth() {
   return sizeof(T) == 2 ? 2 : 1;
