@@ -295,6 +295,7 @@ def pic_attn_decode_append(q, new_k, new_v, q_pos, k_pool, v_pool, block_table, 
     if validation_enabled():
         _validate(fn, None, q_pos, block_table, seq_lens, cu_seqlens_k, k_pos, 1, max_seq_len,
                   cos_tab.shape[0], nb)
+        _validate_append(fn, block_table, seq_lens, bs)
     _check(_load().pic_attn_decode_append(
         _ptr(q, "q"), _ptr(new_k, "new_k", q.dtype), _ptr(new_v, "new_v", q.dtype),
         _ptr(q_pos, "q_pos", i32), _ptr(k_pool, "k_pool", q.dtype),
@@ -392,6 +393,24 @@ def _validate(fn, cu_seqlens_q, q_pos, block_table, seq_lens, cu_seqlens_k, k_po
         raise ValueError(f"{fn}: {msg}")
     if cu_q is not None and R and int(np.diff(cu_q.astype(np.int64)).max()) > max_q_len:
         raise ValueError(f"{fn}: a request has more than max_q_len = {max_q_len} query rows")
+
+
+def _validate_append(fn, block_table, seq_lens, block_size):
+    """pic_attn_decode_append's own precondition, on host copies: the block that receives a
+    request's new token (its key slot seq_lens[r] - 1) is read by no other request of the
+    call (the launch writes it while the other requests' chunks read theirs)."""
+    bt = block_table.detach().cpu().numpy()
+    sl = seq_lens.detach().cpu().numpy().astype(np.int64)
+    R = sl.shape[0]
+    nb = (np.maximum(sl, 0) + block_size - 1) // block_size
+    owner = np.repeat(np.arange(R), nb)
+    used = np.concatenate([bt[r, :nb[r]] for r in range(R)]) if R else np.zeros(0, np.int64)
+    for r in np.flatnonzero(sl > 0):
+        tail = bt[r, (sl[r] - 1) // block_size]
+        others = owner[(used == tail) & (owner != r)]
+        if others.size:
+            raise ValueError(f"{fn}: request {r} appends to block {tail}, which request "
+                             f"{int(others[0])} also reads")
 
 
 def _decode_call(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, cu_seqlens_k, k_pos,

@@ -483,6 +483,17 @@ def test_binding_validate_mode_checks_device_values(monkeypatch):
             mutate(kw[name])
         with pytest.raises(ValueError, match=what):
             pic.pic_attn_decode(**kw)
+    # decode with append: the block receiving a request's new token must be its own
+    kw = _cpu_decode_args(w)
+    new = kw["q"].new_zeros((w.num_reqs, w.hkv, w.d))
+    app = dict(kw, new_k=new, new_v=new.clone())
+    with pytest.raises(ValueError, match="GPU"):
+        pic.pic_attn_decode_append(**app)
+    bt = app["block_table"]
+    L1 = int(app["seq_lens"][1])
+    bt[1, (L1 - 1) // w.block_size] = bt[0, 0]   # request 1's tail block is request 0's first
+    with pytest.raises(ValueError, match="request 1 appends to block"):
+        pic.pic_attn_decode_append(**app)
     # prefill: a request longer than max_q_len
     import torch
     pw = make_workload("y", values=False, builder="prefill", seed=4, R=2, n_spans=3, span_len=32,
