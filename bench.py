@@ -503,7 +503,7 @@ def attention_ceiling(reps=20):
                 torch.cuda.synchronize()
             ms = float(np.median(_ms(ev)))
             res[label] = {"ms": ms, "TFLOPs": 4 * d * B * H * pairs[label] / (ms * 1e-3) / 1e12}
-        except Exception as e:  # the flash backend may not take this mask on this build
+        except Exception as e:  # the flash backend of this torch version may not take this mask
             res[label] = {"error": f"{type(e).__name__}: {str(e)[:160]}"}
     del q, k, v
     torch.cuda.empty_cache()
