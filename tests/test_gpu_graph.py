@@ -51,3 +51,33 @@ def test_step_replays_from_a_hip_graph(case):
         dw.attention(out=other)  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(_bits(other), _bits(eager)), i
+
+
+def test_decode_step_with_append_replays_from_a_hip_graph():
+    """A decode step as one pic_attn_decode_append call (the launch writes the new tokens),
+    captured and replayed: every replay rewrites the same slots with the same rows and must
+    give the eager output bit for bit, with eager steps between replays."""
+    import torch
+    w = make_workload("decode", **dict(CASES["decode"]))
+    dw = DeviceWorkload(w)
+    assert dw.appends_new_tokens()
+    eager = dw.attention_append().clone()
+    static_out = torch.empty_like(dw.out)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dw.attention_append(out=static_out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dw.attention_append(out=static_out)
+    other = torch.empty_like(dw.out)
+    for i in range(4):
+        static_out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(static_out), _bits(eager)), i
+        dw.attention_append(out=other)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(other), _bits(eager)), i
