@@ -99,14 +99,15 @@ def pool_layers(w, cap=32):
     return int(min(cap, max(4, -(-(1 << 30) // pool))))
 
 
+def _event():
+    """A timing event of the library (no system-scope fence at its records, which costs a
+    step several microseconds with torch's default events)."""
+    import position_independent_kv_amd as pic
+    return pic.TimingEvent()
+
+
 def _events(n):
-    import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
-    for a, b in ev:   # the library records into existing HIP events
-        a.record()
-        b.record()
-    return ev
+    return [(_event(), _event()) for _ in range(n)]
 
 
 def _ms(ev):
@@ -206,7 +207,7 @@ def time_config(name, steps, warmup, with_rows=False, only_timed=False):
     if with_rows and not only_timed:
         # the other rows of the path, timed on their own (same stream, events)
         stream = torch.cuda.current_stream()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [_event() for _ in range(4)]
         cos = torch.empty_like(dw.cos)
         sin = torch.empty_like(dw.sin)
         e[0].record(stream)
@@ -248,7 +249,7 @@ def rope_ablation(name, reps=20):
         dw.attention()
         dw.attention_rotated()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    ev = [[_event() for _ in range(4)] for _ in range(reps)]
     for k in range(reps):
         ev[k][0].record(stream)
         dw.attention()
@@ -290,7 +291,7 @@ def shared_decode(name, reps=20):
         for _ in range(10):
             fn()
     torch.cuda.synchronize()
-    ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    ev = {k: [[_event() for _ in range(4)] for _ in range(reps)]
           for k in calls}
     for k in calls:
         for e in ev[k]:
@@ -343,7 +344,7 @@ def offload_bandwidth(n_blocks=4096, reps=5):
                         ("host_to_device", (hk, hv, dst, dk, dv, src))]:
         pic.pic_blocks_copy(*args)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = _event(), _event()
         e0.record(stream)
         for _ in range(reps):
             pic.pic_blocks_copy(*args)
@@ -384,7 +385,7 @@ def scheduled_trace(budget=8192, max_running=32, num_blocks=8192, reps=3):
         torch.cuda.synchronize()
         times = []
         for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = _event(), _event()
             e0.record(stream)
             tr.run()
             e1.record(stream)

@@ -453,6 +453,26 @@ int pic_decode_split_len(int seq_len, int dtype);
 int pic_set_kernel_events(void* before, void* after);
 
 /*
+ * pic_timing_event_create / _record / _elapsed_ms / _destroy -- measurement
+ * helpers: HIP events (hipEvent_t, passed as void*) created without the
+ * system-scope acquire / release fence of a default event
+ * (hipEventDisableSystemFence).  A default event's record writes back and
+ * invalidates caches and slows the work after it (on a 64-request decode step
+ * about 5-9 us per step with the pair of pic_set_kernel_events set, against
+ * about 2 us for these); nothing may read device memory through these events,
+ * they only time.  _create records the new event once on the default stream
+ * (so an unused pair reads 0 ms) and stores it in *event; _record records it
+ * on `stream`; _elapsed_ms writes the time from `start` to `stop` (both
+ * complete) in ms; _destroy frees it (NULL: no-op).  The library calls are
+ * the ones of the HIP runtime the library itself uses.  Errors: PIC_EINVAL for
+ * a NULL argument (except _destroy), PIC_EHIP when HIP reports an error.
+ */
+int pic_timing_event_create(void** event);
+int pic_timing_event_record(void* event, void* stream);
+int pic_timing_event_elapsed_ms(void* start, void* stop, float* ms);
+int pic_timing_event_destroy(void* event);
+
+/*
  * pic_stream_read -- measurement helper: read `bytes` of device memory at
  * `src` once, with 16-byte loads (`workgroups` workgroups of 256 lanes
  * striding over the buffer in 4 KiB segments, 8 segments per iteration), the

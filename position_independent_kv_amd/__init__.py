@@ -36,7 +36,8 @@ EXPORTS = [
     "pic_build_block_tables", "pic_blocks_copy", "pic_sched_create", "pic_sched_destroy",
     "pic_sched_add_span", "pic_sched_add_request", "pic_sched_step", "pic_set_kernel_events",
     "pic_attn_decode_shared", "pic_attn_decode_shared_workspace_size", "pic_attn_decode_noalloc",
-    "pic_stream_read", "pic_attn_decode_append",
+    "pic_stream_read", "pic_attn_decode_append", "pic_timing_event_create",
+    "pic_timing_event_record", "pic_timing_event_elapsed_ms", "pic_timing_event_destroy",
 ]
 PIC_SCHED_ISPS, PIC_SCHED_BARRIER = 0, 1
 PIC_SEQ_SPAN, PIC_SEQ_PROMPT, PIC_SEQ_DECODE = 0, 1, 2
@@ -114,6 +115,10 @@ def _load():
     lib.pic_sched_step.argtypes = [c_void, ctypes.POINTER(_SchedBatch)]
     lib.pic_set_kernel_events.argtypes = [c_void, c_void]
     lib.pic_attn_decode_shared.argtypes = lib.pic_attn_decode.argtypes
+    lib.pic_timing_event_create.argtypes = [ctypes.POINTER(c_void)]
+    lib.pic_timing_event_record.argtypes = [c_void, c_void]
+    lib.pic_timing_event_elapsed_ms.argtypes = [c_void, c_void, ctypes.POINTER(ctypes.c_float)]
+    lib.pic_timing_event_destroy.argtypes = [c_void]
     lib.pic_attn_decode_append.argtypes = ([c_void] * 7 + [c_int] + [c_void] * 5 + [c_int] * 9
                                            + [c_void, c_void, c_size, c_void])
     lib.pic_attn_decode_noalloc.argtypes = ([c_void] * 5 + [c_int] + [c_void] * 5 + [c_int] * 9
@@ -724,20 +729,53 @@ def pic_stream_read(src, workgroups: int, sink, order=None, piece_bytes: int = 0
                                    _stream(stream)), "pic_stream_read")
 
 
+class TimingEvent:
+    """A HIP event for timing only (pic_timing_event_create: no system-scope fence at its
+    records).  record(stream=None) and elapsed_time(end) in ms, as torch.cuda.Event."""
+
+    def __init__(self):
+        lib = _load()
+        h = ctypes.c_void_p()
+        _check(lib.pic_timing_event_create(ctypes.byref(h)), "pic_timing_event_create")
+        self.handle = h.value
+
+    def record(self, stream=None):
+        _check(_load().pic_timing_event_record(ctypes.c_void_p(self.handle), _stream(stream)),
+               "pic_timing_event_record")
+
+    def elapsed_time(self, end) -> float:
+        ms = ctypes.c_float()
+        _check(_load().pic_timing_event_elapsed_ms(ctypes.c_void_p(self.handle),
+                                                   ctypes.c_void_p(end.handle),
+                                                   ctypes.byref(ms)),
+               "pic_timing_event_elapsed_ms")
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.pic_timing_event_destroy(ctypes.c_void_p(self.handle))
+            self.handle = None
+
+
 def pic_set_kernel_events(before=None, after=None) -> None:
-    """Record two torch.cuda.Event objects around the main kernel of every following
-    attention call on this thread (None, None turns it off); elapsed_time(before, after)
-    is then that kernel's duration alone.  An event whose HIP event does not exist yet
-    (torch creates it on first record) is recorded once here."""
+    """Have the main kernel of every following attention call on this thread record two
+    events at its start and end (None, None turns it off); elapsed_time(before, after) is
+    then that kernel's duration alone.  The events are TimingEvent objects or
+    torch.cuda.Event objects (a torch event whose HIP event does not exist yet is recorded
+    once here)."""
     lib = _load()
     if (before is None) != (after is None):
         raise ValueError("pass both events or neither")
     if before is None:
         _check(lib.pic_set_kernel_events(None, None), "pic_set_kernel_events")
         return
+    handles = []
     for e in (before, after):
-        if not e.cuda_event:
-            e.record()
-    _check(lib.pic_set_kernel_events(ctypes.c_void_p(before.cuda_event),
-                                     ctypes.c_void_p(after.cuda_event)),
+        if isinstance(e, TimingEvent):
+            handles.append(e.handle)
+        else:
+            if not e.cuda_event:
+                e.record()
+            handles.append(e.cuda_event)
+    _check(lib.pic_set_kernel_events(ctypes.c_void_p(handles[0]), ctypes.c_void_p(handles[1])),
            "pic_set_kernel_events")

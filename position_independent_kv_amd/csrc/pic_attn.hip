@@ -2470,6 +2470,40 @@ extern "C" int pic_set_kernel_events(void* before, void* after) {
   return PIC_OK;
 }
 
+// Timing events: HIP events without the system-scope acquire / release that a
+// default event record carries (hipEventDisableSystemFence).  That fence
+// writes back and invalidates caches at every record and slows the work that
+// follows; these events only measure, nothing reads memory through them.
+extern "C" int pic_timing_event_create(void** event) {
+  if (!event) return PIC_EINVAL;
+  *event = nullptr;
+  hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return PIC_EHIP;
+  // recorded once on the default stream, so a pair never recorded since reads 0 ms
+  if (hipEventRecord(e, nullptr) != hipSuccess) {
+    hipEventDestroy(e);
+    return PIC_EHIP;
+  }
+  *event = e;
+  return PIC_OK;
+}
+
+extern "C" int pic_timing_event_record(void* event, void* stream) {
+  if (!event) return PIC_EINVAL;
+  return hipEventRecord((hipEvent_t)event, (hipStream_t)stream) == hipSuccess ? PIC_OK : PIC_EHIP;
+}
+
+extern "C" int pic_timing_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return PIC_EINVAL;
+  return hipEventElapsedTime(ms, (hipEvent_t)start, (hipEvent_t)stop) == hipSuccess ? PIC_OK
+                                                                                    : PIC_EHIP;
+}
+
+extern "C" int pic_timing_event_destroy(void* event) {
+  if (!event) return PIC_OK;
+  return hipEventDestroy((hipEvent_t)event) == hipSuccess ? PIC_OK : PIC_EHIP;
+}
+
 extern "C" int pic_attn_decode(const void* q, const int32_t* q_pos, const void* k_pool,
                                const void* v_pool, const int32_t* block_table,
                                int block_table_stride, const int32_t* seq_lens,

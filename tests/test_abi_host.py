@@ -28,7 +28,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = pic.library()
     names = _declared()
-    assert len(names) == 28
+    assert len(names) == 32
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(pic.EXPORTS)
@@ -49,6 +49,22 @@ def test_kernel_events_hook_arguments():
     assert lib.pic_set_kernel_events(None, None) == pic.PIC_OK
     with pytest.raises(ValueError):
         pic.pic_set_kernel_events(object(), None)
+
+
+def test_timing_event_helpers_reject_null_handles():
+    """The timing-event helpers check their pointers before any HIP call; destroying a null
+    handle is a no-op."""
+    lib = pic.library()
+    assert lib.pic_timing_event_create(None) == pic.PIC_EINVAL
+    assert lib.pic_timing_event_record(None, None) == pic.PIC_EINVAL
+    ms = ctypes.c_float()
+    assert lib.pic_timing_event_elapsed_ms(None, ctypes.c_void_p(16), ctypes.byref(ms)) \
+        == pic.PIC_EINVAL
+    assert lib.pic_timing_event_elapsed_ms(ctypes.c_void_p(16), None, ctypes.byref(ms)) \
+        == pic.PIC_EINVAL
+    assert lib.pic_timing_event_elapsed_ms(ctypes.c_void_p(16), ctypes.c_void_p(16), None) \
+        == pic.PIC_EINVAL
+    assert lib.pic_timing_event_destroy(None) == pic.PIC_OK
 
 
 def test_workspace_size_rules():

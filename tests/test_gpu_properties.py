@@ -325,14 +325,19 @@ def test_single_key_context():
             assert _same_bits(got[r, h], dw.v_pool[blk, h // G, :, 0]), (r, h)
 
 
+@pytest.mark.parametrize("events", ["torch", "timing"])
 @pytest.mark.parametrize("kw", [SMALL_DEC, SMALL_MIX], ids=["decode", "mixed"])
-def test_kernel_events_bracket_the_main_kernel(kw):
+def test_kernel_events_bracket_the_main_kernel(kw, events):
     """With the measurement hook set, the call's results are unchanged and the events
-    span the main kernel only: a positive time no longer than the whole call."""
+    span the main kernel only: a positive time no longer than the whole call.  Both kinds
+    of event: torch's and the library's timing events."""
     torch = _torch()
     w, dw = _fresh(kw)
     base = _rerun(dw)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    if events == "torch":
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    else:
+        ev = [pic.TimingEvent() for _ in range(4)]
     stream = torch.cuda.current_stream()
     pic.pic_set_kernel_events(ev[2], ev[3])
     try:
