@@ -346,6 +346,13 @@ __device__ __forceinline__ void lds_direct_load16(const void* src, unsigned lds_
       : "memory");
 }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory loads of this wave are outstanding (loads
+// complete in issue order, so every load issued before the last N has landed).
+template <int N>
+__device__ __forceinline__ void vm_wait_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 __device__ __forceinline__ unsigned lds_address(const void* p) {
   return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -1072,8 +1079,9 @@ struct Pf {
 //
 // Staging: each 64-key step is gathered from the paged pools once per
 // workgroup.  Every thread loads its share of K rows and cos/sin rows into
-// registers one step before they are written; K is rotated on the way into
-// LDS.  V^T needs no arithmetic, so it goes from the pool straight into LDS
+// registers right after it has rotated the previous ones into LDS, a whole
+// step before they are rotated in turn (in the step's second half); K is
+// rotated on the way into LDS.  V^T needs no arithmetic, so it goes from the pool straight into LDS
 // (16-byte direct loads, no registers, no LDS write instructions).  K is
 // staged two steps ahead (three K stages: the block being exponentiated may
 // be re-read, the next block is being multiplied, and the step after is
@@ -1173,11 +1181,15 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     TV c, s;    // their cos/sin
   };
   KRegs kr;
-  // Addresses (block ids, position) of the next loads, looked up one step
-  // before those loads are issued: kmeta_* / vmeta_* hold the ones in use,
-  // the *_nx copies the ones being fetched.  Lookups are issued before the
-  // data loads of a step, so waiting for a lookup never waits for data (the
-  // load counter completes in issue order).
+  // vector-memory loads issued by one kmeta() and by one kload(): the
+  // counted waits below rely on them
+  constexpr int kMetaLoads = ROT ? 2 : 1;
+  constexpr int kDataLoads = 2 + (ROT ? 2 * cdiv(P::KPT * 4, 16) : 0);
+  // Addresses (block ids, position) of the next loads, looked up before
+  // those loads are issued: kmeta_* / vmeta_* hold the ones in use, the *_nx
+  // copies the ones being fetched.  Lookups are issued at the top of a step,
+  // before its V direct loads, and used at the end of the step (K) or at
+  // the top of the next (V).
   int kmeta_blk, kmeta_pos, vmeta_blk;
   int kmeta_blk_nx, kmeta_pos_nx = 0, vmeta_blk_nx;
   auto kmeta = [&](int kb) {  // kb: absolute key index of a step's first key
@@ -1242,12 +1254,12 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
   };
   auto kstore = [&](int step) { kstore_from(step, kr); };
   // Slots at or beyond L hold no data: once this lane's own direct loads
-  // into V stage `step` have landed, it overwrites those keys of its units
-  // with zeros (only the last step has any).
+  // into V stage `step` have landed (the caller waits for them), it
+  // overwrites those keys of its units with zeros (only the last step has
+  // any).
   auto vfix = [&](int step) {
     const int kb = kofs + step * P::KSTEP;
     if (kb + P::KSTEP > L) {
-      vm_wait_all();
       bf16* vdst = lds + P::V_OFF + (step % P::NVB) * P::VBUF + (vrun0 * 64 + lane) * 8;
 #pragma unroll
       for (int i = 0; i < P::NDMA; ++i) {
@@ -1342,8 +1354,16 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     }
     kstore_from(0, kr);
     kstore_from(1, k1);
-    vm_wait_all();
-    if (with_v) vfix(0);
+    // K step 2 is loaded here and rotated in the first step (each step
+    // rotates the K data loaded at the end of the step before)
+    kmeta_use();
+    kload();
+    if (with_v) {
+      // V step 0 has landed: after its direct loads came one K lookup, one
+      // V lookup and one K step's data
+      vm_wait_n<kMetaLoads + 1 + kDataLoads>();
+      vfix(0);
+    }
     __syncthreads();
   };
   // steps below every row's diagonal (kofs is a multiple of the step)
@@ -1356,9 +1376,7 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     prologue(false, false);
     const Acc zero = Acc{};
     for (int j = 0; j < nsteps; ++j) {
-      kmeta_use();
       kmeta(kofs + (j + 3) * P::KSTEP);
-      kload();
 #pragma unroll
       for (int h = 0; h < P::NBLK; ++h) {
         Acc sc = qk_block(j, h, zero);
@@ -1366,6 +1384,8 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
         mx = fmaxf(mx, col_max(sc));
       }
       kstore(j + 2);
+      kmeta_use();
+      kload();  // K step j+3
       __syncthreads();
     }
     return mx;
@@ -1458,12 +1478,10 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     auto step = [&](int j, auto mask_tag) {
       constexpr bool MASKED = decltype(mask_tag)::value;
       const int kb = kofs + j * P::KSTEP;
-      kmeta_use();
       vmeta_use();
-      kmeta(kb + 3 * P::KSTEP);
       vmeta(kb + 2 * P::KSTEP);
+      kmeta(kb + 3 * P::KSTEP);
       vdma(j + 1);  // V step j+1
-      kload();      // K step j+2 (past the end: valid slots, never used)
       // keep the loads at the top of the step: they have the whole step to land
       __builtin_amdgcn_sched_barrier(0);
 
@@ -1476,8 +1494,12 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
         pv_block(j, h);
       }
 
-      kstore(j + 2);
-      vm_wait_all();
+      kstore(j + 2);  // K step j+2, loaded during the previous step
+      kmeta_use();
+      kload();  // K step j+3 (past the end: valid slots, never used)
+      // V step j+1 has landed: after its direct loads came one K step's
+      // data, still in flight
+      vm_wait_n<kDataLoads>();
       vfix(j + 1);
       // Instruction order for the step (the wave issues in order, so a
       // dependent MFMA chain would otherwise hold back the vector work
