@@ -121,11 +121,11 @@ def time_config(name, steps, warmup, with_rows=False, only_timed=False):
     other layers' data).  A decode batch whose new tokens sit at each request's last key
     slot does both in one call (pic_attn_decode_append); other batches call
     pic_cache_write, then the attention.  The call's main kernel records HIP events at its
-    start and end (pic_set_kernel_events; kernel_*: mean and median over the K steps).
-    Unless only_timed, with >= 10 warm-ups and >= 20 samples each, cold: events around the
-    whole call and around its main kernel in the same steps (call_ms with call_kernel_ms,
-    the pair to compare), the call with no kernel events (what recording them costs); warm
-    (one layer back to back): the main kernel and the call."""
+    start and end (pic_set_kernel_events; kernel_*: mean and median over the K steps), and
+    events on the stream bracket the whole attention call in the same steps (call_*), so
+    each step's kernel time lies inside its call time.  Unless only_timed, with >= 10
+    warm-ups and >= 20 samples each: the cold call with no kernel events (what recording
+    them costs); warm (one layer back to back): the main kernel and the call."""
     import torch
 
     import position_independent_kv_amd as pic
@@ -176,32 +176,33 @@ def time_config(name, steps, warmup, with_rows=False, only_timed=False):
             call()
 
     warm_up(warmup, lambda k: k)
-    kev = _events(steps)
+    kev, cev = _events(steps), _events(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
         dw.use_layer(warmup + k)
         pre()
         pic.pic_set_kernel_events(*kev[k])
+        cev[k][0].record(stream)
         call()
+        cev[k][1].record(stream)
     pic.pic_set_kernel_events(None, None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kern = _ms(kev)
+    kern, callt = _ms(kev), _ms(cev)
+    # kernel and call of the same timed steps: the kernel's events lie inside the call's
     res = dict(name=name, w=w, counts=counts, layers=nl, appends=append,
                step_ms=(t1 - t0) * 1e3 / steps,
                kernel_ms=float(kern.mean()), kernel_median_ms=float(np.median(kern)),
+               call_ms=float(callt.mean()), call_median_ms=float(np.median(callt)),
                step_bytes=step_counts(w, counts))
     if not only_timed:
         n, nw = max(20, steps), max(10, warmup)
         warm_up(nw, lambda k: k)
-        ck, cc = loop(n, lambda k: k, True)        # cold: kernel and call of the same steps
-        warm_up(nw, lambda k: k)
-        _, plain = loop(n, lambda k: k, False)     # cold: the call alone
+        _, plain = loop(n, lambda k: k, False)     # cold: the call alone, no kernel events
         warm_up(nw, lambda k: 0)
         wk, wc = loop(n, lambda k: 0, True)        # warm: one layer back to back
-        res.update(call_kernel_ms=float(np.median(ck)), call_ms=float(np.median(cc)),
-                   call_unhooked_ms=float(np.median(plain)),
+        res.update(call_unhooked_ms=float(np.median(plain)),
                    warm_kernel_ms=float(np.median(wk)), warm_call_ms=float(np.median(wc)),
                    samples=n, sample_warmup=nw)
     if with_rows and not only_timed:
@@ -720,10 +721,9 @@ def main():
     w, counts = main_res["w"], main_res["counts"]
     if not args.only_main:
         m = main_res
-        log(f"[bench] {args.config}: timed steps: kernel {m['kernel_ms'] * 1e3:.1f} us (cold); "
-            f"call loop: kernel {m['call_kernel_ms'] * 1e3:.1f} us within call "
-            f"{m['call_ms'] * 1e3:.1f} us, call without events {m['call_unhooked_ms'] * 1e3:.1f} us; "
-            f"warm kernel {m['warm_kernel_ms'] * 1e3:.1f} us")
+        log(f"[bench] {args.config}: timed steps (cold, means): kernel {m['kernel_ms'] * 1e3:.1f} us "
+            f"within call {m['call_ms'] * 1e3:.1f} us; call without kernel events "
+            f"{m['call_unhooked_ms'] * 1e3:.1f} us; warm kernel {m['warm_kernel_ms'] * 1e3:.1f} us")
     decode = w.kind == "decode"
     kernel = "decode_kernel" if decode else "mixed_kernel"
     if decode:
@@ -757,8 +757,8 @@ def main():
                 algorithmic_bytes=counts["bytes"], algorithmic_flops=counts["flops"],
                 unique_kv_bytes=counts["unique_kv_bytes"])
     if "warm_kernel_ms" in main_res:
-        roof.update(call_ms=main_res["call_ms"], call_kernel_ms=main_res["call_kernel_ms"],
-                    call_frac=rate(main_res["call_unhooked_ms"]) / peak,
+        roof.update(call_ms=main_res["call_ms"], call_median_ms=main_res["call_median_ms"],
+                    call_frac=rate(main_res["call_ms"]) / peak,
                     call_unhooked_ms=main_res["call_unhooked_ms"],
                     warm_kernel_ms=main_res["warm_kernel_ms"],
                     warm_frac=rate(main_res["warm_kernel_ms"]) / peak,
@@ -790,7 +790,7 @@ def main():
         others[name] = {
             "workload": WORKLOAD_TEXT[name], "layers": r["layers"],
             "kernel_ms": r["kernel_ms"], "kernel_median_ms": r["kernel_median_ms"],
-            "call_ms": r["call_ms"], "call_kernel_ms": r["call_kernel_ms"],
+            "call_ms": r["call_ms"], "call_median_ms": r["call_median_ms"],
             "call_unhooked_ms": r["call_unhooked_ms"],
             "warm_kernel_ms": r["warm_kernel_ms"],
             "warm_call_ms": r["warm_call_ms"], "step_ms": r["step_ms"],
@@ -799,17 +799,16 @@ def main():
             "kernel_hbm_frac": c["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "kernel_TFLOPs": c["flops"] / (r["kernel_ms"] * 1e-3) / 1e12,
             "kernel_mfma_frac": c["flops"] / (r["kernel_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "call_GBps": c["bytes"] / (r["call_unhooked_ms"] * 1e-3) / 1e9,
-            "call_TFLOPs": c["flops"] / (r["call_unhooked_ms"] * 1e-3) / 1e12,
+            "call_GBps": c["bytes"] / (r["call_ms"] * 1e-3) / 1e9,
+            "call_TFLOPs": c["flops"] / (r["call_ms"] * 1e-3) / 1e12,
             "warm_kernel_GBps": c["bytes"] / (r["warm_kernel_ms"] * 1e-3) / 1e9,
             "warm_kernel_TFLOPs": c["flops"] / (r["warm_kernel_ms"] * 1e-3) / 1e12,
             "unique_kv_bytes": c["unique_kv_bytes"], "algorithmic_bytes": c["bytes"],
             "flops": c["flops"],
         }
-        log(f"[bench] {name}: timed steps: kernel {r['kernel_ms'] * 1e3:.1f} us (cold); "
-            f"call loop: kernel {r['call_kernel_ms'] * 1e3:.1f} us within call "
-            f"{r['call_ms'] * 1e3:.1f} us, call without events {r['call_unhooked_ms'] * 1e3:.1f} us; "
-            f"warm kernel {r['warm_kernel_ms'] * 1e3:.1f} us; "
+        log(f"[bench] {name}: timed steps (cold, means): kernel {r['kernel_ms'] * 1e3:.1f} us "
+            f"within call {r['call_ms'] * 1e3:.1f} us; call without kernel events "
+            f"{r['call_unhooked_ms'] * 1e3:.1f} us; warm kernel {r['warm_kernel_ms'] * 1e3:.1f} us; "
             f"{others[name]['kernel_GBps']:.0f} GB/s, {others[name]['kernel_TFLOPs']:.1f} TFLOP/s")
         if not args.no_cpu_baseline:
             t = time.time()
