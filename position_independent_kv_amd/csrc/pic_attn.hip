@@ -1016,31 +1016,6 @@ __device__ void prefill_tile(const AttnArgs& a, int r, int g, int tile, unsigned
 // [tile*ROWS, tile*ROWS + ROWS), ROWS = 32 per wave
 // ---------------------------------------------------------------------------
 
-// Scheduling groups (mask bits of __builtin_amdgcn_sched_group_barrier).
-constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
-
-// Eight MFMAs, each followed by R LDS reads and V vector instructions.
-template <int R, int V>
-__device__ __forceinline__ void sched_phase() {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, R, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, V, 0);
-  }
-}
-
-// Order of one prefill step of NBLK 32-key blocks: score MFMAs with softmax
-// work, PV MFMAs with staging work.
-template <int NBLK>
-__device__ __forceinline__ void sched_interleave() {
-#pragma unroll
-  for (int b = 0; b < NBLK; ++b) {
-    sched_phase<2, 6>();
-    sched_phase<1, 5>();
-  }
-}
-
 // Swizzle of the V^T stage: row r's unit u sits at slot u ^ vswz(r), so the
 // PV operand reads (32 rows, one unit each, per half wave) and the direct
 // loads (8 rows x 8 units per 64 lanes) hit distinct LDS banks.
@@ -1072,10 +1047,10 @@ struct Pf {
   static_assert(KPT % 4 == 0 && KPT <= D / 2, "whole 8-byte K pieces per thread");
 };
 
-// One prefill tile, bf16, software-pipelined over 32-key blocks so each wave
-// always has matrix and vector work in flight together: the score MFMAs of
-// block b+1 run while block b is exponentiated, and the PV MFMAs of block b
-// run while the next K step is rotated into LDS.
+// One prefill tile, bf16, software-pipelined over 32-key blocks: the score
+// MFMAs of block b+1 do not depend on the exponentials of block b or on its
+// PV MFMAs, so matrix and vector work can overlap, within a wave and between
+// the two waves of a SIMD (the instruction order is the compiler's).
 //
 // Staging: each 64-key step is gathered from the paged pools once per
 // workgroup.  Every thread loads its share of K rows and cos/sin rows into
@@ -1472,9 +1447,9 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
 #pragma unroll
     for (int db = 0; db < P::NDB; ++db) o[db] = Acc{};
 
-    // step j: blocks (j, 0) .. (j, NBLK-1); the score MFMAs of the next block
-    // run while a block is exponentiated, the PV MFMAs of a block while the
-    // next data is staged.  Stages K j+2 and V j+1.
+    // step j: blocks (j, 0) .. (j, NBLK-1), the scores of each next block
+    // computed before the current block is exponentiated and multiplied by V.
+    // Stages K j+2 and V j+1.
     auto step = [&](int j, auto mask_tag) {
       constexpr bool MASKED = decltype(mask_tag)::value;
       const int kb = kofs + j * P::KSTEP;
@@ -1501,12 +1476,6 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
       // data, still in flight
       vm_wait_n<kDataLoads>();
       vfix(j + 1);
-      // Instruction order for the step (the wave issues in order, so a
-      // dependent MFMA chain would otherwise hold back the vector work
-      // behind it): each score MFMA of the next block is followed by a slice
-      // of the current block's softmax, each PV MFMA by a slice of the
-      // staging work.
-      sched_interleave<P::NBLK>();
       __syncthreads();
     };
     for (int j = 0; j < jfull; ++j) step(j, std::false_type{});
