@@ -1156,8 +1156,12 @@ __device__ void prefill_tile_bf16(const AttnArgs& a, int r, int g, int tile, int
     TV c, s;    // their cos/sin
   };
   KRegs kr;
-  // vector-memory loads issued by one kmeta() and by one kload(): the
-  // counted waits below rely on them
+  // vector-memory loads issued by one kmeta() and by one kload(), at least:
+  // a load instruction moves at most 16 bytes, so the compiler can only
+  // issue more, and a counted wait below (at most N loads outstanding, in
+  // issue order) then waits for more than it needs, never for less.  The
+  // direct-load and wait statements are compiler barriers for memory
+  // accesses, so these loads stay between them.
   constexpr int kMetaLoads = ROT ? 2 : 1;
   constexpr int kDataLoads = 2 + (ROT ? 2 * cdiv(P::KPT * 4, 16) : 0);
   // Addresses (block ids, position) of the next loads, looked up before
