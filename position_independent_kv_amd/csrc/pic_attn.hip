@@ -1056,8 +1056,9 @@ struct Pf {
 // workgroup.  Every thread loads its share of K rows and cos/sin rows into
 // registers right after it has rotated the previous ones into LDS, a whole
 // step before they are rotated in turn (in the step's second half); K is
-// rotated on the way into LDS.  V^T needs no arithmetic, so it goes from the pool straight into LDS
-// (16-byte direct loads, no registers, no LDS write instructions).  K is
+// rotated on the way into LDS.  V^T needs no arithmetic, so it goes from the
+// pool straight into LDS (16-byte direct loads, no registers, no LDS write
+// instructions).  K is
 // staged two steps ahead (three K stages: the block being exponentiated may
 // be re-read, the next block is being multiplied, and the step after is
 // being written), V^T one step ahead (two stages).
