@@ -82,6 +82,7 @@ struct AttnArgs {
   int max_seq_len;
   int s_max;
   int nhg;
+  int dec_cpi;       // decode launch: consecutive key chunks per work item (1 or 2)
   float scale_log2;  // log2(e) / sqrt(d): scores are kept in base-2 units
   void* out;
   float2* ws_ml;
@@ -357,9 +358,10 @@ __device__ __forceinline__ unsigned lds_address(const void* p) {
   return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <typename T, int D, int NTAB = 2>
+template <typename T, int D, int NTAB = 2, int CPI = 1>
 struct DecodeSmem {
   static constexpr int NTS = NTAB;        // table stages: steps in flight + 1
+  static constexpr int MAXK = CPI * kMaxChunk;  // keys of the longest work item
   static constexpr int KSTEP = Cfg<T, D>::KSTEP;
   static constexpr int TROW = D / 2;      // floats per table row (unpadded: direct-load runs)
   static constexpr int UPR = TROW / 4;    // 16-byte units per row
@@ -368,8 +370,8 @@ struct DecodeSmem {
   static_assert(KSTEP % RPC == 0, "whole runs per table step");
   float cs[NTS][KSTEP][TROW];
   float sn[NTS][KSTEP][TROW];
-  int pos[kMaxChunk];
-  int blk[kMaxChunk / kBlockSize + 2];
+  int pos[MAXK];
+  int blk[MAXK / kBlockSize + 2];
 };
 
 // One decode work item: request r, key chunk s, kv heads hg*NW .. hg*NW+NW-1
@@ -395,13 +397,14 @@ struct DecodeSmem {
 // keeps them in LDS (s_new: [2][NW][D], K then V), and its last step takes
 // key L - 1 from there instead of from the pools, so no workgroup reads
 // what another one writes in the same launch.
-template <typename T, int D, int NB, int NW, bool ROT, bool APPEND = false>
+template <typename T, int D, int NB, int NW, bool ROT, bool APPEND = false, int CPI = 1>
 __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long qrow,
-                            unsigned char* smem_raw, T* s_new = nullptr) {
+                            unsigned char* smem_raw, T* s_new = nullptr, int s_cnt = 1) {
+  static_assert(CPI == 1 || CPI == 2, "one or two chunks per item");
   using C = Cfg<T, D>;
   using M = Mma<T>;
   typedef typename M::Op Op;
-  using SM = DecodeSmem<T, D, NB + 1>;
+  using SM = DecodeSmem<T, D, NB + 1, CPI>;
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -423,6 +426,10 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     }
     return;
   }
+  // chunks s .. s_last, walked as one key range; each chunk's (m, l, o) is
+  // written as its own partial, so the result is the same as with one chunk
+  // per item
+  const int s_last = CPI > 1 ? min(s + s_cnt, S) - 1 : s;
   int k0, k1;
   if (a.cdc_start) {  // block-aligned chunk from the table, at most kCdcMaxKeys keys
     const int* st = a.cdc_start + (size_t)r * (a.s_max + 1);
@@ -432,12 +439,14 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     if (k1 <= k0) return;
   } else {
     k0 = chunk_start(L, s, C::KSTEP);
-    k1 = chunk_start(L, s + 1, C::KSTEP);
+    k1 = chunk_start(L, s_last + 1, C::KSTEP);
   }
   const int nsteps = cdiv(k1 - k0, C::KSTEP);
+  // first step of chunk s + 1 (chunk starts are whole steps)
+  const int jsplit = s_last > s ? (chunk_start(L, s + 1, C::KSTEP) - k0) / C::KSTEP : nsteps;
 
   // append: the new token's K and V elements this thread stores (below)
-  const bool append = APPEND && s == S - 1;
+  const bool append = APPEND && s_last == S - 1;
   constexpr int kNewPerThread = APPEND ? (NW * D + NTH - 1) / NTH : 1;
   T new_kx[kNewPerThread], new_vx[kNewPerThread];
   if (append) {
@@ -569,6 +578,25 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   for (int dt = 0; dt < C::ND; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
+  // chunk sc done: its normalised output (a single-chunk request) or its
+  // partial (o / l, and (m, l)) for the merge
+  auto finish = [&](int sc) {
+    const float l_tot = col_sum(l_run);
+    if (!active || row16 >= G) return;
+    const float inv = 1.0f / l_tot;
+    if (S == 1) {
+      T* out = (T*)a.out + ((size_t)qrow * a.hq + g * G + row16) * D + grp * 4;
+#pragma unroll
+      for (int dt = 0; dt < C::ND; ++dt) store4<T>(out + dt * 16, acc[dt], inv);
+      return;
+    }
+    const size_t pidx = (((size_t)r * a.hkv + g) * a.s_max + sc) * G + row16;
+    float* po = a.ws_o + pidx * D + grp * 4;
+#pragma unroll
+    for (int dt = 0; dt < C::ND; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = acc[dt] * inv;
+    if (grp == 0) a.ws_ml[pidx] = make_float2(m_run, l_tot);
+  };
+
 #pragma unroll
   for (int b = 0; b < NB; ++b)
     if (b < nsteps) issue(b, grpbuf[b]);
@@ -577,6 +605,15 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
   auto step = [&](int j, Group& gb) {
     const int buf = j % SM::NTS;
     const int kb = k0 + j * C::KSTEP;  // absolute key index
+    if constexpr (CPI > 1) {
+      if (j == jsplit) {  // chunk s ends: its partial, then a fresh state for chunk s + 1
+        finish(s);
+#pragma unroll
+        for (int dt = 0; dt < C::ND; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.0f;
+      }
+    }
     if constexpr (ROT) {
       wait_k(gb);
       __syncthreads();
@@ -662,20 +699,7 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
       }
     }
   }
-  const float l_tot = col_sum(l_run);
-  if (!active || row16 >= G) return;
-  const float inv = 1.0f / l_tot;
-  if (S == 1) {
-    T* out = (T*)a.out + ((size_t)qrow * a.hq + g * G + row16) * D + grp * 4;
-#pragma unroll
-    for (int dt = 0; dt < C::ND; ++dt) store4<T>(out + dt * 16, acc[dt], inv);
-    return;
-  }
-  const size_t pidx = (((size_t)r * a.hkv + g) * a.s_max + s) * G + row16;
-  float* po = a.ws_o + pidx * D + grp * 4;
-#pragma unroll
-  for (int dt = 0; dt < C::ND; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = acc[dt] * inv;
-  if (grp == 0) a.ws_ml[pidx] = make_float2(m_run, l_tot);
+  finish(s_last);
 }
 
 // Merge the chunk partials of every multi-chunk q_len == 1 request:
@@ -1615,15 +1639,16 @@ constexpr int kDecodeDepth = 2;
 template <typename T, int D, bool ROT, bool APPEND = false>
 __global__ void __launch_bounds__(kThreads, 2) decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16)))
-  unsigned char smem[sizeof(DecodeSmem<T, D, kDecodeDepth + 1>)];
+  unsigned char smem[sizeof(DecodeSmem<T, D, kDecodeDepth + 1, 2>)];
   __shared__ __attribute__((aligned(16))) T s_new[APPEND ? 2 * kWaves * D : 1];
   const long long n = (long long)gridDim.x;
   const long long l = xcd_logical(blockIdx.x, n);
   const int hg = (int)(l % a.nhg);
   const long long rs = l / a.nhg;
   const int r = (int)(rs % a.num_reqs);
-  const int s = (int)(rs / a.num_reqs);
-  decode_item<T, D, kDecodeDepth, kWaves, ROT, APPEND>(a, r, hg, s, r, smem, s_new);
+  const int p = (int)(rs / a.num_reqs);  // item p: chunks p * dec_cpi ..
+  decode_item<T, D, kDecodeDepth, kWaves, ROT, APPEND, 2>(a, r, hg, p * a.dec_cpi, r, smem, s_new,
+                                                          a.dec_cpi);
 }
 
 // ---------------------------------------------------------------------------
@@ -2276,6 +2301,7 @@ static AttnArgs make_args(const AttnHostArgs& h, const WorkspaceLayout& w) {
   a.max_seq_len = h.max_seq_len;
   a.s_max = w.s_max;
   a.nhg = w.nhg;
+  a.dec_cpi = 1;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)h.head_dim));
   a.out = h.out;
   unsigned char* ws = (unsigned char*)h.workspace;
@@ -2311,10 +2337,45 @@ static void launch_combine(const AttnArgs& a, hipStream_t s, bool all_reqs,
                        dim3(kThreads), 0, s, a, dec_blocks, dsplit);
 }
 
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device (queried once per device).
+static std::atomic<int> g_cus[kMaxDevices];
+static int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int c = g_cus[dev].load(std::memory_order_relaxed);
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        c <= 0)
+      c = 256;
+    g_cus[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
+// Key chunks per work item of a decode launch with `items` single-chunk
+// items.  Two consecutive chunks in one workgroup share its start (chunk
+// metadata, query load and rotation) and keep its loads flowing across the
+// boundary, and each still writes its own partial, so the results do not
+// depend on this choice.  A compute unit then runs ceil(items / CUs) chunks
+// with one chunk per item and 2 x ceil(items / (2 CUs)) with two: pair when
+// that is no more (measured on 16 decode batches of 1-128 requests x 2k-33k
+// keys: pairing gains 1.5-4.5% wherever this holds and loses 10-70% on the
+// batches where it does not).
+static int decode_chunks_per_item(long long items) {
+  const long long cus = device_cus();
+  const long long one = (items + cus - 1) / cus;
+  const long long two = 2 * ((items + 2 * cus - 1) / (2 * cus));
+  return two <= one ? 2 : 1;
+}
+
 template <typename T, int D, bool ROT>
-static int launch_decode(const AttnArgs& a, hipStream_t s) {
-  const long long n = (long long)a.num_reqs * a.s_max * a.nhg;
-  if (n > 0x7fffffffLL || (long long)a.num_reqs * a.hkv > 0x7fffffffLL) return PIC_EUNSUPPORTED;
+static int launch_decode(AttnArgs a, hipStream_t s) {
+  const long long n1 = (long long)a.num_reqs * a.s_max * a.nhg;
+  if (n1 > 0x7fffffffLL || (long long)a.num_reqs * a.hkv > 0x7fffffffLL) return PIC_EUNSUPPORTED;
+  a.dec_cpi = decode_chunks_per_item(n1);
+  const long long n = (long long)a.num_reqs * cdiv(a.s_max, a.dec_cpi) * a.nhg;
   if constexpr (ROT) {
     if (a.new_k) {
       hipExtLaunchKernelGGL((decode_kernel<T, D, true, true>), dim3((unsigned)n),
@@ -2422,7 +2483,6 @@ static int attn_decode_shared(const AttnHostArgs& h, hipStream_t s) {
 // name is a host-side stand-in, never a device address).
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
-constexpr int kMaxDevices = 64;
 static std::atomic<void*> g_scratch_ptr[kMaxDevices];
 
 static void* scratch_address() {
