@@ -247,6 +247,33 @@ def test_decode_launch_equals_mixed_launch():
     assert _same_bits(a, b)
 
 
+def test_two_chunk_decode_items_equal_one_chunk_items():
+    """A decode batch big enough for two-chunk work items (64 requests x 4097 keys: 1024
+    single-chunk items, an even number per compute unit, so the decode launch walks two
+    consecutive chunks per workgroup) equals, bit for bit, the same batch through the mixed
+    launch, whose decode items take one chunk each, and a request decoded alone (one chunk
+    per item): each chunk's partial is the same either way."""
+    torch = _torch()
+    w, dw = _fresh(dict(builder="decode", seed=29, R=64, seg_len=1024, n_seg=4, n_shared=2,
+                        n_spans=32))
+    a = _rerun(dw, decode=True)
+    b = _rerun(dw, decode=False)
+    assert torch.isfinite(a.float()).all()
+    assert _same_bits(a, b)
+    r = 5
+    L = int(w.seq_lens[r])
+    one = torch.empty((1, w.hq, w.d), dtype=dw.dtype, device="cuda")
+    ws = torch.zeros(pic.pic_attn_workspace_size(1, 1, L, w.hq, w.hkv, w.d, dw.dtype),
+                     dtype=torch.uint8, device="cuda")
+    k0 = int(w.cu_seqlens_k[r])
+    pic.pic_attn_decode(dw.q[r:r + 1].contiguous(), dw.q_pos[r:r + 1].contiguous(),
+                        dw.k_pool, dw.v_pool, dw.block_table[r:r + 1].contiguous(),
+                        dw.seq_lens[r:r + 1].contiguous(), i32(np.array([0, L])),
+                        dw.k_pos[k0:k0 + L].contiguous(), dw.cos, dw.sin, L, one, ws)
+    torch.cuda.synchronize()
+    assert _same_bits(one[0], a[r])
+
+
 def test_prefill_request_alone_equals_in_mixed_batch():
     torch = _torch()
     w, dw = _fresh(SMALL_MIX)
