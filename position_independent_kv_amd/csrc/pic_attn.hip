@@ -624,7 +624,7 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     const int kb = k0 + j * C::KSTEP;  // absolute key index
     if constexpr (CPI > 1) {
       if (j == jsplit) {  // chunk s ends: its partial, then a fresh state for chunk s + 1
-        finish(s, s_stash != nullptr);
+        finish(s, s_stash != nullptr && G <= kStashGroup);
 #pragma unroll
         for (int dt = 0; dt < C::ND; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         m_run = -INFINITY;
@@ -717,7 +717,8 @@ __device__ void decode_item(const AttnArgs& a, int r, int hg, int s, long long q
     }
   }
   finish(s_last, false);
-  if (CPI > 1 && s_stash && jsplit < nsteps && active && row16 < G) {  // chunk s's partial
+  if (CPI > 1 && s_stash && G <= kStashGroup && jsplit < nsteps && active &&
+      row16 < G) {  // chunk s's partial, from the stash
     const float* st = s_stash + ((size_t)wave * kStashGroup + row16) * (D + 2);
     const size_t pidx = (((size_t)r * a.hkv + g) * a.s_max + s) * G + row16;
     float* po = a.ws_o + pidx * D + grp * 4;
